@@ -1,0 +1,308 @@
+"""Level-synchronous CPU oracle (float64 NumPy) for the pyramid selector and the
+block-sparse causal attention that runs over its selection.
+
+TEST INFRASTRUCTURE ONLY: used by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py; never by the product path.
+
+Notation (PISA abstract; PHBA §A.1.2):
+  block     tokens per key block and per query block (64 throughout the path)
+  nb        ceil(Tk / block), number of finest-level key blocks
+  b         branching factor of the pyramid
+  n_l       nodes at level l: n_0 = nb, n_{l+1} = ceil(n_l / b), down to one root
+  K         nodes kept per level (the diagonal block is added on top of them)
+  scale     1 / sqrt(d) unless given
+  unit      (batch, KV head, query block); all query heads of the KV group share
+            the unit's selection; query head h belongs to KV head h // (Hq / Hk)
+
+Readings of the pages this oracle rests on (the pages leave these open):
+  R1  Only nodes that lie entirely before the diagonal block are ever scored or
+      kept.  The chain of ancestors of the diagonal block is always expanded and
+      does not count against K; its fully-past children join the candidate set.
+      PHBA routes only to strictly preceding blocks (§A.1.2); scoring a node
+      that also covers future keys would let the future steer the selection.
+  R2  The pyramid is built up to a single root.  Levels with at most K
+      candidates keep all of them without scoring, so the start level does not
+      change the result.
+  R3  A pooled key is the mean of all key tokens the node covers (valid tokens
+      only for a ragged last block), kept in full precision (fp64 here).
+  R4  The LogSumExp of a unit runs over the union of the rows of all query heads
+      of the KV group: G heads x (tokens of the query block).
+  R5  Score of node n: log sum_r exp(scale * q_r . P_l[n]), natural log, no
+      node-size term.
+  R6  K counts kept fully-past nodes per level; the finest level therefore
+      yields at most K historical blocks plus the diagonal block.
+  R7  Equal scores: the lower node index wins.
+  R8  Fewer than K candidates: keep them all; unused route slots hold -1
+      (PHBA §A.1.2).
+  R9  The route row lists the kept finest-level blocks in ascending order, then
+      the diagonal block, then -1 padding up to K+1 slots.
+  R10 Decode: the single query token sits at position Tk-1 and its own key is
+      in the cache; its diagonal block is (Tk-1) // block.
+  R11 Attention is token-causal: a query at position t sees key positions
+      s <= t of its selected blocks only (this masks the diagonal block alone).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Pyramid geometry (PISA abstract: O(log N) pooled levels)
+# ---------------------------------------------------------------------------
+
+def num_blocks(n_tokens: int, block: int) -> int:
+    """Number of key blocks covering n_tokens tokens (the last may be ragged)."""
+    return -(-n_tokens // block)
+
+
+def level_sizes(n_blocks: int, branching: int) -> list[int]:
+    """Node counts per level, finest first: n_0 = n_blocks, n_{l+1} = ceil(n_l/b),
+    ending at the single root (reading R2)."""
+    if n_blocks < 1:
+        return []
+    sizes = [n_blocks]
+    while sizes[-1] > 1:
+        sizes.append(-(-sizes[-1] // branching))
+    return sizes
+
+
+def node_block_range(level: int, m: int, n_blocks: int, branching: int) -> tuple[int, int]:
+    """Finest-level blocks [lo, hi) covered by node m of a level."""
+    span = branching ** level
+    return m * span, min((m + 1) * span, n_blocks)
+
+
+def children(level: int, m: int, sizes: list[int], branching: int) -> list[int]:
+    """Children (at level-1) of node m of level `level`."""
+    return [c for c in range(m * branching, (m + 1) * branching) if c < sizes[level - 1]]
+
+
+# ---------------------------------------------------------------------------
+# Pyramid build (reading R3)
+# ---------------------------------------------------------------------------
+
+def build_pyramid(k: np.ndarray, block: int, branching: int) -> list[np.ndarray]:
+    """Mean-pooled key pyramid.
+
+    k: [B, Hk, Tk, d] keys (any float dtype; upcast exactly to float64).
+    Returns one float64 array [B, Hk, n_l, d] per level, finest first.  Every
+    node is the plain mean of the key tokens it covers, taken straight from the
+    tokens, not from the level below.
+    """
+    k = np.asarray(k, dtype=np.float64)
+    B, Hk, Tk, d = k.shape
+    nb = num_blocks(Tk, block)
+    sizes = level_sizes(nb, branching)
+    levels = []
+    for lvl, n in enumerate(sizes):
+        out = np.empty((B, Hk, n, d), dtype=np.float64)
+        for m in range(n):
+            lo, hi = node_block_range(lvl, m, nb, branching)
+            t0, t1 = lo * block, min(hi * block, Tk)
+            out[:, :, m, :] = k[:, :, t0:t1, :].mean(axis=2)
+        levels.append(out)
+    return levels
+
+
+def concat_levels(levels: list[np.ndarray]) -> np.ndarray:
+    """Levels concatenated finest first along the node axis: [B, Hk, N_tot, d]."""
+    return np.concatenate(levels, axis=2)
+
+
+# ---------------------------------------------------------------------------
+# Units
+# ---------------------------------------------------------------------------
+
+def _check_lengths(Tq: int, Tk: int) -> None:
+    if not (Tq == Tk or Tq == 1):
+        raise ValueError("oracle covers prefill (q_len == kv_len) and decode (q_len == 1) only")
+
+
+def query_positions(Tq: int, Tk: int) -> np.ndarray:
+    """Absolute position of every query token (prefill: t; decode: Tk-1, R10)."""
+    _check_lengths(Tq, Tk)
+    return np.arange(Tq) + (Tk - Tq)
+
+
+def num_query_blocks(Tq: int, Tk: int, block: int) -> int:
+    _check_lengths(Tq, Tk)
+    return 1 if (Tq == 1 and Tk > 1) else num_blocks(Tq, block)
+
+
+def unit_tokens(i: int, Tq: int, Tk: int, block: int) -> tuple[np.ndarray, int]:
+    """Query-token indices of query block i and the unit's diagonal block."""
+    pos = query_positions(Tq, Tk)
+    if Tq == 1 and Tk > 1:
+        toks = np.array([0])
+    else:
+        toks = np.arange(i * block, min((i + 1) * block, Tq))
+    diag = int(pos[toks[0]]) // block
+    return toks, diag
+
+
+def unit_rows(q: np.ndarray, bi: int, hk: int, group: int, toks: np.ndarray) -> np.ndarray:
+    """Rows of a unit (reading R4): every query head of the KV group, every token
+    of the query block, stacked head-major into [G * len(toks), d] float64."""
+    heads = range(hk * group, (hk + 1) * group)
+    return np.concatenate([np.asarray(q[bi, h, toks, :], dtype=np.float64) for h in heads], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Selection (PISA abstract; readings R1, R4-R9)
+# ---------------------------------------------------------------------------
+
+def lse_scores(rows: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
+    """s(n) = log sum_r exp(scale * rows[r] . keys[n]), max-subtracted, float64."""
+    z = scale * (rows @ keys.T)            # [R, C]
+    mx = z.max(axis=0)
+    return mx + np.log(np.exp(z - mx).sum(axis=0))
+
+
+def top_k_nodes(cand: list[int], s: np.ndarray, top_k: int) -> list[int]:
+    """The top_k candidates by score, higher first; equal scores prefer the
+    lower node index (reading R7)."""
+    order = sorted(range(len(cand)), key=lambda j: (-s[j], cand[j]))
+    return [cand[j] for j in order[:top_k]]
+
+
+@dataclass
+class UnitSelection:
+    sel: list[int]                                   # kept finest blocks ascending, then diag
+    kept: list[list[int]] = field(default_factory=list)       # per level (finest first), ascending
+    cands: list[list[int]] = field(default_factory=list)      # per level, in construction order
+    scores: list[np.ndarray | None] = field(default_factory=list)  # per level, None if unscored
+
+
+def candidates(level: int, kept_above: list[int], diag: int, sizes: list[int],
+               branching: int) -> list[int]:
+    """Bounded candidate set of one level (reading R1).
+
+    Top level: every node of that level lying wholly before the diagonal block's
+    ancestor.  Below: the children of the nodes kept one level up, followed by
+    the children of the diagonal's ancestor one level up that lie wholly before
+    the diagonal's ancestor at this level.
+    """
+    anc = diag // branching ** level
+    if level == len(sizes) - 1:
+        return list(range(anc))
+    anc_up = diag // branching ** (level + 1)
+    out = []
+    for p in kept_above:
+        out.extend(children(level + 1, p, sizes, branching))
+    out.extend(range(anc_up * branching, anc))
+    return out
+
+
+def select_unit(rows: np.ndarray, levels: list[np.ndarray], diag: int, branching: int,
+                top_k: int, scale: float) -> UnitSelection:
+    """Coarse-to-fine top-K for one unit.
+
+    rows:   [R, d] query rows of the unit.
+    levels: per level [n_l, d] pooled keys of the unit's (batch, KV head).
+    """
+    sizes = [lv.shape[0] for lv in levels]
+    L = len(sizes)
+    res = UnitSelection(sel=[], kept=[None] * L, cands=[None] * L, scores=[None] * L)
+    kept: list[int] = []
+    for level in range(L - 1, -1, -1):
+        cand = candidates(level, kept, diag, sizes, branching)
+        res.cands[level] = cand
+        if len(cand) <= top_k:                      # R8: keep all, nothing to rank
+            kept = sorted(cand)
+        else:
+            s = lse_scores(rows, levels[level][cand], scale)
+            res.scores[level] = s
+            kept = sorted(top_k_nodes(cand, s, top_k))
+        res.kept[level] = kept
+    res.sel = sorted(kept) + [diag]                  # R9
+    return res
+
+
+def select(q: np.ndarray, levels: list[np.ndarray], Tk: int, block: int, branching: int,
+           top_k: int, scale: float | None = None, units=None):
+    """Route table for every (or the listed) unit.
+
+    q:      [B, Hq, Tq, d]; levels: output of build_pyramid for [B, Hk, Tk, d] keys.
+    units:  optional iterable of (batch, kv_head, query_block); default all.
+    Returns (sel, trace) with sel an int64 array [B, Hk, nqb, K+1] (-1 padded,
+    rows not listed in `units` left at -2) and trace a dict keyed by unit
+    holding the UnitSelection.
+    """
+    B, Hq, Tq, d = q.shape
+    Hk = levels[0].shape[1]
+    group = Hq // Hk
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nqb = num_query_blocks(Tq, Tk, block)
+    sel = np.full((B, Hk, nqb, top_k + 1), -2, dtype=np.int64)
+    trace = {}
+    if units is None:
+        units = [(bi, hk, i) for bi in range(B) for hk in range(Hk) for i in range(nqb)]
+    for bi, hk, i in units:
+        toks, diag = unit_tokens(i, Tq, Tk, block)
+        rows = unit_rows(q, bi, hk, group, toks)
+        lv = [x[bi, hk] for x in levels]
+        us = select_unit(rows, lv, diag, branching, top_k, scale)
+        sel[bi, hk, i, :] = -1
+        sel[bi, hk, i, :len(us.sel)] = us.sel
+        trace[(bi, hk, i)] = us
+    return sel, trace
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse causal attention (PHBA §3.1, §A.1.3; reading R11)
+# ---------------------------------------------------------------------------
+
+def attend_rows(rows: np.ndarray, row_pos: np.ndarray, k_bh: np.ndarray, v_bh: np.ndarray,
+                blocks: list[int], block: int, scale: float):
+    """Exact softmax attention of `rows` over the tokens of `blocks`.
+
+    rows [R, d] at absolute positions row_pos [R]; k_bh, v_bh [Tk, d] of the KV
+    head.  A row sees key position s only if s lies in a listed block and
+    s <= its own position.  Returns (o [R, d], lse [R]) in float64.
+    """
+    Tk = k_bh.shape[0]
+    key_pos = np.concatenate([np.arange(j * block, min((j + 1) * block, Tk)) for j in blocks])
+    kk = np.asarray(k_bh[key_pos], dtype=np.float64)
+    vv = np.asarray(v_bh[key_pos], dtype=np.float64)
+    z = scale * (rows @ kk.T)                                  # [R, S]
+    visible = key_pos[None, :] <= row_pos[:, None]
+    z = np.where(visible, z, -np.inf)
+    mx = z.max(axis=1, keepdims=True)
+    p = np.exp(z - mx)
+    denom = p.sum(axis=1, keepdims=True)
+    o = (p @ vv) / denom
+    lse = mx[:, 0] + np.log(denom[:, 0])
+    return o, lse
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, block: int,
+              scale: float | None = None, units=None):
+    """Block-sparse causal attention over a route table.
+
+    q [B, Hq, Tq, d]; k, v [B, Hk, Tk, d]; sel [B, Hk, nqb, K+1] (-1 padded).
+    Returns o [B, Hq, Tq, d] and lse [B, Hq, Tq] in float64 (NaN outside the
+    listed units).
+    """
+    B, Hq, Tq, d = q.shape
+    _, Hk, Tk, _ = k.shape
+    group = Hq // Hk
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nqb = num_query_blocks(Tq, Tk, block)
+    pos = query_positions(Tq, Tk)
+    o = np.full((B, Hq, Tq, d), np.nan)
+    lse = np.full((B, Hq, Tq), np.nan)
+    if units is None:
+        units = [(bi, hk, i) for bi in range(B) for hk in range(Hk) for i in range(nqb)]
+    for bi, hk, i in units:
+        toks, _ = unit_tokens(i, Tq, Tk, block)
+        blocks = [int(x) for x in sel[bi, hk, i] if x >= 0]
+        for h in range(hk * group, (hk + 1) * group):
+            rows = np.asarray(q[bi, h, toks, :], dtype=np.float64)
+            oo, ll = attend_rows(rows, pos[toks], k[bi, hk], v[bi, hk], blocks, block, scale)
+            o[bi, h, toks, :] = oo
+            lse[bi, h, toks] = ll
+    return o, lse
