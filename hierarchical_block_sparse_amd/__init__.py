@@ -1,0 +1,14 @@
+"""Pyramid top-K block selection + block-sparse causal attention for AMD MI355X.
+
+The compute path is libpyr.so (HIP kernels for gfx950 behind the C ABI of
+include/pyr.h); this package is its thin ctypes binding.  Importing the package
+does not load the library; the first call does, and fails loudly if the library
+is missing.
+"""
+
+from ._binding import (  # noqa: F401
+    PYR_BF16, PYR_F32, Problem, PyrError, alloc_pyramid, alloc_sel, alloc_trace,
+    alloc_workspace, declared_functions, forward, lib, problem_for, pyr_abi_version,
+    pyr_attn_workspace_bytes, pyr_block_sparse_attn, pyr_build_pyramid, pyr_level_offset,
+    pyr_num_levels, pyr_num_query_blocks, pyr_pyramid_nodes, pyr_select_topk,
+)

@@ -1,0 +1,250 @@
+"""ctypes binding of libpyr (include/pyr.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libpyr.so.  Tensors are torch tensors used as device memory; work goes on the
+current torch stream unless a stream is given.  Each entry point checks on the
+host that the tensors have the shapes, dtypes and device the problem implies,
+so a kernel never sees a buffer smaller than its grid assumes.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpyr.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "pyr.h")
+
+PYR_F32, PYR_BF16 = 0, 1
+STATUS = {0: "PYR_OK", 1: "PYR_ERR_NULL", 2: "PYR_ERR_INVALID", 3: "PYR_ERR_UNSUPPORTED",
+          4: "PYR_ERR_MISALIGNED", 5: "PYR_ERR_WORKSPACE", 6: "PYR_ERR_HIP"}
+
+
+class PyrError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class PyrProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
+        ("block", ctypes.c_int32), ("branching", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+    ]
+
+
+_lib_handle = None
+
+
+def lib():
+    """The loaded libpyr.so.  Raises if the HIP library has not been built: there
+    is no fallback path."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m hierarchical_block_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(PyrProblem)
+        vp, st = ctypes.c_void_p, ctypes.c_int
+        for name, res, args in [
+            ("pyr_num_levels", ctypes.c_int32, [P]),
+            ("pyr_level_offset", ctypes.c_int64, [P, ctypes.c_int32]),
+            ("pyr_pyramid_nodes", ctypes.c_int64, [P]),
+            ("pyr_num_query_blocks", ctypes.c_int64, [P]),
+            ("pyr_attn_workspace_bytes", ctypes.c_size_t, [P]),
+            ("pyr_build_pyramid", st, [P, vp, vp, vp]),
+            ("pyr_select_topk", st, [P, vp, vp, vp, vp, vp, vp]),
+            ("pyr_block_sparse_attn", st, [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+            ("pyr_status_string", ctypes.c_char_p, [st]),
+            ("pyr_last_error", ctypes.c_char_p, []),
+            ("pyr_abi_version", ctypes.c_int32, []),
+        ]:
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib_handle = L
+    return _lib_handle
+
+
+def declared_functions() -> list[str]:
+    """Names of every function include/pyr.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pyr_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != 0:
+        raise PyrError(status, lib().pyr_last_error().decode())
+
+
+@dataclass(frozen=True)
+class Problem:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    q_len: int
+    kv_len: int
+    branching: int
+    top_k: int
+    dtype: torch.dtype
+    scale: float = 0.0
+    block: int = 64
+
+    def c(self) -> PyrProblem:
+        code = {torch.float32: PYR_F32, torch.bfloat16: PYR_BF16}.get(self.dtype, 99)
+        return PyrProblem(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.q_len,
+                          self.kv_len, self.block, self.branching, self.top_k, code, self.scale)
+
+    @property
+    def decode(self) -> bool:
+        return self.q_len == 1 and self.kv_len > 1
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _expect(t, name, shape, dtype, device_type="cuda"):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device.type != device_type:
+        raise ValueError(f"{name}: must be a {device_type} tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+# ---- geometry helpers (same names as the C ABI) ----
+
+def pyr_num_levels(p: Problem) -> int:
+    return lib().pyr_num_levels(ctypes.byref(p.c()))
+
+
+def pyr_level_offset(p: Problem, level: int) -> int:
+    return lib().pyr_level_offset(ctypes.byref(p.c()), level)
+
+
+def pyr_pyramid_nodes(p: Problem) -> int:
+    return lib().pyr_pyramid_nodes(ctypes.byref(p.c()))
+
+
+def pyr_num_query_blocks(p: Problem) -> int:
+    return lib().pyr_num_query_blocks(ctypes.byref(p.c()))
+
+
+def pyr_attn_workspace_bytes(p: Problem) -> int:
+    return lib().pyr_attn_workspace_bytes(ctypes.byref(p.c()))
+
+
+def pyr_abi_version() -> int:
+    return lib().pyr_abi_version()
+
+
+# ---- the hot path (same names as the C ABI) ----
+
+def pyr_build_pyramid(p: Problem, k, pyramid, stream=None):
+    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_len, p.head_dim), p.dtype)
+    _expect(pyramid, "pyramid", (p.batch, p.n_kv_heads, pyr_pyramid_nodes(p), p.head_dim),
+            torch.float32)
+    _check(lib().pyr_build_pyramid(ctypes.byref(p.c()), _ptr(k), _ptr(pyramid), _stream(stream)))
+
+
+def pyr_select_topk(p: Problem, q, pyramid, sel, trace_ids=None, trace_scores=None, stream=None):
+    nqb, L = pyr_num_query_blocks(p), pyr_num_levels(p)
+    _expect(q, "q", (p.batch, p.n_q_heads, p.q_len, p.head_dim), p.dtype)
+    _expect(pyramid, "pyramid", (p.batch, p.n_kv_heads, pyr_pyramid_nodes(p), p.head_dim),
+            torch.float32)
+    _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
+    _expect(trace_ids, "trace_ids", (p.batch, p.n_kv_heads, nqb, L, p.top_k), torch.int32)
+    _expect(trace_scores, "trace_scores", (p.batch, p.n_kv_heads, nqb, L, p.top_k + 1),
+            torch.float32)
+    _check(lib().pyr_select_topk(ctypes.byref(p.c()), _ptr(q), _ptr(pyramid), _ptr(sel),
+                                 _ptr(trace_ids), _ptr(trace_scores), _stream(stream)))
+
+
+def pyr_block_sparse_attn(p: Problem, q, k, v, sel, o, lse=None, workspace=None, stream=None):
+    nqb = pyr_num_query_blocks(p)
+    _expect(q, "q", (p.batch, p.n_q_heads, p.q_len, p.head_dim), p.dtype)
+    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_len, p.head_dim), p.dtype)
+    _expect(v, "v", (p.batch, p.n_kv_heads, p.kv_len, p.head_dim), p.dtype)
+    _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
+    _expect(o, "o", (p.batch, p.n_q_heads, p.q_len, p.head_dim), p.dtype)
+    _expect(lse, "lse", (p.batch, p.n_q_heads, p.q_len), torch.float32)
+    nbytes = 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace: must be a contiguous cuda tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().pyr_block_sparse_attn(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
+                                       _ptr(o), _ptr(lse), _ptr(workspace), nbytes,
+                                       _stream(stream)))
+
+
+# ---- allocating conveniences (torch allocates; the library computes) ----
+
+def alloc_pyramid(p: Problem, device="cuda"):
+    return torch.empty((p.batch, p.n_kv_heads, pyr_pyramid_nodes(p), p.head_dim),
+                       dtype=torch.float32, device=device)
+
+
+def alloc_sel(p: Problem, device="cuda"):
+    return torch.empty((p.batch, p.n_kv_heads, pyr_num_query_blocks(p), p.top_k + 1),
+                       dtype=torch.int32, device=device)
+
+
+def alloc_trace(p: Problem, device="cuda"):
+    nqb, L = pyr_num_query_blocks(p), pyr_num_levels(p)
+    ids = torch.empty((p.batch, p.n_kv_heads, nqb, L, p.top_k), dtype=torch.int32, device=device)
+    sc = torch.empty((p.batch, p.n_kv_heads, nqb, L, p.top_k + 1), dtype=torch.float32,
+                     device=device)
+    return ids, sc
+
+
+def alloc_workspace(p: Problem, device="cuda"):
+    n = pyr_attn_workspace_bytes(p)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device) if n else None
+
+
+def problem_for(q, k, branching: int, top_k: int, scale: float = 0.0) -> Problem:
+    B, Hq, Tq, d = q.shape
+    _, Hk, Tk, _ = k.shape
+    return Problem(B, Hq, Hk, d, Tq, Tk, branching, top_k, q.dtype, scale)
+
+
+def forward(q, k, v, branching: int, top_k: int, scale: float = 0.0, pyramid=None,
+            with_trace: bool = False):
+    """The whole path: build the pyramid (unless given), select, attend.
+    Returns (o, lse, sel, pyramid[, (trace_ids, trace_scores)])."""
+    p = problem_for(q, k, branching, top_k, scale)
+    if pyramid is None:
+        pyramid = alloc_pyramid(p, q.device)
+        pyr_build_pyramid(p, k, pyramid)
+    sel = alloc_sel(p, q.device)
+    trace = alloc_trace(p, q.device) if with_trace else (None, None)
+    pyr_select_topk(p, q, pyramid, sel, *trace)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    pyr_block_sparse_attn(p, q, k, v, sel, o, lse, alloc_workspace(p, q.device))
+    if with_trace:
+        return o, lse, sel, pyramid, trace
+    return o, lse, sel, pyramid

@@ -1,0 +1,46 @@
+// Internal declarations shared by the host API and the kernel translation units
+// of libpyr (gfx950).  Not part of the public ABI (include/pyr.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define PYR_MAX_LEVELS 48
+#define PYR_BLOCK 64
+
+// Problem geometry resolved once on the host and passed by value to kernels.
+struct PyrGeom {
+  int64_t Tq, Tk;          // query / key lengths
+  int64_t n_tot;           // pyramid nodes per (batch, KV head) slab
+  int32_t B, Hq, Hk, G, D; // batch, heads, group size Hq/Hk, head dim
+  int32_t nb;              // finest-level blocks: ceil(Tk / 64)
+  int32_t nqb;             // query blocks per (batch, KV head)
+  int32_t L;               // pyramid levels (finest .. root)
+  int32_t branching, K;    // children per node, nodes kept per level
+  int32_t decode;          // 1: one query token at position Tk-1
+  float scale;             // scoring / softmax scale
+  int32_t lsize[PYR_MAX_LEVELS];  // nodes per level, finest first
+  int64_t loff[PYR_MAX_LEVELS];   // node offset of each level inside a slab
+};
+
+// Token count covered by node m of level `level` (blocks [m b^l, (m+1) b^l)).
+__host__ __device__ inline int64_t pyr_node_tokens(const PyrGeom& g, int level, int64_t m) {
+  int64_t span = PYR_BLOCK;
+  for (int i = 0; i < level; ++i) span *= g.branching;
+  int64_t t0 = m * span, t1 = t0 + span;
+  if (t1 > g.Tk) t1 = g.Tk;
+  return t1 > t0 ? t1 - t0 : 0;
+}
+
+// Launchers (each returns the hipError_t of its launches).
+hipError_t pyr_launch_build(const PyrGeom& g, int dtype, const void* k, float* pyr,
+                            hipStream_t st);
+hipError_t pyr_launch_select(const PyrGeom& g, int dtype, const void* q, const float* pyr,
+                             int32_t* sel, int32_t* trace_ids, float* trace_scores,
+                             hipStream_t st);
+size_t pyr_attn_ws_bytes(const PyrGeom& g);
+hipError_t pyr_launch_attn(const PyrGeom& g, int dtype, const void* q, const void* k,
+                           const void* v, const int32_t* sel, void* o, float* lse, void* ws,
+                           hipStream_t st);
+// Selection kernels need this much dynamic LDS (bytes); validated on the host.
+size_t pyr_select_lds_bytes(const PyrGeom& g, int dtype);

@@ -1,0 +1,192 @@
+// Pooled key pyramid on gfx950.
+//
+// PISA (peercurrent.com record), abstract: keys are pooled into a
+// coarse-to-fine hierarchy of O(log N) levels.  PHBA (Prefix-State Hybrid
+// Block Attention), §A.1.2: a block summary is the mean of the block's valid
+// key rows, accumulated in fp32 registers.  Here node m of level l is the mean
+// of all key tokens under it; levels are stored finest first in one fp32 slab
+// per (batch, KV head).
+//
+// Two kernels:
+//  * build_chunk: one workgroup per chunk of `chunk` = b^s consecutive 64-token
+//    blocks of one (batch, KV head).  It streams the chunk's keys from HBM once
+//    (16-byte loads, several blocks in flight per thread), reduces each block
+//    to its mean, then folds the chunk's nodes up s levels inside LDS.  This is
+//    the HBM-bound pass: every key byte is read exactly once.
+//  * build_top: one workgroup per (batch, KV head) folds the remaining levels
+//    (above level s) from the nodes in the output slab; these are a few
+//    hundred KiB at most and stay in L2.
+// A parent is the token-weighted mean of its children, so a ragged last block
+// or a ragged last node gives the exact token mean.
+#include "pyr_device.h"
+#include "pyr_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunkMax = 16;  // finest blocks per workgroup (b^s <= 16)
+constexpr int kBatch = 4;      // blocks whose loads are in flight together
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
+                                                        float* __restrict__ pyr, PyrGeom g,
+                                                        int chunk, int s_levels,
+                                                        int chunks_per_bh) {
+  constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte load
+  constexpr int TPR = D / VEC;          // threads per key row
+  constexpr int RPP = kThreads / TPR;   // rows per pass of the workgroup
+  constexpr int PASSES = PYR_BLOCK / RPP;
+  static_assert(PYR_BLOCK % RPP == 0, "rows per pass must divide the block");
+
+  __shared__ float part[kBatch][RPP][D];
+  __shared__ float nodes[2][kChunkMax][D];
+
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x / chunks_per_bh;
+  const int c = blockIdx.x % chunks_per_bh;
+  const int64_t blk0 = (int64_t)c * chunk;
+  const int nblk = (int)min<int64_t>(chunk, g.nb - blk0);
+  const T* kb = k + bh * g.Tk * D;
+  float* slab = pyr + bh * g.n_tot * D;
+
+  const int col = (tid % TPR) * VEC;
+  const int r0 = tid / TPR;
+
+  for (int jb = 0; jb < nblk; jb += kBatch) {
+    uint4 raw[kBatch][PASSES];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int64_t tok = (blk0 + jb + u) * PYR_BLOCK + r0 + p * RPP;
+        if (jb + u < nblk && tok < g.Tk)
+          raw[u][p] = ld16_nt(kb + tok * D + col);
+        else
+          raw[u][p] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      float acc[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        float x[VEC];
+        unpack16<T>(raw[u][p], x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += x[e];
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part[u][r0][col + e] = acc[e];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kBatch * D; idx += kThreads) {
+      const int u = idx / D, dcol = idx % D;
+      if (jb + u < nblk) {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPP; ++r) s += part[u][r][dcol];
+        const int64_t m = blk0 + jb + u;
+        const float mean = s / (float)pyr_node_tokens(g, 0, m);
+        nodes[0][jb + u][dcol] = mean;
+        slab[(g.loff[0] + m) * D + dcol] = mean;
+      }
+    }
+    __syncthreads();
+  }
+
+  // Fold the chunk up s levels inside LDS (token-weighted means).
+  int cur = 0;
+  int n_below = nblk;
+  int64_t first_below = blk0;  // global index of the chunk's first node one level down
+  for (int lvl = 1; lvl <= s_levels; ++lvl) {
+    const int b = g.branching;
+    const int n_here = (n_below + b - 1) / b;
+    const int64_t first_here = first_below / b;
+    for (int idx = tid; idx < n_here * D; idx += kThreads) {
+      const int m = idx / D, dcol = idx % D;
+      float num = 0.f, den = 0.f;
+      for (int j = 0; j < b; ++j) {
+        const int cidx = m * b + j;
+        if (cidx < n_below) {
+          const float w = (float)pyr_node_tokens(g, lvl - 1, first_below + cidx);
+          num += nodes[cur][cidx][dcol] * w;
+          den += w;
+        }
+      }
+      const float mean = num / den;
+      nodes[cur ^ 1][m][dcol] = mean;
+      slab[(g.loff[lvl] + first_here + m) * D + dcol] = mean;
+    }
+    __syncthreads();
+    cur ^= 1;
+    n_below = n_here;
+    first_below = first_here;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void build_top(float* __restrict__ pyr, PyrGeom g,
+                                                      int first_level) {
+  float* slab = pyr + (int64_t)blockIdx.x * g.n_tot * D;
+  const int b = g.branching;
+  for (int lvl = first_level; lvl < g.L; ++lvl) {
+    const int n_here = g.lsize[lvl];
+    const int n_below = g.lsize[lvl - 1];
+    const float* below = slab + g.loff[lvl - 1] * D;
+    float* here = slab + g.loff[lvl] * D;
+    for (int idx = threadIdx.x; idx < n_here * D; idx += kThreads) {
+      const int m = idx / D, dcol = idx % D;
+      float num = 0.f, den = 0.f;
+      for (int j = 0; j < b; ++j) {
+        const int64_t cidx = (int64_t)m * b + j;
+        if (cidx < n_below) {
+          const float w = (float)pyr_node_tokens(g, lvl - 1, cidx);
+          num += below[cidx * D + dcol] * w;
+          den += w;
+        }
+      }
+      here[(int64_t)m * D + dcol] = num / den;
+    }
+    __threadfence_block();
+    __syncthreads();
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_build_t(const PyrGeom& g, const void* k, float* pyr, hipStream_t st) {
+  const int64_t n_bh = (int64_t)g.B * g.Hk;
+  if (n_bh == 0 || g.nb == 0) return hipSuccess;
+  // s = levels folded inside a workgroup: the largest s with b^s <= kChunkMax
+  // and s < L (never past the root).
+  int s = 0, chunk = 1;
+  while ((int64_t)chunk * g.branching <= kChunkMax && s + 1 < g.L) {
+    chunk *= g.branching;
+    ++s;
+  }
+  const int chunks_per_bh = (g.nb + chunk - 1) / chunk;
+  hipLaunchKernelGGL((build_chunk<T, D>), dim3((unsigned)(n_bh * chunks_per_bh)),
+                     dim3(kThreads), 0, st, static_cast<const T*>(k), pyr, g, chunk, s,
+                     chunks_per_bh);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (s + 1 < g.L) {
+    hipLaunchKernelGGL((build_top<D>), dim3((unsigned)n_bh), dim3(kThreads), 0, st, pyr, g,
+                       s + 1);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+hipError_t pyr_launch_build(const PyrGeom& g, int dtype, const void* k, float* pyr,
+                            hipStream_t st) {
+  if (dtype == 1) {
+    return g.D == 64 ? launch_build_t<bf16_t, 64>(g, k, pyr, st)
+                     : launch_build_t<bf16_t, 128>(g, k, pyr, st);
+  }
+  return g.D == 64 ? launch_build_t<float, 64>(g, k, pyr, st)
+                   : launch_build_t<float, 128>(g, k, pyr, st);
+}

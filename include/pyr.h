@@ -1,0 +1,164 @@
+/*
+ * pyr.h -- C ABI of libpyr: pyramid top-K block selection followed by
+ * block-sparse causal attention, on AMD Instinct MI355X (gfx950).
+ *
+ * The method (PISA, peercurrent.com record of the PISA preprint, abstract):
+ * keys are mean-pooled into a coarse-to-fine pyramid of O(log N) levels;
+ * selection starts at the coarsest level, scores a bounded candidate set per
+ * level with LogSumExp over the query block, keeps the top K and descends to
+ * their children, down to 64-token key blocks; attention then runs exactly,
+ * with an online softmax, over the selected blocks only.  The selected blocks
+ * are strictly preceding ones and unused route slots hold -1 (PHBA:
+ * Prefix-State Hybrid Block Attention, paperlayer.ai summary, §A.1.2); the
+ * query's own block always supplies local causal attention (PHBA §3.1); the
+ * attention writes its output and log-sum-exp (PHBA §A.1.3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, row-major [B, H, T, d]; a 64-token tile of one head is
+ *    one contiguous chunk.  Query head h belongs to KV head h / (Hq / Hk).
+ *  - Every tensor pointer is a DEVICE pointer, 16-byte aligned, owned by the
+ *    caller.  The library never allocates, frees or synchronises, and keeps no
+ *    state beyond a thread-local error string.
+ *  - Work is enqueued on the given HIP stream (NULL = the default stream) and
+ *    runs asynchronously; device faults surface at the caller's next
+ *    synchronising call.
+ *  - Outputs are fully overwritten (including -1 padding); callers need not
+ *    clear them.
+ *  - Arguments are validated before anything is enqueued: any status other
+ *    than PYR_OK / PYR_ERR_HIP means nothing was launched.  PYR_ERR_HIP means
+ *    a launch failed; pyr_last_error() holds the HIP error text.
+ *  - Entry points are reentrant; concurrent calls on different streams are
+ *    independent.
+ *  - A unit is (batch, KV head, query block); all query heads of a KV group
+ *    share the unit's selection, and the LogSumExp of a unit runs over the
+ *    rows of all those heads.
+ *  - Prefill: q_len == kv_len, query block i holds tokens [64i, 64i+64) and
+ *    its diagonal block is i.  Decode: q_len == 1 with kv_len > 1, the single
+ *    query token sits at position kv_len-1, and there is one query block whose
+ *    diagonal block is (kv_len-1)/64.  Other q_len are PYR_ERR_UNSUPPORTED.
+ *    kv_len need not be a multiple of 64: a ragged last block is pooled over
+ *    its valid tokens and masked beyond kv_len.
+ */
+#ifndef PYR_H_
+#define PYR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PYR_ABI_VERSION 1
+
+typedef enum pyr_status {
+  PYR_OK = 0,
+  PYR_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  PYR_ERR_INVALID = 2,     /* a size or parameter is out of range               */
+  PYR_ERR_UNSUPPORTED = 3, /* valid, but outside what this build implements     */
+  PYR_ERR_MISALIGNED = 4,  /* a tensor pointer is not 16-byte aligned           */
+  PYR_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
+  PYR_ERR_HIP = 6          /* a HIP launch failed (text in pyr_last_error)      */
+} pyr_status;
+
+typedef enum pyr_dtype {
+  PYR_F32 = 0,  /* IEEE binary32 */
+  PYR_BF16 = 1  /* bfloat16      */
+} pyr_dtype;
+
+typedef struct pyr_problem {
+  int32_t batch;       /* B >= 0                                              */
+  int32_t n_q_heads;   /* Hq >= 1, a multiple of n_kv_heads                   */
+  int32_t n_kv_heads;  /* Hk >= 1                                             */
+  int32_t head_dim;    /* d: 64 or 128                                        */
+  int64_t q_len;       /* Tq: == kv_len (prefill) or 1 (decode)               */
+  int64_t kv_len;      /* Tk >= 0                                             */
+  int32_t block;       /* tokens per query and key block: must be 64          */
+  int32_t branching;   /* b >= 2: children per pyramid node                   */
+  int32_t top_k;       /* K >= 1: nodes kept per level; the diagonal block is
+                          added on top, so a route row has K+1 slots          */
+  int32_t dtype;       /* pyr_dtype of q, k, v and o                          */
+  float scale;         /* softmax and scoring scale; 0 => 1/sqrt(head_dim)    */
+} pyr_problem;
+
+/* ---- geometry helpers (host-only, no device work; -1 on invalid input) ---- */
+
+/* Number of pyramid levels L, finest (64-token blocks) to the single root:
+ * n_0 = ceil(kv_len/64), n_{l+1} = ceil(n_l / b) until n = 1. */
+int32_t pyr_num_levels(const pyr_problem* p);
+/* Node offset of a level inside one (batch, KV head) pyramid slab (finest
+ * level first; levels are concatenated). */
+int64_t pyr_level_offset(const pyr_problem* p, int32_t level);
+/* Nodes per (batch, KV head) slab: sum of all level sizes. */
+int64_t pyr_pyramid_nodes(const pyr_problem* p);
+/* Query blocks per (batch, KV head): ceil(q_len/64) in prefill, 1 in decode. */
+int64_t pyr_num_query_blocks(const pyr_problem* p);
+/* Bytes of device workspace pyr_block_sparse_attn needs (0 if none). */
+size_t pyr_attn_workspace_bytes(const pyr_problem* p);
+
+/* ---- the hot path ---- */
+
+/* Pooled key pyramid (PISA abstract: pooling builds the coarse-to-fine key
+ * levels; PHBA §A.1.2: block means over valid rows, fp32 accumulation).
+ *   k        [B, Hk, kv_len, d] in p->dtype                          (input)
+ *   pyramid  [B, Hk, pyr_pyramid_nodes(p), d] float32                (output)
+ * Node m of level l is the mean of every key token it covers (blocks
+ * [m b^l, (m+1) b^l) clipped to the sequence); levels are concatenated finest
+ * first at pyr_level_offset(p, l). */
+pyr_status pyr_build_pyramid(const pyr_problem* p, const void* k, float* pyramid,
+                             hipStream_t stream);
+
+/* Coarse-to-fine top-K selection (PISA abstract).  For every unit, starting at
+ * the root: the candidates of a level are the children of the nodes kept one
+ * level up plus the children of the diagonal block's ancestor that lie wholly
+ * before the diagonal block's ancestor at this level; nodes that reach the
+ * diagonal block are never candidates.  With more than K candidates each is
+ * scored s(n) = log sum_r exp(scale * q_r . P_l[n]) over the unit's rows and
+ * the K best are kept (equal scores: lower index first); otherwise all are
+ * kept.  No query-by-key score matrix is written to memory.
+ *   q            [B, Hq, q_len, d] in p->dtype                       (input)
+ *   pyramid      output of pyr_build_pyramid for the same problem     (input)
+ *   sel          [B, Hk, nqb, K+1] int32: the finest kept blocks in ascending
+ *                order, then the diagonal block, then -1 padding      (output)
+ *   trace_ids    NULL or [B, Hk, nqb, L, K] int32: kept node ids of every
+ *                level (finest first), ascending, -1 padded           (output)
+ *   trace_scores NULL or [B, Hk, nqb, L, K+1] float32: the scores of those
+ *                kept nodes in the same order, then the best rejected score;
+ *                NaN where a level was not scored or a slot is unused (output)
+ */
+pyr_status pyr_select_topk(const pyr_problem* p, const void* q, const float* pyramid,
+                           int32_t* sel, int32_t* trace_ids, float* trace_scores,
+                           hipStream_t stream);
+
+/* Exact attention over the selected blocks (PHBA §A.1.3: online-softmax
+ * accumulation over routed blocks loaded straight from their original
+ * layouts, writing output and log-sum-exp).  Query token t at position
+ * pos(t) attends to every key s <= pos(t) of the blocks listed in its unit's
+ * route row (entries < 0 are ignored).
+ *   q, k, v    [B, Hq, q_len, d], [B, Hk, kv_len, d] x2, p->dtype    (input)
+ *   sel        [B, Hk, nqb, K+1] int32 route rows (any valid block ids;
+ *              pyr_select_topk writes them)                          (input)
+ *   o          [B, Hq, q_len, d] in p->dtype                         (output)
+ *   lse        NULL or [B, Hq, q_len] float32, natural log            (output)
+ *   workspace  device scratch of workspace_bytes >=
+ *              pyr_attn_workspace_bytes(p); may be NULL when that is 0.
+ * Route entries outside [0, ceil(kv_len/64)) are ignored (the host cannot read
+ * device route rows without synchronising, so they are not an error). */
+pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void* k,
+                                 const void* v, const int32_t* sel, void* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- diagnostics ---- */
+const char* pyr_status_string(pyr_status s);
+/* Thread-local detail of the last non-OK return on this thread ("" if none). */
+const char* pyr_last_error(void);
+int32_t pyr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PYR_H_ */

@@ -1,0 +1,139 @@
+"""The C ABI library on the CPU: it loads, exports every function include/pyr.h
+declares, and its host-only helpers and argument validation behave as the
+header states.  No call here enqueues device work: every call either is a
+geometry helper or fails validation, which happens before any HIP call."""
+
+import ctypes
+import os
+
+import pytest
+import torch
+
+import hierarchical_block_sparse_amd as H
+from hierarchical_block_sparse_amd import _binding as B
+from oracle import reference
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libpyr.so not built (run __graft_entry__.build())")
+
+
+def _p(**kw):
+    base = dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, q_len=4096, kv_len=4096,
+                branching=4, top_k=8, dtype=torch.bfloat16)
+    base.update(kw)
+    return H.Problem(**base)
+
+
+def test_exports_every_declared_function():
+    lib = H.lib()
+    names = H.declared_functions()
+    assert {"pyr_build_pyramid", "pyr_select_topk", "pyr_block_sparse_attn"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert H.pyr_abi_version() == 1
+
+
+def test_single_hip_runtime_in_process():
+    H.lib()
+    with open("/proc/self/maps") as f:
+        libs = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(libs) == 1, libs
+
+
+@pytest.mark.parametrize("kv_len,b", [(131072, 4), (32768, 4), (2048, 2), (1048576, 4),
+                                      (64 * 37 + 13, 3), (1, 2), (64, 4), (65, 4)])
+def test_geometry_matches_oracle(kv_len, b):
+    p = _p(q_len=kv_len, kv_len=kv_len, branching=b)
+    sizes = reference.level_sizes(reference.num_blocks(kv_len, 64), b)
+    assert H.pyr_num_levels(p) == len(sizes)
+    assert H.pyr_pyramid_nodes(p) == sum(sizes)
+    offs = [sum(sizes[:i]) for i in range(len(sizes))]
+    assert [H.pyr_level_offset(p, i) for i in range(len(sizes))] == offs
+    assert H.pyr_level_offset(p, len(sizes)) == -1
+    assert H.pyr_num_query_blocks(p) == reference.num_blocks(kv_len, 64)
+    assert H.pyr_attn_workspace_bytes(p) == 0
+
+
+def test_decode_geometry():
+    p = _p(batch=64, n_q_heads=32, n_kv_heads=8, q_len=1, kv_len=262144, top_k=64)
+    assert H.pyr_num_query_blocks(p) == 1
+    assert H.pyr_num_levels(p) == 7
+    assert H.pyr_pyramid_nodes(p) == 5461
+    assert H.pyr_attn_workspace_bytes(p) > 0
+
+
+def _status(fn, *args):
+    lib = H.lib()
+    return getattr(lib, fn)(*args), lib.pyr_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 3), (dict(n_q_heads=6, n_kv_heads=4), 2), (dict(branching=1), 2),
+    (dict(top_k=0), 2), (dict(q_len=100, kv_len=4096), 3), (dict(batch=-1), 2),
+    (dict(top_k=2000), 3),
+])
+def test_invalid_problems_rejected_before_launch(kw, status):
+    p = _p(**kw)
+    dummy = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    s, msg = _status("pyr_build_pyramid", ctypes.byref(p.c()), dummy, dummy, None)
+    assert s == status and msg
+    assert H.pyr_num_levels(p) == -1
+
+
+def test_bad_block_and_dtype():
+    p = _p()
+    c = p.c()
+    c.block = 32
+    s, _ = _status("pyr_build_pyramid", ctypes.byref(c), ctypes.c_void_p(16), ctypes.c_void_p(16), None)
+    assert s == 3
+    c = p.c()
+    c.dtype = 7
+    s, _ = _status("pyr_select_topk", ctypes.byref(c), *([ctypes.c_void_p(16)] * 3), None, None, None)
+    assert s == 2
+
+
+def test_null_and_misaligned_pointers():
+    p = _p()
+    c = ctypes.byref(p.c())
+    s, msg = _status("pyr_build_pyramid", c, None, ctypes.c_void_p(16), None)
+    assert s == 1 and "NULL" in msg
+    s, _ = _status("pyr_build_pyramid", c, ctypes.c_void_p(18), ctypes.c_void_p(16), None)
+    assert s == 4
+    s, _ = _status("pyr_select_topk", c, ctypes.c_void_p(16), None, ctypes.c_void_p(16), None, None, None)
+    assert s == 1
+    s, _ = _status("pyr_block_sparse_attn", c, *([ctypes.c_void_p(16)] * 4), None, None, None, 0, None)
+    assert s == 1
+
+
+def test_decode_workspace_required():
+    p = _p(q_len=1, kv_len=8192)
+    c = ctypes.byref(p.c())
+    ptr = ctypes.c_void_p(16)
+    s, msg = _status("pyr_block_sparse_attn", c, ptr, ptr, ptr, ptr, ptr, None, None, 0, None)
+    assert s == 5 and "workspace" in msg
+    need = H.pyr_attn_workspace_bytes(p)
+    s, _ = _status("pyr_block_sparse_attn", c, ptr, ptr, ptr, ptr, ptr, None, ptr, need - 1, None)
+    assert s == 5
+
+
+def test_empty_problems_are_noops():
+    for kw in (dict(batch=0), dict(q_len=0, kv_len=0)):
+        p = _p(**kw)
+        c = ctypes.byref(p.c())
+        assert _status("pyr_build_pyramid", c, None, None, None)[0] == 0
+        assert _status("pyr_select_topk", c, None, None, None, None, None, None)[0] == 0
+        assert _status("pyr_block_sparse_attn", c, None, None, None, None, None, None, None, 0,
+                       None)[0] == 0
+
+
+def test_status_strings():
+    lib = H.lib()
+    for s in range(7):
+        assert lib.pyr_status_string(s)
+
+
+def test_binding_rejects_wrong_shapes_on_host():
+    p = _p(q_len=128, kv_len=128)
+    k = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        H.pyr_build_pyramid(p, k, torch.zeros(1))
