@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark: pyramid top-K selection + block-sparse causal attention on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input already resident
+in HBM: pyr_build_pyramid -> pyr_select_topk -> pyr_block_sparse_attn (for the
+decode workload the pyramid of the KV cache is built once beforehand and a step
+is selection + attention).  W untimed warm-up steps, then K timed steps
+bracketed by torch.cuda.synchronize(); per-stage times come from HIP events
+recorded on the stream the library launches on.
+
+Prints one JSON line.  `value` is tokens/s of the whole path; `roofline`
+describes the dominant kernel (the attention); `cpu_baseline` is the float64
+CPU oracle timed on this host over a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "select+sparse-attn tokens/s at T=128K; TFLOP/s & HBM GB/s as % of peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa_128k",
+                    choices=["gqa_128k", "mha_32k", "prefill_1m", "decode_256k", "tiny_fp32"])
+    ap.add_argument("--cpu-baseline-units", type=int, default=384,
+                    help="units of the workload the oracle runs for the CPU baseline (0: skip)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (the per-unit figures are derived in the design doc)
+# ---------------------------------------------------------------------------
+
+def attn_work(cfg):
+    """(flops, bytes) of the attention over the selection: every attended
+    (query row, key) pair costs 4d flops (QK^T and PV); bytes = Q read + O write
+    + the gathered K and V tiles of every selected block, once per unit."""
+    from oracle.reference import num_blocks  # geometry only
+    s = 2 if cfg.dtype.itemsize == 2 else 4
+    d, G, K = cfg.head_dim, cfg.group, cfg.top_k
+    bh = cfg.batch * cfg.n_kv_heads
+    if cfg.decode:
+        diag = (cfg.kv_len - 1) // 64
+        keys = min(K, diag) * 64 + (cfg.kv_len - diag * 64)
+        flops = bh * G * keys * 4 * d
+        byts = bh * (2 * G * d * s + 2 * keys * d * s)
+        return flops, byts
+    nqb = num_blocks(cfg.q_len, 64)
+    pairs = sum(min(K, i) * 64 * 64 + 64 * 65 // 2 for i in range(nqb))
+    tiles = sum(min(K, i) + 1 for i in range(nqb))
+    flops = bh * G * pairs * 4 * d
+    byts = bh * (2 * G * cfg.q_len * d * s + tiles * 2 * 64 * d * s)
+    return flops, byts
+
+
+def build_bytes(cfg, n_tot):
+    s = 2 if cfg.dtype.itemsize == 2 else 4
+    bh = cfg.batch * cfg.n_kv_heads
+    return bh * (cfg.kv_len * cfg.head_dim * s + n_tot * cfg.head_dim * 4)
+
+
+def select_work(cfg, sel_levels_cands):
+    """(flops, bytes): flops = sum over scored candidates of rows * 2d (fp32
+    dot products); bytes = Q read + route rows written (pooled keys are
+    L2-resident and not counted)."""
+    s = 2 if cfg.dtype.itemsize == 2 else 4
+    rows = cfg.group * (1 if cfg.decode else 64)
+    flops = sel_levels_cands * rows * 2 * cfg.head_dim
+    bh = cfg.batch * cfg.n_kv_heads
+    nqb = 1 if cfg.decode else -(-cfg.q_len // 64)
+    byts = cfg.batch * cfg.n_q_heads * cfg.q_len * cfg.head_dim * s + bh * nqb * (cfg.top_k + 1) * 4
+    return flops, byts
+
+
+def scored_candidates(cfg):
+    """Total candidates scored over all units (levels with more than K
+    candidates), from the selection geometry: every scored level of a unit
+    has b*K children of kept nodes plus the ancestor's fully-past children."""
+    from oracle.reference import level_sizes, num_blocks
+    b, K = cfg.branching, cfg.top_k
+    sizes = level_sizes(num_blocks(cfg.kv_len, 64), b)
+    L = len(sizes)
+    diags = [(cfg.kv_len - 1) // 64] if cfg.decode else range(-(-cfg.q_len // 64))
+    total = 0
+    for diag in diags:
+        nk = 0
+        for lvl in range(L - 1, -1, -1):
+            anc = diag // b ** lvl
+            C = anc if lvl == L - 1 else nk * b + (anc - (diag // b ** (lvl + 1)) * b)
+            if C > K:
+                total += C
+                nk = K
+            else:
+                nk = C
+    return total * cfg.batch * cfg.n_kv_heads
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(cfg, q, k, v, n_units):
+    import math
+
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import reference
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        blas_threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+        rng = np.random.default_rng(0)
+        nqb = 1 if cfg.decode else -(-cfg.q_len // 64)
+        bh_pairs = [(bi, hk) for bi in range(cfg.batch) for hk in range(cfg.n_kv_heads)]
+        # sample: one (batch, KV head), units spread over its query blocks
+        bi, hk = bh_pairs[int(rng.integers(len(bh_pairs)))]
+        if cfg.decode:
+            units = [(bi, hk, 0)]
+        else:
+            idx = sorted(set([0, 1, cfg.top_k, nqb - 1] +
+                             list(rng.choice(nqb, size=min(nqb, n_units), replace=False))))
+            units = [(bi, hk, int(i)) for i in idx[:max(n_units, 4)]]
+        t0 = time.perf_counter()
+        k64 = k[bi:bi + 1, hk:hk + 1].float().cpu().numpy().astype(np.float64)
+        v64 = v[bi:bi + 1, hk:hk + 1].float().cpu().numpy().astype(np.float64)
+        heads = slice(hk * cfg.group, (hk + 1) * cfg.group)
+        t_copy = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        levels = reference.build_pyramid(k64, 64, cfg.branching)
+        t_pyr = time.perf_counter() - t0
+        q64 = q[bi:bi + 1, heads].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        scale = 1 / math.sqrt(cfg.head_dim)
+        for (_, _, i) in units:
+            toks, diag = reference.unit_tokens(i, cfg.q_len, cfg.kv_len, 64)
+            rows = reference.unit_rows(q64, 0, 0, cfg.group, toks)
+            us = reference.select_unit(rows, [x[0, 0] for x in levels], diag, cfg.branching,
+                                       cfg.top_k, scale)
+            pos = reference.query_positions(cfg.q_len, cfg.kv_len)[toks]
+            for h in range(cfg.group):
+                reference.attend_rows(q64[0, h, toks], pos, k64[0, 0], v64[0, 0], us.sel, 64, scale)
+        t_units = time.perf_counter() - t0
+    n_bh = len(bh_pairs)
+    # decode steps start from a prebuilt pyramid, as on the device
+    total = (0.0 if cfg.decode else t_pyr * n_bh) + t_units / len(units) * (nqb * n_bh)
+    tokens = cfg.batch * (1 if cfg.decode else cfg.q_len)
+    return {
+        "value": tokens / total, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+        "sample": (f"float64 NumPy oracle on {len(units)} of {nqb * n_bh} units (one batch/KV-head "
+                   f"slab: pyramid {t_pyr:.2f}s, units {t_units:.2f}s; D2H copy {t_copy:.2f}s "
+                   f"excluded); whole-workload time extrapolated as pyramid x {n_bh} slabs + "
+                   f"mean unit time x {nqb * n_bh} units"),
+        "host_cores_visible": cores,
+    }
+
+
+def kernel_traffic(workload):
+    """HBM bytes per attention dispatch from the committed rocprofv3 counter
+    summary, if it was taken on the current attention source."""
+    path = os.path.join(ROOT, "profiles", f"attn_{workload}_pmc.json")
+    src = os.path.join(ROOT, "hierarchical_block_sparse_amd", "csrc", "attn.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("attn_src_sha256") != digest:
+            return None
+        return rec.get("bytes_per_dispatch")
+    except (OSError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+
+    import hierarchical_block_sparse_amd as H
+    from hierarchical_block_sparse_amd import workloads as W
+
+    cfg = W.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = W.make_inputs(cfg, dev)
+    p = H.Problem(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.q_len, cfg.kv_len,
+                  cfg.branching, cfg.top_k, cfg.dtype)
+    pyr = H.alloc_pyramid(p, dev)
+    sel = H.alloc_sel(p, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = H.alloc_workspace(p, dev)
+    stream = torch.cuda.current_stream()
+    if cfg.decode:
+        H.pyr_build_pyramid(p, k, pyr, stream)   # the cache's pyramid exists before decoding
+
+    n_stage = 3
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stage + 1)]
+          for _ in range(args.steps)]
+
+    def step(events=None):
+        if events:
+            events[0].record(stream)
+        if not cfg.decode:
+            H.pyr_build_pyramid(p, k, pyr, stream)
+        if events:
+            events[1].record(stream)
+        H.pyr_select_topk(p, q, pyr, sel, None, None, stream)
+        if events:
+            events[2].record(stream)
+        H.pyr_block_sparse_attn(p, q, k, v, sel, o, lse, ws, stream)
+        if events:
+            events[3].record(stream)
+
+    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+                for i in range(n_stage)]
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = cfg.batch * (1 if cfg.decode else cfg.q_len)
+    value = tokens / (ms_per_step / 1e3)
+
+    a_flops, a_bytes = attn_work(cfg)
+    n_tot = H.pyr_pyramid_nodes(p)
+    b_bytes = build_bytes(cfg, n_tot)
+    s_flops, s_bytes = select_work(cfg, scored_candidates(cfg))
+    t_build, t_sel, t_attn = (x / 1e3 for x in stage_ms)
+    achieved = a_flops / t_attn / 1e12
+    traffic = kernel_traffic(cfg.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v with planted retrieval blocks)",
+        "config": {
+            "workload": cfg.name, "batch": cfg.batch, "q_heads": cfg.n_q_heads,
+            "kv_heads": cfg.n_kv_heads, "q_len": cfg.q_len, "kv_len": cfg.kv_len,
+            "head_dim": cfg.head_dim, "block": 64, "branching": cfg.branching,
+            "top_k": cfg.top_k, "step": ("select+attn (pyramid prebuilt)" if cfg.decode
+                                         else "build+select+attn"),
+        },
+        "roofline": {
+            "kernel": "attn_prefill_mfma" if not cfg.decode else "attn_decode_split+combine",
+            "bound": "mfma" if not cfg.decode else "hbm",
+            "achieved": round(achieved, 2) if not cfg.decode else round(a_bytes / t_attn / 1e9, 1),
+            "peak": PEAK_BF16_TFLOPS if not cfg.decode else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if not cfg.decode else "GB/s",
+            "frac": round((achieved / PEAK_BF16_TFLOPS) if not cfg.decode
+                          else (a_bytes / t_attn / 1e9 / PEAK_HBM_GBS), 4),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": a_flops,
+            "algorithmic_bytes_per_launch": a_bytes,
+            "avg_launch_ms": round(stage_ms[2], 4),
+        },
+        "stages": {
+            "build": {"ms": round(stage_ms[0], 4), "GB/s": round(b_bytes / t_build / 1e9, 1) if t_build > 0 and not cfg.decode else None,
+                      "hbm_frac": round(b_bytes / t_build / 1e9 / PEAK_HBM_GBS, 4) if t_build > 0 and not cfg.decode else None},
+            "select": {"ms": round(stage_ms[1], 4), "GB/s": round(s_bytes / t_sel / 1e9, 1),
+                       "TFLOP/s_fp32_equiv": round(s_flops / t_sel / 1e12, 2)},
+            "attn": {"ms": round(stage_ms[2], 4), "TFLOP/s": round(achieved, 2),
+                     "GB/s_gathered": round(a_bytes / t_attn / 1e9, 1)},
+            "build_plus_select_hbm_frac": (round((b_bytes + s_bytes) / (t_build + t_sel) / 1e9 / PEAK_HBM_GBS, 4)
+                                           if not cfg.decode else None),
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_baseline_units > 0:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_baseline_units)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -45,18 +45,65 @@ __device__ __forceinline__ void unit_of(const PyrGeom& g, int64_t u_ord, int& bi
 
 // ---------------------------------------------------------------------------
 // bf16 prefill, MFMA
+//
+// K and V tiles of the selected blocks stream global -> LDS with direct
+// 16-byte loads (no VGPR staging), double-buffered: the tiles of the next
+// selected block are in flight while the current one is computed, and one
+// barrier per block separates the two.  Tiles keep the global row-major layout
+// with a per-row XOR swizzle of the 16-byte chunks, chosen so that the K reads
+// (one row per lane) and the transposed V reads are both free of bank
+// conflicts.  V^T fragments for the PV MFMA come from ds_read_b64_tr_b16:
+// within each 16-lane group, lane i receives element (i % 4) of the 8-byte
+// chunk that lane 4j + i/4 addresses, j = 0..3, so lanes that address a 4-key x
+// 16-dim patch row by row receive 4 consecutive keys of one dim each.
 // ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kRescaleLog2 = 8.f;  // rescale O only when a row max grows by > 2^8
+
+template <int D>
+struct TileGeom {
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int ROW = 2 * D;            // bytes per row
+  static constexpr int TILE = 64 * ROW;        // bytes per K or V tile
+  static constexpr int RP = 256 / ROW;         // rows per 256-byte bank sweep
+  __device__ static int swz_k(int r) { return (r / RP) % CPR; }
+  __device__ static int swz_v(int r) { return 4 * ((r / RP) % (CPR / 4)); }
+};
+
+// Issue the K and V tiles of block j into stage st.  Instruction t of a tile
+// fills LDS chunks [64t, 64t+64): lane l writes chunk p = 64t + l, i.e. row
+// p / CPR, stored chunk p % CPR, which holds logical chunk (p % CPR) ^ swz(row).
+// Rows past the sequence end re-read its last row (finite values that the
+// causal mask gives zero weight).
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_prefill_mfma(
+__device__ __forceinline__ void issue_tiles(const bf16_t* kh, const bf16_t* vh, int64_t Tk, int j,
+                                            unsigned char* ktile, unsigned char* vtile, int w,
+                                            int l) {
+  using TG = TileGeom<D>;
+  const int64_t key0 = (int64_t)j * PYR_BLOCK;
+#pragma unroll
+  for (int tt = 0; tt < TG::CPR / NW; ++tt) {
+    const int t = tt * NW + w;
+    const int p = t * 64 + l, row = p / TG::CPR, sc = p % TG::CPR;
+    const int64_t kp = min<int64_t>(key0 + row, Tk - 1);
+    __builtin_amdgcn_global_load_lds(kh + kp * D + (sc ^ TG::swz_k(row)) * 8,
+                                     (lds_void*)(ktile + t * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vh + kp * D + (sc ^ TG::swz_v(row)) * 8,
+                                     (lds_void*)(vtile + t * 1024), 16, 0, 0);
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_prefill_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ sel, bf16_t* __restrict__ o, float* __restrict__ lse, PyrGeom g,
     int wg_per_unit) {
+  using TG = TileGeom<D>;
   constexpr int NT = NW * 64;
-  constexpr int KS = D + 8;   // K tile row stride (elements): 16-byte pad
-  constexpr int VS = 64 + 4;  // V^T tile row stride (elements): 8-byte pad
-  constexpr int SEG = D / 8;  // 16-byte segments per row
-  __shared__ __align__(16) bf16_t Ks[64 * KS];
-  __shared__ __align__(16) bf16_t Vt[D * VS];
+  __shared__ __align__(16) unsigned char tiles[2][2][TG::TILE];  // [stage][K, V]
   __shared__ int s_sel[kMaxSel];
 
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
@@ -68,19 +115,25 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_mfma(
   const int h = hk * g.G + sub * NW + w;
   const float sl2 = g.scale * PYR_LOG2E;
   const int64_t row0 = (int64_t)i * PYR_BLOCK;  // first query token of the unit
+  const bf16_t* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
+  const bf16_t* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
 
-  // route row -> LDS (entries outside [0, nb) are skipped below)
   for (int jj = tid; jj <= g.K; jj += NT) s_sel[jj] = sel[unit * (g.K + 1) + jj];
 
-  // Q^T fragments (B operand): lane holds query row rt*32 + lr and d = ks*16 + 8*half .. +7
+  __syncthreads();  // s_sel visible
+  int first = 0;
+  while (first <= g.K && (s_sel[first] < 0 || s_sel[first] >= g.nb)) ++first;
+  if (first <= g.K) issue_tiles<D, NW>(kh, vh, g.Tk, s_sel[first], tiles[0][0], tiles[0][1], w, l);
+
+  // Q^T fragments (B operand): lane holds query row rt*32 + lr and d = ks*16 + 8*half .. +7.
+  // Rows past the end of a ragged last block load the last row instead; they are never stored.
   const bf16_t* qh = q + ((int64_t)bi * g.Hq + h) * g.Tq * D;
   uint4 qb[2][D / 16];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const int64_t tok = row0 + rt * 32 + lr;
+    const int64_t tok = min<int64_t>(row0 + rt * 32 + lr, g.Tq - 1);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      qb[rt][ks] = tok < g.Tq ? ld16(qh + tok * D + ks * 16 + 8 * half) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < D / 16; ++ks) qb[rt][ks] = ld16(qh + tok * D + ks * 16 + 8 * half);
   }
 
   f32x16 oacc[D / 32][2];
@@ -93,132 +146,116 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_mfma(
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
-  const bf16_t* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
-  const bf16_t* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
-  __syncthreads();
+  // per-lane LDS offsets that do not depend on the block
+  const int g16 = l / 16, s16 = l % 16;
+  int vrow[2][2];   // [kt][k2] first V row this lane addresses for the transposed reads
+  int vcol[D / 32]; // byte offset of the lane's 8-byte V chunk per 32-dim tile (row-dependent swizzle applied below)
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) vrow[kt][k2] = kt * 32 + 16 * k2 + 4 * half + s16 / 4;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) vcol[dt] = dt * 32 + (g16 % 2) * 16 + 4 * (s16 % 4);
 
-  for (int jj = 0; jj <= g.K; ++jj) {
+  int st = 0;
+  for (int jj = first; jj <= g.K; ++jj) {
     const int j = s_sel[jj];
     if (j < 0 || j >= g.nb) continue;  // uniform across the workgroup
+    int nx = jj + 1;
+    while (nx <= g.K && (s_sel[nx] < 0 || s_sel[nx] >= g.nb)) ++nx;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
+    __syncthreads();                     // every wave's loads landed; previous stage free
+    if (nx <= g.K) issue_tiles<D, NW>(kh, vh, g.Tk, s_sel[nx], tiles[st ^ 1][0], tiles[st ^ 1][1], w, l);
+    const unsigned char* Kt = tiles[st][0];
+    const unsigned char* Vt = tiles[st][1];
     const int64_t key0 = (int64_t)j * PYR_BLOCK;
-    __syncthreads();  // previous tile fully consumed
-    // K tile, row-major
-    for (int s = tid; s < 64 * SEG; s += NT) {
-      const int key = s / SEG, seg = s % SEG;
-      const int64_t kp = key0 + key;
-      const uint4 x = kp < g.Tk ? ld16(kh + kp * D + seg * 8) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(Ks + key * KS + seg * 8) = x;
-    }
-    // V tile, transposed: 4 keys x 8 dims per slot
-    for (int s = tid; s < 16 * SEG; s += NT) {
-      const int kg = s / SEG, seg = s % SEG;
-      uint4 r[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int64_t kp = key0 + kg * 4 + rr;
-        r[rr] = kp < g.Tk ? ld16(vh + kp * D + seg * 8) : make_uint4(0, 0, 0, 0);
-      }
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&r[0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&r[1]);
-      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&r[2]);
-      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&r[3]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e / 2, sh = (e % 2) * 16;
-        const uint32_t a0 = (r0[wd] >> sh) & 0xffffu, a1 = (r1[wd] >> sh) & 0xffffu;
-        const uint32_t a2 = (r2[wd] >> sh) & 0xffffu, a3 = (r3[wd] >> sh) & 0xffffu;
-        *reinterpret_cast<uint2*>(Vt + (seg * 8 + e) * VS + kg * 4) =
-            make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-      }
-    }
-    __syncthreads();
 
-    // S^T = K Q^T: [64 keys x 64 rows] as 2x2 tiles of 32x32
-    f32x16 sacc[2][2];
+    // Two halves of 32 keys: S^T = K Q^T for the half, online softmax, then
+    // O^T += V^T P^T for the half (keeps only one half's scores live).
+    const bool need_mask = key0 + PYR_BLOCK - 1 > row0;  // only the diagonal (or later) block
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 sacc[2];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kt][rt][e] = 0.f;
+        for (int e = 0; e < 16; ++e) sacc[rt][e] = 0.f;
+      const int krow = kt * 32 + lr;
+      const unsigned char* kbase = Kt + krow * TG::ROW;
+      const int kswz = TG::swz_k(krow);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + (kt * 32 + lr) * KS + ks * 16 + 8 * half));
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + (((2 * ks + half) ^ kswz) << 4)));
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
-          sacc[kt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(qb[rt][ks]), sacc[kt][rt], 0, 0, 0);
+          sacc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(qb[rt][ks]), sacc[rt], 0, 0, 0);
       }
-    }
 
-    // online softmax per query row (lane's row = rt*32 + lr)
-    const bool need_mask = key0 + PYR_BLOCK - 1 > row0;  // only the diagonal (or later) block
-    uint4 pb[2][2][2];  // [rt][kt][ks2] P^T fragments as bf16x8
+      // online softmax per query row (lane's row = rt*32 + lr), log2 domain
+      bf16x8 pb[2][2];  // [rt][k2] P^T fragments
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int64_t rp = row0 + rt * 32 + lr;
-      float mx = -INFINITY;
+      for (int rt = 0; rt < 2; ++rt) {
+        if (need_mask) {
+          // key position minus row position, in the block's local coordinates
+          const int rel = (int)(row0 - key0) + rt * 32 + lr;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = sacc[kt][rt][e] * sl2;
-          if (need_mask) {
-            const int64_t kp = key0 + kt * 32 + (e / 4) * 8 + half * 4 + (e % 4);
-            if (kp > rp) x = -INFINITY;
-          }
-          sacc[kt][rt][e] = x;
-          mx = fmaxf(mx, x);
+          for (int e = 0; e < 16; ++e)
+            if (kt * 32 + (e / 4) * 8 + half * 4 + (e % 4) > rel) sacc[rt][e] = -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[rt], mx);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run[rt] - m_new);
-      float psum = 0.f;
+        float mraw = sacc[rt][0];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int e = 1; e < 16; ++e) mraw = fmaxf(mraw, sacc[rt][e]);
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+        const float mx = mraw * sl2;
+        const bool need = mx > m_run[rt] + kRescaleLog2;
+        if (__any(need)) {
+          const float m_new = need ? mx : m_run[rt];
+          const float alpha = m_new == m_run[rt] ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+          l_run[rt] *= alpha;
+          m_run[rt] = m_new;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[dt][rt][e] *= alpha;
+        }
+        // a row that has seen no visible key yet keeps m_run = -inf: all its p are 0
+        const float mneg = m_run[rt] == -INFINITY ? 0.f : -m_run[rt];
+        float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = m_new == -INFINITY ? 0.f : exp2f(sacc[kt][rt][e] - m_new);
-          sacc[kt][rt][e] = p;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[rt][e], sl2, mneg));
+          sacc[rt][e] = p;
           psum += p;
         }
-      l_run[rt] = l_run[rt] * alpha + psum;
-      m_run[rt] = m_new;
+        l_run[rt] += psum;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[dt][rt][e] *= alpha;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int e0 = k2 * 8;
-          pb[rt][kt][k2] = make_uint4(pack_bf16x2(sacc[kt][rt][e0 + 0], sacc[kt][rt][e0 + 1]),
-                                      pack_bf16x2(sacc[kt][rt][e0 + 2], sacc[kt][rt][e0 + 3]),
-                                      pack_bf16x2(sacc[kt][rt][e0 + 4], sacc[kt][rt][e0 + 5]),
-                                      pack_bf16x2(sacc[kt][rt][e0 + 6], sacc[kt][rt][e0 + 7]));
-        }
-    }
+          for (int e = 0; e < 8; ++e) pb[rt][k2][e] = (__bf16)sacc[rt][k2 * 8 + e];
+      }
 
-    // O^T += V^T P^T.  MFMA k index 8*half + jj maps to key
-    // kt*32 + 16*k2 + 4*half + jj (jj < 4) or + 8 + (jj - 4) (jj >= 4), the
-    // order in which the S^T accumulator holds P.
+      // O^T += V^T P^T.  MFMA k index 8*half + jj maps to key
+      // kt*32 + 16*k2 + 4*half + jj (jj < 4) or + 8 + (jj - 4) (jj >= 4), the
+      // order in which the S^T accumulator holds P.
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int r1 = vrow[kt][k2];
+        const unsigned char* vbase = Vt + r1 * TG::ROW;
+        const int vswz = TG::swz_v(r1);  // row + 8 has the same swizzle
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const bf16_t* vrow = Vt + (dt * 32 + lr) * VS + kt * 32 + 16 * k2 + 4 * half;
-          const uint2 a0 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 8);
-          const bf16x8 a = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int c = vcol[dt];
+          const int off1 = (((c >> 3) ^ vswz) << 4) + (c & 7) * 2;
+          const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + off1));
+          const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + off1 + 8 * TG::ROW));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt)
-            oacc[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(pb[rt][kt][k2]), oacc[dt][rt], 0, 0, 0);
+            oacc[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rt][k2], oacc[dt][rt], 0, 0, 0);
         }
+      }
     }
+    st ^= 1;
   }
 
   // finalize: rows of this lane = rt*32 + lr; dims of oacc[dt][rt][e] =
@@ -235,14 +272,15 @@ __global__ __launch_bounds__(NW * 64) void attn_prefill_mfma(
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = dt * 32 + g4 * 8 + half * 4;
-        const uint2 pk = make_uint2(pack_bf16x2(oacc[dt][rt][g4 * 4 + 0] * inv, oacc[dt][rt][g4 * 4 + 1] * inv),
-                                    pack_bf16x2(oacc[dt][rt][g4 * 4 + 2] * inv, oacc[dt][rt][g4 * 4 + 3] * inv));
-        *reinterpret_cast<uint2*>(oh + tok * D + d0) = pk;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(oacc[dt][rt][g4 * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(oh + tok * D + d0) = pk;
       }
     if (lse && half == 0) lse[((int64_t)bi * g.Hq + h) * g.Tq + tok] = (m_run[rt] + log2f(lt)) * PYR_LN2;
   }
 }
-
 // ---------------------------------------------------------------------------
 // fp32 (any dtype) prefill on the vector ALUs: one thread per query row.
 // ---------------------------------------------------------------------------
