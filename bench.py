@@ -37,9 +37,28 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gqa_128k",
                     choices=["gqa_128k", "mha_32k", "prefill_1m", "decode_256k", "tiny_fp32"])
-    ap.add_argument("--cpu-baseline-units", type=int, default=384,
+    ap.add_argument("--cpu-baseline-units", type=int, default=2048,
                     help="units of the workload the oracle runs for the CPU baseline (0: skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 5 device-to-device copies of 1 GiB (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": dt * 1e3,
+                      "GB/s_read+write": 2 * n / dt / 1e9}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -192,6 +211,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
 
     import hierarchical_block_sparse_amd as H

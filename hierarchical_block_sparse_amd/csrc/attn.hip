@@ -96,8 +96,8 @@ __device__ __forceinline__ void issue_tiles(const bf16_t* kh, const bf16_t* vh, 
   }
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void attn_prefill_mfma(
+template <int D, int NW, int RT>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ sel, bf16_t* __restrict__ o, float* __restrict__ lse, PyrGeom g,
     int wg_per_unit) {
@@ -108,13 +108,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_mfma(
 
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
   const int half = l / 32, lr = l % 32;
+  // RT row tiles of 32 per wave: a wave covers rows [rsub, rsub + 32*RT) of one head
+  constexpr int WPH = 2 / RT;  // waves per head
   const int sub = (int)(blockIdx.x % wg_per_unit);
   int bi, hk, i;
   int64_t unit;
   unit_of(g, blockIdx.x / wg_per_unit, bi, hk, i, unit);
-  const int h = hk * g.G + sub * NW + w;
+  const int h = hk * g.G + sub * (NW / WPH) + w / WPH;
+  const int rsub = (w % WPH) * 32;
   const float sl2 = g.scale * PYR_LOG2E;
-  const int64_t row0 = (int64_t)i * PYR_BLOCK;  // first query token of the unit
+  const int64_t row0 = (int64_t)i * PYR_BLOCK + rsub;  // first query token of this wave
   const bf16_t* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
   const bf16_t* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
 
@@ -128,23 +131,27 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_mfma(
   // Q^T fragments (B operand): lane holds query row rt*32 + lr and d = ks*16 + 8*half .. +7.
   // Rows past the end of a ragged last block load the last row instead; they are never stored.
   const bf16_t* qh = q + ((int64_t)bi * g.Hq + h) * g.Tq * D;
-  uint4 qb[2][D / 16];
+  uint4 qb[RT][D / 16];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const int64_t tok = min<int64_t>(row0 + rt * 32 + lr, g.Tq - 1);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qb[rt][ks] = ld16(qh + tok * D + ks * 16 + 8 * half);
   }
 
-  f32x16 oacc[D / 32][2];
+  f32x16 oacc[D / 32][RT];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[dt][rt][e] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+  float m_run[RT], l_run[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+  }
 
   // per-lane LDS offsets that do not depend on the block
   const int g16 = l / 16, s16 = l % 16;
@@ -173,11 +180,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_mfma(
     // Two halves of 32 keys: S^T = K Q^T for the half, online softmax, then
     // O^T += V^T P^T for the half (keeps only one half's scores live).
     const bool need_mask = key0 + PYR_BLOCK - 1 > row0;  // only the diagonal (or later) block
+    // (row0 here is the wave's first row; rows of the wave run to row0 + 32*RT - 1)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      f32x16 sacc[2];
+      f32x16 sacc[RT];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[rt][e] = 0.f;
       const int krow = kt * 32 + lr;
@@ -187,14 +195,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_mfma(
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kbase + (((2 * ks + half) ^ kswz) << 4)));
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
           sacc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(qb[rt][ks]), sacc[rt], 0, 0, 0);
       }
 
       // online softmax per query row (lane's row = rt*32 + lr), log2 domain
-      bf16x8 pb[2][2];  // [rt][k2] P^T fragments
+      bf16x8 pb[RT][2];  // [rt][k2] P^T fragments
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         if (need_mask) {
           // key position minus row position, in the block's local coordinates
           const int rel = (int)(row0 - key0) + rt * 32 + lr;
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_mfma(
           const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + off1 + 8 * TG::ROW));
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
+          for (int rt = 0; rt < RT; ++rt)
             oacc[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rt][k2], oacc[dt][rt], 0, 0, 0);
         }
       }
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_mfma(
   // dt*32 + (e/4)*8 + half*4 + e%4
   bf16_t* oh = o + ((int64_t)bi * g.Hq + h) * g.Tq * D;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const float lt = l_run[rt] + __shfl_xor(l_run[rt], 32, 64);
     const int64_t tok = row0 + rt * 32 + lr;
     if (tok >= g.Tq) continue;
@@ -587,19 +595,21 @@ hipError_t launch_attn_d(const PyrGeom& g, int dtype, const void* q, const void*
     return hipGetLastError();
   }
   if (dtype == 1) {
-    const int nw = g.G % 4 == 0 ? 4 : (g.G % 2 == 0 ? 2 : 1);
-    const int wpu = g.G / nw;
+    // heads per workgroup: 4, 2 or 1 (whichever divides G); 32 query rows per wave,
+    // two waves per head
+    const int nh = g.G % 4 == 0 ? 4 : (g.G % 2 == 0 ? 2 : 1);
+    const int wpu = g.G / nh;
     const dim3 grid((unsigned)(units * wpu));
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
     const bf16_t* vv = static_cast<const bf16_t*>(v);
     bf16_t* oo = static_cast<bf16_t*>(o);
-    if (nw == 4)
-      hipLaunchKernelGGL((attn_prefill_mfma<D, 4>), grid, dim3(256), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
-    else if (nw == 2)
-      hipLaunchKernelGGL((attn_prefill_mfma<D, 2>), grid, dim3(128), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
+    if (nh == 4)
+      hipLaunchKernelGGL((attn_prefill_mfma<D, 8, 1>), grid, dim3(512), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
+    else if (nh == 2)
+      hipLaunchKernelGGL((attn_prefill_mfma<D, 4, 1>), grid, dim3(256), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
     else
-      hipLaunchKernelGGL((attn_prefill_mfma<D, 1>), grid, dim3(64), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
+      hipLaunchKernelGGL((attn_prefill_mfma<D, 2, 1>), grid, dim3(128), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
   } else {
     hipLaunchKernelGGL((attn_prefill_valu<float, D>), dim3((unsigned)(units * g.G)), dim3(64), 0,
                        st, static_cast<const float*>(q), static_cast<const float*>(k),
