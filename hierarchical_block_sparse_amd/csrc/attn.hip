@@ -103,8 +103,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
     int wg_per_unit) {
   using TG = TileGeom<D>;
   constexpr int NT = NW * 64;
-  __shared__ __align__(16) unsigned char tiles[2][2][TG::TILE];  // [stage][K, V]
+  // one 8-wave workgroup per CU keeps three tile stages in flight; smaller
+  // workgroups share a CU and keep two
+  constexpr int NSTAGE = NW >= 8 ? 3 : 2;
+  constexpr int NLOAD = 2 * (TG::CPR / NW);  // tile-load instructions per block per wave
+  constexpr int WAIT_ONE = 0x0F70 | (NLOAD & 15) | ((NLOAD >> 4) << 14);  // vmcnt(NLOAD)
+  __shared__ __align__(16) unsigned char tiles[NSTAGE][2][TG::TILE];  // [stage][K, V]
   __shared__ int s_sel[kMaxSel];
+  __shared__ int s_n;
 
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
   const int half = l / 32, lr = l % 32;
@@ -124,9 +130,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
   for (int jj = tid; jj <= g.K; jj += NT) s_sel[jj] = sel[unit * (g.K + 1) + jj];
 
   __syncthreads();  // s_sel visible
-  int first = 0;
-  while (first <= g.K && (s_sel[first] < 0 || s_sel[first] >= g.nb)) ++first;
-  if (first <= g.K) issue_tiles<D, NW>(kh, vh, g.Tk, s_sel[first], tiles[0][0], tiles[0][1], w, l);
+  if (tid == 0) {   // compact the route row in place: entries outside [0, nb) are skipped
+    int n = 0;
+    for (int jj = 0; jj <= g.K; ++jj) {
+      const int j = s_sel[jj];
+      if (j >= 0 && j < g.nb) s_sel[n++] = j;
+    }
+    s_n = n;
+  }
+  __syncthreads();
+  const int nsel = s_n;
+#pragma unroll
+  for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+    if (s0 < nsel) issue_tiles<D, NW>(kh, vh, g.Tk, s_sel[s0], tiles[s0][0], tiles[s0][1], w, l);
 
   // Q^T fragments (B operand): lane holds query row rt*32 + lr and d = ks*16 + 8*half .. +7.
   // Rows past the end of a ragged last block load the last row instead; they are never stored.
@@ -165,14 +181,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
   for (int dt = 0; dt < D / 32; ++dt) vcol[dt] = dt * 32 + (g16 % 2) * 16 + 4 * (s16 % 4);
 
   int st = 0;
-  for (int jj = first; jj <= g.K; ++jj) {
+  for (int jj = 0; jj < nsel; ++jj) {
     const int j = s_sel[jj];
-    if (j < 0 || j >= g.nb) continue;  // uniform across the workgroup
-    int nx = jj + 1;
-    while (nx <= g.K && (s_sel[nx] < 0 || s_sel[nx] >= g.nb)) ++nx;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads landed
-    __syncthreads();                     // every wave's loads landed; previous stage free
-    if (nx <= g.K) issue_tiles<D, NW>(kh, vh, g.Tk, s_sel[nx], tiles[st ^ 1][0], tiles[st ^ 1][1], w, l);
+    // this wave's loads of block jj have landed once at most the loads of the
+    // blocks issued after it are outstanding (loads complete in order)
+    if (NSTAGE > 2 && jj + 1 < nsel)
+      __builtin_amdgcn_s_waitcnt(WAIT_ONE);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();  // every wave's loads of block jj landed; the oldest stage is free
+    const int nx = jj + NSTAGE - 1;
+    const int nst = st + NSTAGE - 1 >= NSTAGE ? st - 1 : st + NSTAGE - 1;
+    if (nx < nsel) issue_tiles<D, NW>(kh, vh, g.Tk, s_sel[nx], tiles[nst][0], tiles[nst][1], w, l);
     const unsigned char* Kt = tiles[st][0];
     const unsigned char* Vt = tiles[st][1];
     const int64_t key0 = (int64_t)j * PYR_BLOCK;
@@ -263,7 +283,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
         }
       }
     }
-    st ^= 1;
+    st = st + 1 == NSTAGE ? 0 : st + 1;
   }
 
   // finalize: rows of this lane = rt*32 + lr; dims of oacc[dt][rt][e] =
