@@ -19,12 +19,15 @@
 // Scoring, bf16 prefill path: rows are the M side of v_mfma_f32_16x16x32_bf16
 // and candidates the N side; each wave keeps its rows of Q in VGPRs for the
 // whole unit.  Pooled keys are fp32; each is split into hi = bf16(x) and
-// lo = bf16(x - hi) in LDS and both are contracted against the exact bf16 q,
-// so a dot product carries ~2^-17 relative error instead of bf16's 2^-9.  The
-// LogSumExp over rows is reduced in-lane, across the 4 lane groups with
-// shuffles, and across waves through LDS, as (max, sum) pairs in the log2
-// domain.  Generic path (fp32 inputs, decode, other group sizes): fp32 dot
-// products on the vector ALUs, same selection logic.
+// lo = bf16(x - hi) and both are contracted against the exact bf16 q, so a dot
+// product carries ~2^-17 relative error instead of bf16's 2^-9.  Candidates go
+// through LDS in chunks of 32: the pooled keys of the next chunk are loaded
+// into registers while the current chunk's MFMAs run, then converted to hi/lo
+// into the other LDS buffer (one barrier per chunk).  Each wave reduces its
+// rows' LogSumExp per candidate in-lane and across its 4 lane groups with
+// shuffles, as (max, sum) pairs in the log2 domain; the waves' partials are
+// merged once per level.  Generic path (fp32 inputs, decode, other group
+// sizes): fp32 dot products on the vector ALUs, same selection logic.
 #include <math.h>
 
 #include "pyr_device.h"
@@ -34,79 +37,99 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kChunk = 64;        // candidates staged per round (MFMA path)
-constexpr int kZbuf = 8192;       // fp32 scratch for the generic path
+constexpr int kChunk = 32;   // candidates per LDS chunk (MFMA path): two 16-wide N tiles
+constexpr int kZbuf = 8192;  // fp32 scratch for the generic path
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Dynamic LDS layout shared by host (sizing) and device.
 struct SelLayout {
-  int cmax;   // candidate capacity: b*K + b - 1, rounded up to 4
-  int off_kept, off_kscore, off_cand, off_score, off_rank, off_pos, off_scratch;
+  int cmax;  // candidate capacity: b*K + b - 1, rounded up to the chunk size
+  int off_kept, off_kscore, off_cand, off_score, off_rank, off_part, off_hl, off_zbuf;
   int total;  // bytes
-  __host__ __device__ SelLayout(int K, int b, int scratch_bytes) {
-    cmax = (b * K + b - 1 + 3) & ~3;
+  __host__ __device__ SelLayout(int K, int b, int D, bool mfma) {
+    cmax = (b * K + b - 1 + kChunk - 1) / kChunk * kChunk;
+    const int kp = (K + 3) & ~3;
     int o = 0;
-    off_kept = o;   o += 4 * ((K + 3) & ~3);
-    off_kscore = o; o += 4 * ((K + 3) & ~3);
+    off_kept = o;   o += 4 * kp;
+    off_kscore = o; o += 4 * kp;
     off_cand = o;   o += 4 * cmax;
-    off_score = o;  o += 4 * cmax;
+    off_score = o;  o += 4 * cmax;  // 16-byte aligned: read as float4
     off_rank = o;   o += 4 * cmax;
-    off_pos = o;    o += 4 * cmax;
-    o = (o + 15) & ~15;
-    off_scratch = o;
-    total = o + scratch_bytes;
+    if (mfma) {
+      off_part = o;  o += 8 * kWaves * cmax;             // float2 [wave][candidate]
+      off_hl = o;    o += 2 * 2 * kChunk * (D + 8) * 2;  // bf16 [stage][hi, lo][cand][D + 8]
+      off_zbuf = o;
+    } else {
+      off_part = off_hl = o;
+      off_zbuf = o;  o += 4 * kZbuf;
+    }
+    total = o;
   }
 };
 
-template <int D>
-constexpr int mfma_scratch_bytes() {
-  // part[kWaves][kChunk] float2 + khi/klo[kChunk][D+8] bf16
-  return kWaves * kChunk * 8 + 2 * kChunk * (D + 8) * 2;
-}
-
-__device__ __forceinline__ int64_t ipow(int b, int e) {
-  int64_t r = 1;
-  for (int i = 0; i < e; ++i) r *= b;
-  return r;
+// Ancestor of the diagonal block at every level: anc[l] = diag / b^l.
+__device__ void ancestors(const PyrGeom& g, int diag, int* s_anc) {
+  if (threadIdx.x == 0) {
+    int a = diag;
+    for (int l = 0; l < g.L; ++l) {
+      s_anc[l] = a;
+      a /= g.branching;
+    }
+  }
 }
 
 // Rank every candidate, keep the top K in ascending index order, write trace.
+// Candidates are ascending by node index, so "lower index wins a tie" is
+// "lower position wins": rank(j) = #{s > s_j} + #{jj < j : s == s_j}.  Scores
+// are never NaN (callers map NaN to -inf).
 __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* cand,
-                                float* score, int* rank, int* pos, int* kept, float* kscore,
+                                const float* score, int* rank, int* kept, float* kscore,
                                 int* nkept, int32_t* tr_ids, float* tr_scores) {
-  const int tid = threadIdx.x;
+  __shared__ int wsum[kWaves];
+  const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
   const int K = g.K;
   for (int j = tid; j < C; j += kThreads) {
-    float s = score[j];
-    if (s != s) score[j] = -INFINITY;  // a NaN score ranks last
-  }
-  __syncthreads();
-  for (int j = tid; j < C; j += kThreads) {
     const float sj = score[j];
-    const int cj = cand[j];
-    int r = 0;
-    for (int jj = 0; jj < C; ++jj) {
+    int r = 0, jj = 0;
+    for (; jj + 4 <= C; jj += 4) {
+      const float4 s4 = *reinterpret_cast<const float4*>(score + jj);
+      r += (s4.x > sj) | ((s4.x == sj) & (jj + 0 < j));
+      r += (s4.y > sj) | ((s4.y == sj) & (jj + 1 < j));
+      r += (s4.z > sj) | ((s4.z == sj) & (jj + 2 < j));
+      r += (s4.w > sj) | ((s4.w == sj) & (jj + 3 < j));
+    }
+    for (; jj < C; ++jj) {
       const float s2 = score[jj];
-      r += (s2 > sj) || (s2 == sj && cand[jj] < cj);
+      r += (s2 > sj) | ((s2 == sj) & (jj < j));
     }
     rank[j] = r;
   }
   __syncthreads();
-  // position among kept, in candidate (= ascending index) order
-  for (int j = tid; j < C; j += kThreads) {
-    int p = 0;
-    if (rank[j] < K)
-      for (int jj = 0; jj < j; ++jj) p += rank[jj] < K;
-    pos[j] = p;
-  }
-  __syncthreads();
-  for (int j = tid; j < C; j += kThreads) {
-    if (rank[j] < K) {
-      kept[pos[j]] = cand[j];
-      kscore[pos[j]] = score[j];
-    } else if (rank[j] == K && tr_scores) {
+  // stream compaction of the kept set (rank < K) in index order
+  int base = 0;
+  for (int j0 = 0; j0 < C; j0 += kThreads) {
+    const int j = j0 + tid;
+    const bool keep = j < C && rank[j] < K;
+    const unsigned long long m = __ballot(keep);
+    if (l == 0) wsum[w] = __popcll(m);
+    __syncthreads();
+    int off = base, tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      off += ww < w ? wsum[ww] : 0;
+      tot += wsum[ww];
+    }
+    if (keep) {
+      const int p = off + __popcll(m & ((1ull << l) - 1ull));
+      kept[p] = cand[j];
+      kscore[p] = score[j];
+    } else if (j < C && rank[j] == K && tr_scores) {
       tr_scores[level * (K + 1) + K] = score[j];  // best rejected candidate
     }
+    base += tot;
+    __syncthreads();
   }
-  __syncthreads();
   if (tr_ids) {
     for (int j = tid; j < K; j += kThreads) tr_ids[level * K + j] = kept[j];
   }
@@ -119,26 +142,22 @@ __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* c
 
 // Candidates of one level into cand[]; returns the count.  Must be called by
 // every thread (ends with a barrier).
-__device__ int build_candidates(const PyrGeom& g, int level, int64_t diag, const int* kept,
+__device__ int build_candidates(const PyrGeom& g, int level, const int* s_anc, const int* kept,
                                 int nkept, int* cand) {
   const int b = g.branching;
-  const int64_t anc = diag / ipow(b, level);
-  int C;
-  int64_t base;
-  int nchild;
+  const int anc = s_anc[level];
+  int C, base, nchild;
   if (level == g.L - 1) {
-    C = (int)anc;
+    C = anc;
     nchild = 0;
     base = 0;
   } else {
-    const int64_t anc_up = diag / ipow(b, level + 1);
     nchild = nkept * b;
-    base = anc_up * b;
-    C = nchild + (int)(anc - base);
+    base = s_anc[level + 1] * b;
+    C = nchild + (anc - base);
   }
-  for (int j = threadIdx.x; j < C; j += kThreads) {
-    cand[j] = j < nchild ? kept[j / b] * b + j % b : (int)(base + (j - nchild));
-  }
+  for (int j = threadIdx.x; j < C; j += kThreads)
+    cand[j] = j < nchild ? kept[j / b] * b + j % b : base + (j - nchild);
   __syncthreads();
   return C;
 }
@@ -158,9 +177,55 @@ __device__ void keep_all(const PyrGeom& g, int C, int level, const int* cand, in
   __syncthreads();
 }
 
+__device__ __forceinline__ void write_route(const PyrGeom& g, int64_t unit, const int* kept,
+                                            int nk, int diag, int32_t* sel) {
+  int32_t* out = sel + unit * (g.K + 1);
+  for (int j = threadIdx.x; j <= g.K; j += kThreads) out[j] = j < nk ? kept[j] : (j == nk ? diag : -1);
+}
+
 // ---------------------------------------------------------------------------
 // bf16 prefill path: MFMA scoring.  MT = 16-row M tiles per wave.
 // ---------------------------------------------------------------------------
+
+// Pooled keys of chunk c (fp32 rows of the level) -> registers.  Slot s of a
+// thread is float4 number tid + s*kThreads of the chunk's kChunk x D block.
+template <int D>
+__device__ __forceinline__ void load_chunk(const float* lvl, const int* cand, int C, int c,
+                                           float4* stg) {
+  constexpr int SLOTS = kChunk * (D / 4) / kThreads;
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int idx = threadIdx.x + s * kThreads;
+    const int cc = idx / (D / 4), d4 = idx % (D / 4);
+    const int j = c * kChunk + cc;
+    stg[s] = j < C ? *reinterpret_cast<const float4*>(lvl + (int64_t)cand[j] * D + d4 * 4)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// Registers -> hi/lo bf16 rows of one LDS stage.
+template <int D>
+__device__ __forceinline__ void store_chunk(const float4* stg, bf16_t* hi, bf16_t* lo) {
+  constexpr int SLOTS = kChunk * (D / 4) / kThreads;
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int idx = threadIdx.x + s * kThreads;
+    const int cc = idx / (D / 4), d4 = idx % (D / 4);
+    const float4 x = stg[s];
+    bf16x4 h, r;
+    h[0] = (__bf16)x.x;
+    h[1] = (__bf16)x.y;
+    h[2] = (__bf16)x.z;
+    h[3] = (__bf16)x.w;
+    r[0] = (__bf16)(x.x - (float)h[0]);
+    r[1] = (__bf16)(x.y - (float)h[1]);
+    r[2] = (__bf16)(x.z - (float)h[2]);
+    r[3] = (__bf16)(x.w - (float)h[3]);
+    *reinterpret_cast<bf16x4*>(hi + cc * (D + 8) + d4 * 4) = h;
+    *reinterpret_cast<bf16x4*>(lo + cc * (D + 8) + d4 * 4) = r;
+  }
+}
+
 template <int D, int MT>
 __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict__ q,
                                                         const float* __restrict__ pyr,
@@ -168,27 +233,33 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
                                                         int32_t* __restrict__ trace_ids,
                                                         float* __restrict__ trace_scores,
                                                         PyrGeom g) {
+  static_assert(kChunk * (D / 4) % kThreads == 0, "chunk must split evenly");
+  constexpr int SLOTS = kChunk * (D / 4) / kThreads;
+  constexpr int STAGE = 2 * kChunk * (D + 8);  // bf16 elements per stage (hi then lo)
   extern __shared__ __align__(16) unsigned char smem[];
-  const SelLayout lay(g.K, g.branching, mfma_scratch_bytes<D>());
+  const SelLayout lay(g.K, g.branching, D, true);
   int* kept = reinterpret_cast<int*>(smem + lay.off_kept);
   float* kscore = reinterpret_cast<float*>(smem + lay.off_kscore);
   int* cand = reinterpret_cast<int*>(smem + lay.off_cand);
   float* score = reinterpret_cast<float*>(smem + lay.off_score);
   int* rank = reinterpret_cast<int*>(smem + lay.off_rank);
-  int* pos = reinterpret_cast<int*>(smem + lay.off_pos);
-  float2* part = reinterpret_cast<float2*>(smem + lay.off_scratch);
-  bf16_t* khi = reinterpret_cast<bf16_t*>(smem + lay.off_scratch + kWaves * kChunk * 8);
-  bf16_t* klo = khi + kChunk * (D + 8);
+  float2* part = reinterpret_cast<float2*>(smem + lay.off_part);
+  bf16_t* hl = reinterpret_cast<bf16_t*>(smem + lay.off_hl);
   __shared__ int s_nkept;
+  __shared__ int s_anc[PYR_MAX_LEVELS];
 
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
   const int64_t unit = blockIdx.x;
   const int i = (int)(unit % g.nqb);
   const int64_t bhk = unit / g.nqb;  // b * Hk + hk
   const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
-  const int64_t diag = i;
+  const int diag = i;
   const int RW = MT * 16;  // rows per wave
   const float sl2 = g.scale * PYR_LOG2E;
+  const int cmax = lay.cmax;
+
+  if (tid == 0) s_nkept = 0;
+  ancestors(g, diag, s_anc);
 
   // Q fragments (A operand): lane holds row (l % 16) of each M tile and the
   // 8 consecutive d at 32*ks + 8*(l/16).
@@ -198,55 +269,46 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
   for (int mt = 0; mt < MT; ++mt) {
     const int ra = w * RW + mt * 16 + (l % 16);
     const int h = ra / PYR_BLOCK, t = ra % PYR_BLOCK;
-    const int64_t tok = (int64_t)i * PYR_BLOCK + t;
+    const int64_t tok = min<int64_t>((int64_t)i * PYR_BLOCK + t, g.Tq - 1);
     const bf16_t* qrow = q + (((int64_t)bi * g.Hq + (int64_t)hk * g.G + h) * g.Tq + tok) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      qa[mt][ks] = tok < g.Tq ? ld16(qrow + ks * 32 + 8 * (l / 16)) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < D / 32; ++ks) qa[mt][ks] = ld16(qrow + ks * 32 + 8 * (l / 16));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rc = w * RW + mt * 16 + 4 * (l / 16) + j;
-      const int64_t tc = (int64_t)i * PYR_BLOCK + rc % PYR_BLOCK;
-      if (tc < g.Tq) rowvalid |= 1u << (mt * 4 + j);
+      if ((int64_t)i * PYR_BLOCK + rc % PYR_BLOCK < g.Tq) rowvalid |= 1u << (mt * 4 + j);
     }
   }
 
   const float* slab = pyr + bhk * g.n_tot * D;
   int32_t* tr_ids = trace_ids ? trace_ids + unit * g.L * g.K : nullptr;
   float* tr_sc = trace_scores ? trace_scores + unit * g.L * (g.K + 1) : nullptr;
-  if (tid == 0) s_nkept = 0;
   __syncthreads();
 
   for (int level = g.L - 1; level >= 0; --level) {
-    const int C = build_candidates(g, level, diag, kept, s_nkept, cand);
+    const int C = build_candidates(g, level, s_anc, kept, s_nkept, cand);
     if (C <= g.K) {
       keep_all(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
       continue;
     }
     const float* lvl = slab + g.loff[level] * D;
-    for (int c0 = 0; c0 < C; c0 += kChunk) {
-      const int nch = min(kChunk, C - c0);
-      // stage pooled keys of this chunk as hi/lo bf16 pairs
-      for (int idx = tid; idx < kChunk * (D / 4); idx += kThreads) {
-        const int cc = idx / (D / 4), d4 = idx % (D / 4);
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (cc < nch) x = *reinterpret_cast<const float4*>(lvl + (int64_t)cand[c0 + cc] * D + d4 * 4);
-        const uint32_t h0 = f32_to_bf16_bits(x.x), h1 = f32_to_bf16_bits(x.y);
-        const uint32_t h2 = f32_to_bf16_bits(x.z), h3 = f32_to_bf16_bits(x.w);
-        const uint32_t l0 = f32_to_bf16_bits(x.x - bf16_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_bits(x.y - bf16_to_f32(h1));
-        const uint32_t l2 = f32_to_bf16_bits(x.z - bf16_to_f32(h2));
-        const uint32_t l3 = f32_to_bf16_bits(x.w - bf16_to_f32(h3));
-        *reinterpret_cast<uint2*>(khi + cc * (D + 8) + d4 * 4) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        *reinterpret_cast<uint2*>(klo + cc * (D + 8) + d4 * 4) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-      }
-      __syncthreads();
-      for (int nt = 0; nt * 16 < nch; ++nt) {
+    const int nchunks = (C + kChunk - 1) / kChunk;
+    float4 stg[SLOTS];
+    load_chunk<D>(lvl, cand, C, 0, stg);
+    store_chunk<D>(stg, hl, hl + kChunk * (D + 8));
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      if (c + 1 < nchunks) load_chunk<D>(lvl, cand, C, c + 1, stg);  // in flight during the MFMAs
+      const bf16_t* hi = hl + (c & 1) * STAGE;
+      const bf16_t* lo = hi + kChunk * (D + 8);
+#pragma unroll
+      for (int nt = 0; nt < kChunk / 16; ++nt) {
+        if (c * kChunk + nt * 16 >= C) break;  // uniform
         f32x4 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16_t* bh_row = khi + (nt * 16 + (l % 16)) * (D + 8) + 8 * (l / 16);
-        const bf16_t* bl_row = klo + (nt * 16 + (l % 16)) * (D + 8) + 8 * (l / 16);
+        const bf16_t* bh_row = hi + (nt * 16 + (l % 16)) * (D + 8) + 8 * (l / 16);
+        const bf16_t* bl_row = lo + (nt * 16 + (l % 16)) * (D + 8) + 8 * (l / 16);
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
           const bf16x8 bhv = as_bf16x8(*reinterpret_cast<const uint4*>(bh_row + ks * 32));
@@ -257,45 +319,50 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
             acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), blv, acc[mt], 0, 0, 0);
           }
         }
+        // this wave's LogSumExp over its rows, per candidate (lane column l % 16)
         float m = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (rowvalid >> (mt * 4 + j) & 1u) m = fmaxf(m, acc[mt][j] * sl2);
+            if (rowvalid >> (mt * 4 + j) & 1u) m = fmaxf(m, acc[mt][j]);
         float s = 0.f;
+        m *= sl2;
         if (m != -INFINITY) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              if (rowvalid >> (mt * 4 + j) & 1u) s += exp2f(acc[mt][j] * sl2 - m);
+              if (rowvalid >> (mt * 4 + j) & 1u)
+                s += __builtin_amdgcn_exp2f(fmaf(acc[mt][j], sl2, -m));
         }
 #pragma unroll
         for (int o = 16; o < 64; o <<= 1) {
           const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
           lse2_merge(m, s, m2, s2);
         }
-        if (l < 16) part[w * kChunk + nt * 16 + l] = make_float2(m, s);
+        if (l < 16) part[w * cmax + c * kChunk + nt * 16 + l] = make_float2(m, s);
       }
-      __syncthreads();
-      for (int cc = tid; cc < nch; cc += kThreads) {
-        float m = -INFINITY, s = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-          const float2 p = part[ww * kChunk + cc];
-          lse2_merge(m, s, p.x, p.y);
-        }
-        score[c0 + cc] = (m + log2f(s)) * PYR_LN2;
+      if (c + 1 < nchunks) {
+        bf16_t* nhi = hl + ((c + 1) & 1) * STAGE;
+        store_chunk<D>(stg, nhi, nhi + kChunk * (D + 8));
       }
       __syncthreads();
     }
-    top_k_and_trace(g, C, level, cand, score, rank, pos, kept, kscore, &s_nkept, tr_ids, tr_sc);
+    for (int j = tid; j < C; j += kThreads) {
+      float m = -INFINITY, s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float2 p = part[ww * cmax + j];
+        lse2_merge(m, s, p.x, p.y);
+      }
+      const float sc = (m + log2f(s)) * PYR_LN2;
+      score[j] = sc == sc ? sc : -INFINITY;  // a NaN score ranks last
+    }
+    __syncthreads();
+    top_k_and_trace(g, C, level, cand, score, rank, kept, kscore, &s_nkept, tr_ids, tr_sc);
   }
-
-  int32_t* out = sel + unit * (g.K + 1);
-  const int nk = s_nkept;
-  for (int j = tid; j <= g.K; j += kThreads) out[j] = j < nk ? kept[j] : (j == nk ? (int)diag : -1);
+  write_route(g, unit, kept, s_nkept, diag, sel);
 }
 
 // ---------------------------------------------------------------------------
@@ -310,26 +377,27 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
                                                         float* __restrict__ trace_scores,
                                                         PyrGeom g) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const SelLayout lay(g.K, g.branching, kZbuf * 4);
+  const SelLayout lay(g.K, g.branching, D, false);
   int* kept = reinterpret_cast<int*>(smem + lay.off_kept);
   float* kscore = reinterpret_cast<float*>(smem + lay.off_kscore);
   int* cand = reinterpret_cast<int*>(smem + lay.off_cand);
   float* score = reinterpret_cast<float*>(smem + lay.off_score);
   int* rank = reinterpret_cast<int*>(smem + lay.off_rank);
-  int* pos = reinterpret_cast<int*>(smem + lay.off_pos);
-  float* zbuf = reinterpret_cast<float*>(smem + lay.off_scratch);
+  float* zbuf = reinterpret_cast<float*>(smem + lay.off_zbuf);
   __shared__ int s_nkept;
+  __shared__ int s_anc[PYR_MAX_LEVELS];
 
   const int tid = threadIdx.x;
   const int64_t unit = blockIdx.x;
   const int i = (int)(unit % g.nqb);
   const int64_t bhk = unit / g.nqb;
   const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
-  int64_t tok0, ntok, diag;
+  int64_t tok0, ntok;
+  int diag;
   if (g.decode) {
     tok0 = 0;
     ntok = 1;
-    diag = (g.Tk - 1) / PYR_BLOCK;
+    diag = (int)((g.Tk - 1) / PYR_BLOCK);
   } else {
     tok0 = (int64_t)i * PYR_BLOCK;
     ntok = min<int64_t>(PYR_BLOCK, g.Tq - tok0);
@@ -342,10 +410,11 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
   float* tr_sc = trace_scores ? trace_scores + unit * g.L * (g.K + 1) : nullptr;
   const int chv = max(1, kZbuf / R);
   if (tid == 0) s_nkept = 0;
+  ancestors(g, diag, s_anc);
   __syncthreads();
 
   for (int level = g.L - 1; level >= 0; --level) {
-    const int C = build_candidates(g, level, diag, kept, s_nkept, cand);
+    const int C = build_candidates(g, level, s_anc, kept, s_nkept, cand);
     if (C <= g.K) {
       keep_all(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
       continue;
@@ -374,16 +443,14 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
         for (int r = 0; r < R; ++r) m = fmaxf(m, zbuf[cc * R + r]);
         float s = 0.f;
         for (int r = 0; r < R; ++r) s += exp2f(zbuf[cc * R + r] - m);
-        score[c0 + cc] = (m + log2f(s)) * PYR_LN2;
+        const float sc = (m + log2f(s)) * PYR_LN2;
+        score[c0 + cc] = sc == sc ? sc : -INFINITY;  // a NaN score ranks last
       }
       __syncthreads();
     }
-    top_k_and_trace(g, C, level, cand, score, rank, pos, kept, kscore, &s_nkept, tr_ids, tr_sc);
+    top_k_and_trace(g, C, level, cand, score, rank, kept, kscore, &s_nkept, tr_ids, tr_sc);
   }
-
-  int32_t* out = sel + unit * (g.K + 1);
-  const int nk = s_nkept;
-  for (int j = tid; j <= g.K; j += kThreads) out[j] = j < nk ? kept[j] : (j == nk ? (int)diag : -1);
+  write_route(g, unit, kept, s_nkept, diag, sel);
 }
 
 int mfma_tiles(const PyrGeom& g, int dtype) {
@@ -404,8 +471,8 @@ hipError_t launch_select_d(const PyrGeom& g, int dtype, const void* q, const flo
   if (units == 0) return hipSuccess;
   const int mt = mfma_tiles(g, dtype);
   const dim3 grid((unsigned)units), block(kThreads);
+  const size_t lds = SelLayout(g.K, g.branching, D, mt != 0).total;
   if (mt) {
-    const size_t lds = SelLayout(g.K, g.branching, mfma_scratch_bytes<D>()).total;
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     switch (mt) {
       case 1: hipLaunchKernelGGL((select_mfma<D, 1>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
@@ -413,14 +480,12 @@ hipError_t launch_select_d(const PyrGeom& g, int dtype, const void* q, const flo
       case 4: hipLaunchKernelGGL((select_mfma<D, 4>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
       default: hipLaunchKernelGGL((select_mfma<D, 8>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
     }
+  } else if (dtype == 1) {
+    hipLaunchKernelGGL((select_valu<bf16_t, D>), grid, block, lds, st,
+                       static_cast<const bf16_t*>(q), pyr, sel, tid_, tsc, g);
   } else {
-    const size_t lds = SelLayout(g.K, g.branching, kZbuf * 4).total;
-    if (dtype == 1)
-      hipLaunchKernelGGL((select_valu<bf16_t, D>), grid, block, lds, st,
-                         static_cast<const bf16_t*>(q), pyr, sel, tid_, tsc, g);
-    else
-      hipLaunchKernelGGL((select_valu<float, D>), grid, block, lds, st,
-                         static_cast<const float*>(q), pyr, sel, tid_, tsc, g);
+    hipLaunchKernelGGL((select_valu<float, D>), grid, block, lds, st,
+                       static_cast<const float*>(q), pyr, sel, tid_, tsc, g);
   }
   return hipGetLastError();
 }
@@ -428,10 +493,7 @@ hipError_t launch_select_d(const PyrGeom& g, int dtype, const void* q, const flo
 }  // namespace
 
 size_t pyr_select_lds_bytes(const PyrGeom& g, int dtype) {
-  if (mfma_tiles(g, dtype))
-    return SelLayout(g.K, g.branching,
-                     g.D == 64 ? mfma_scratch_bytes<64>() : mfma_scratch_bytes<128>()).total;
-  return SelLayout(g.K, g.branching, kZbuf * 4).total;
+  return SelLayout(g.K, g.branching, g.D, mfma_tiles(g, dtype) != 0).total;
 }
 
 hipError_t pyr_launch_select(const PyrGeom& g, int dtype, const void* q, const float* pyr,
