@@ -79,65 +79,102 @@ __device__ void ancestors(const PyrGeom& g, int diag, int* s_anc) {
   }
 }
 
-// Rank every candidate, keep the top K in ascending index order, write trace.
-// Candidates are ascending by node index, so "lower index wins a tie" is
-// "lower position wins": rank(j) = #{s > s_j} + #{jj < j : s == s_j}.  Scores
-// are never NaN (callers map NaN to -inf).
+// Order-preserving map of a score to an unsigned key: a larger score gives a
+// larger key, -inf gives 0x007fffff, and 0 is left free to mark "no candidate"
+// (scores are never NaN).
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// One 64-candidate chunk of the in-order compaction of the kept set.
+__device__ __forceinline__ void keep_chunk(int j, uint32_t kj, int C, uint32_t T, int need,
+                                           unsigned long long lt, const int* cand,
+                                           const float* score, int* kept, float* kscore,
+                                           int& pos, int& ties, uint32_t& rej) {
+  const bool eq = kj == T && j < C;
+  const unsigned long long em = __ballot(eq);
+  const bool keep = kj > T || (eq && ties + __popcll(em & lt) < need);
+  const unsigned long long km = __ballot(keep);
+  if (keep) {
+    const int p = pos + __popcll(km & lt);
+    kept[p] = cand[j];
+    kscore[p] = score[j];
+  } else if (j < C && kj > rej) {
+    rej = kj;
+  }
+  pos += __popcll(km);
+  ties += __popcll(em);
+}
+
+// Keep the top K of C > K candidates in ascending index order and write the
+// trace.  Candidates are ascending by node index, so "lower index wins a tie"
+// is "lower position wins": the kept set is every candidate with a score above
+// the K-th largest, T, plus the first (by position) of those equal to T until
+// there are K.  Wave 0 finds T bit by bit (the largest key with at least K
+// keys >= it) with ballots over the candidates, four per lane in registers
+// (more are re-read from LDS), then compacts the kept set in index order.
 __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* cand,
                                 const float* score, int* rank, int* kept, float* kscore,
                                 int* nkept, int32_t* tr_ids, float* tr_scores) {
-  __shared__ int wsum[kWaves];
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
   const int K = g.K;
-  for (int j = tid; j < C; j += kThreads) {
-    const float sj = score[j];
-    int r = 0, jj = 0;
-    for (; jj + 4 <= C; jj += 4) {
-      const float4 s4 = *reinterpret_cast<const float4*>(score + jj);
-      r += (s4.x > sj) | ((s4.x == sj) & (jj + 0 < j));
-      r += (s4.y > sj) | ((s4.y == sj) & (jj + 1 < j));
-      r += (s4.z > sj) | ((s4.z == sj) & (jj + 2 < j));
-      r += (s4.w > sj) | ((s4.w == sj) & (jj + 3 < j));
+  const int nch = (C + 63) / 64;
+  if (w == 0) {
+    uint32_t kr[4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int j = ch * 64 + l;
+      kr[ch] = j < C ? score_key(score[j]) : 0u;
     }
-    for (; jj < C; ++jj) {
-      const float s2 = score[jj];
-      r += (s2 > sj) | ((s2 == sj) & (jj < j));
+    uint32_t* keys = reinterpret_cast<uint32_t*>(rank);
+    for (int ch = 4; ch < nch; ++ch) {
+      const int j = ch * 64 + l;
+      keys[j] = j < C ? score_key(score[j]) : 0u;
     }
-    rank[j] = r;
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) cnt += __popcll(__ballot(kr[ch] >= t));
+      for (int ch = 4; ch < nch; ++ch) cnt += __popcll(__ballot(keys[ch * 64 + l] >= t));
+      if (cnt >= K) T = t;
+    }
+    int above = 0;  // candidates strictly above T (fewer than K)
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) above += __popcll(__ballot(kr[ch] > T));
+    for (int ch = 4; ch < nch; ++ch) above += __popcll(__ballot(keys[ch * 64 + l] > T));
+    const int need = K - above;  // ties at T to keep, lowest positions first
+    const unsigned long long lt = (1ull << l) - 1ull;
+    int pos = 0, ties = 0;
+    uint32_t rej = 0;  // best rejected key of this lane
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+      if (ch < nch)
+        keep_chunk(ch * 64 + l, kr[ch], C, T, need, lt, cand, score, kept, kscore, pos, ties, rej);
+    for (int ch = 4; ch < nch; ++ch)
+      keep_chunk(ch * 64 + l, keys[ch * 64 + l], C, T, need, lt, cand, score, kept, kscore, pos,
+                 ties, rej);
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint32_t r2 = (uint32_t)__shfl_xor((int)rej, o, 64);
+      rej = r2 > rej ? r2 : rej;
+    }
+    if (l == 0) {
+      if (tr_scores) tr_scores[level * (K + 1) + K] = key_score(rej);  // best rejected candidate
+      *nkept = K;
+    }
   }
   __syncthreads();
-  // stream compaction of the kept set (rank < K) in index order
-  int base = 0;
-  for (int j0 = 0; j0 < C; j0 += kThreads) {
-    const int j = j0 + tid;
-    const bool keep = j < C && rank[j] < K;
-    const unsigned long long m = __ballot(keep);
-    if (l == 0) wsum[w] = __popcll(m);
-    __syncthreads();
-    int off = base, tot = 0;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      off += ww < w ? wsum[ww] : 0;
-      tot += wsum[ww];
-    }
-    if (keep) {
-      const int p = off + __popcll(m & ((1ull << l) - 1ull));
-      kept[p] = cand[j];
-      kscore[p] = score[j];
-    } else if (j < C && rank[j] == K && tr_scores) {
-      tr_scores[level * (K + 1) + K] = score[j];  // best rejected candidate
-    }
-    base += tot;
-    __syncthreads();
-  }
   if (tr_ids) {
     for (int j = tid; j < K; j += kThreads) tr_ids[level * K + j] = kept[j];
   }
   if (tr_scores) {
     for (int j = tid; j < K; j += kThreads) tr_scores[level * (K + 1) + j] = kscore[j];
   }
-  if (tid == 0) *nkept = K;
-  __syncthreads();
 }
 
 // Candidates of one level into cand[]; returns the count.  Must be called by
@@ -226,6 +263,51 @@ __device__ __forceinline__ void store_chunk(const float4* stg, bf16_t* hi, bf16_
   }
 }
 
+// Values of a lane's partner in the other 16-lane row (xor 16) or the other
+// 32-lane half (xor 32): the swap hands each lane the pair (even, odd) of the
+// two lanes, so a symmetric merge of the pair needs no select.
+__device__ __forceinline__ void lse_swap_merge16(float& m, float& s) {
+  const auto rm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  const auto rs = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  m = __uint_as_float(rm[0]);
+  s = __uint_as_float(rs[0]);
+  lse2_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
+}
+__device__ __forceinline__ void lse_swap_merge32(float& m, float& s) {
+  const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  m = __uint_as_float(rm[0]);
+  s = __uint_as_float(rs[0]);
+  lse2_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
+}
+
+// LogSumExp (log2 domain: max m and sum s of 2^(x - m)) of one wave's rows for
+// the 16 candidates of an N tile; lane l ends with the value of candidate
+// l % 16.  Row j of M tile mt in the C layout is row 4*(l/16) + j; FULL skips
+// the per-row validity bits.
+template <int MT, bool FULL>
+__device__ __forceinline__ void tile_lse(const f32x4 (&acc)[MT], uint32_t rowvalid, float sl2,
+                                         float& m, float& s) {
+  m = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (FULL || (rowvalid >> (mt * 4 + j) & 1u)) m = fmaxf(m, acc[mt][j]);
+  s = 0.f;
+  m *= sl2;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (FULL || (rowvalid >> (mt * 4 + j) & 1u))
+          s += __builtin_amdgcn_exp2f(fmaf(acc[mt][j], sl2, -m));
+  }
+  lse_swap_merge16(m, s);
+  lse_swap_merge32(m, s);
+}
+
 template <int D, int MT>
 __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict__ q,
                                                         const float* __restrict__ pyr,
@@ -280,6 +362,7 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
     }
   }
 
+  const bool full = (int64_t)(i + 1) * PYR_BLOCK <= g.Tq;  // every row of the unit is real
   const float* slab = pyr + bhk * g.n_tot * D;
   int32_t* tr_ids = trace_ids ? trace_ids + unit * g.L * g.K : nullptr;
   float* tr_sc = trace_scores ? trace_scores + unit * g.L * (g.K + 1) : nullptr;
@@ -320,27 +403,11 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
           }
         }
         // this wave's LogSumExp over its rows, per candidate (lane column l % 16)
-        float m = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (rowvalid >> (mt * 4 + j) & 1u) m = fmaxf(m, acc[mt][j]);
-        float s = 0.f;
-        m *= sl2;
-        if (m != -INFINITY) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (rowvalid >> (mt * 4 + j) & 1u)
-                s += __builtin_amdgcn_exp2f(fmaf(acc[mt][j], sl2, -m));
-        }
-#pragma unroll
-        for (int o = 16; o < 64; o <<= 1) {
-          const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
-          lse2_merge(m, s, m2, s2);
-        }
+        float m, s;
+        if (full)
+          tile_lse<MT, true>(acc, rowvalid, sl2, m, s);
+        else
+          tile_lse<MT, false>(acc, rowvalid, sl2, m, s);
         if (l < 16) part[w * cmax + c * kChunk + nt * 16 + l] = make_float2(m, s);
       }
       if (c + 1 < nchunks) {
