@@ -87,10 +87,12 @@ def attn_work(cfg):
     return flops, byts
 
 
-def build_bytes(cfg, n_tot):
+def build_bytes(cfg, n_tot, planes):
+    """Keys read once plus every pyramid plane written (fp32 means, and the
+    bf16 hi/lo plane of bf16 problems)."""
     s = 2 if cfg.dtype.itemsize == 2 else 4
     bh = cfg.batch * cfg.n_kv_heads
-    return bh * (cfg.kv_len * cfg.head_dim * s + n_tot * cfg.head_dim * 4)
+    return bh * (cfg.kv_len * cfg.head_dim * s + planes * n_tot * cfg.head_dim * 4)
 
 
 def select_work(cfg, sel_levels_cands):
@@ -272,7 +274,7 @@ def main():
 
     a_flops, a_bytes = attn_work(cfg)
     n_tot = H.pyr_pyramid_nodes(p)
-    b_bytes = build_bytes(cfg, n_tot)
+    b_bytes = build_bytes(cfg, n_tot, H.pyr_pyramid_planes(p))
     s_flops, s_bytes = select_work(cfg, scored_candidates(cfg))
     t_build, t_sel, t_attn = (x / 1e3 for x in stage_ms)
     achieved = a_flops / t_attn / 1e12

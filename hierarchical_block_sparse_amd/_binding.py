@@ -59,6 +59,7 @@ def lib():
             ("pyr_num_levels", ctypes.c_int32, [P]),
             ("pyr_level_offset", ctypes.c_int64, [P, ctypes.c_int32]),
             ("pyr_pyramid_nodes", ctypes.c_int64, [P]),
+            ("pyr_pyramid_planes", ctypes.c_int32, [P]),
             ("pyr_num_query_blocks", ctypes.c_int64, [P]),
             ("pyr_attn_workspace_bytes", ctypes.c_size_t, [P]),
             ("pyr_build_pyramid", st, [P, vp, vp, vp]),
@@ -148,6 +149,15 @@ def pyr_pyramid_nodes(p: Problem) -> int:
     return lib().pyr_pyramid_nodes(ctypes.byref(p.c()))
 
 
+def pyr_pyramid_planes(p: Problem) -> int:
+    return lib().pyr_pyramid_planes(ctypes.byref(p.c()))
+
+
+def pyramid_shape(p: Problem):
+    """[B, Hk, planes, nodes, d]: the float32 pyramid buffer of a problem."""
+    return (p.batch, p.n_kv_heads, pyr_pyramid_planes(p), pyr_pyramid_nodes(p), p.head_dim)
+
+
 def pyr_num_query_blocks(p: Problem) -> int:
     return lib().pyr_num_query_blocks(ctypes.byref(p.c()))
 
@@ -164,16 +174,14 @@ def pyr_abi_version() -> int:
 
 def pyr_build_pyramid(p: Problem, k, pyramid, stream=None):
     _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_len, p.head_dim), p.dtype)
-    _expect(pyramid, "pyramid", (p.batch, p.n_kv_heads, pyr_pyramid_nodes(p), p.head_dim),
-            torch.float32)
+    _expect(pyramid, "pyramid", pyramid_shape(p), torch.float32)
     _check(lib().pyr_build_pyramid(ctypes.byref(p.c()), _ptr(k), _ptr(pyramid), _stream(stream)))
 
 
 def pyr_select_topk(p: Problem, q, pyramid, sel, trace_ids=None, trace_scores=None, stream=None):
     nqb, L = pyr_num_query_blocks(p), pyr_num_levels(p)
     _expect(q, "q", (p.batch, p.n_q_heads, p.q_len, p.head_dim), p.dtype)
-    _expect(pyramid, "pyramid", (p.batch, p.n_kv_heads, pyr_pyramid_nodes(p), p.head_dim),
-            torch.float32)
+    _expect(pyramid, "pyramid", pyramid_shape(p), torch.float32)
     _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
     _expect(trace_ids, "trace_ids", (p.batch, p.n_kv_heads, nqb, L, p.top_k), torch.int32)
     _expect(trace_scores, "trace_scores", (p.batch, p.n_kv_heads, nqb, L, p.top_k + 1),
@@ -203,8 +211,7 @@ def pyr_block_sparse_attn(p: Problem, q, k, v, sel, o, lse=None, workspace=None,
 # ---- allocating conveniences (torch allocates; the library computes) ----
 
 def alloc_pyramid(p: Problem, device="cuda"):
-    return torch.empty((p.batch, p.n_kv_heads, pyr_pyramid_nodes(p), p.head_dim),
-                       dtype=torch.float32, device=device)
+    return torch.empty(pyramid_shape(p), dtype=torch.float32, device=device)
 
 
 def alloc_sel(p: Problem, device="cuda"):

@@ -89,6 +89,7 @@ pyr_status resolve(const pyr_problem* p, PyrGeom* g) {
   g->branching = p->branching;
   g->K = p->top_k;
   g->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  g->planes = p->dtype == PYR_BF16 ? 2 : 1;
   const int L = level_sizes(g->nb, p->branching, g->lsize, g->loff, &g->n_tot);
   if (L < 0) return fail(PYR_ERR_UNSUPPORTED, "more than %d pyramid levels", PYR_MAX_LEVELS);
   g->L = L;
@@ -122,6 +123,11 @@ int64_t pyr_level_offset(const pyr_problem* p, int32_t level) {
 int64_t pyr_pyramid_nodes(const pyr_problem* p) {
   PyrGeom g;
   return resolve(p, &g) == PYR_OK ? g.n_tot : -1;
+}
+
+int32_t pyr_pyramid_planes(const pyr_problem* p) {
+  PyrGeom g;
+  return resolve(p, &g) == PYR_OK ? g.planes : -1;
 }
 
 int64_t pyr_num_query_blocks(const pyr_problem* p) {

@@ -83,6 +83,19 @@ __device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s
   m = mx;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() carries a
+// workgroup fence, and a fence waits for every direct global-to-LDS load in
+// flight (the compiler counts them as pending LDS writes), which would undo a
+// prefetch; code that waits for its own loads explicitly uses this instead.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier; lgkmcnt(0) completes this wave's LDS accesses first.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Full-wavefront reductions (64 lanes).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

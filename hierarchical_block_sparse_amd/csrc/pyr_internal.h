@@ -12,6 +12,7 @@
 struct PyrGeom {
   int64_t Tq, Tk;          // query / key lengths
   int64_t n_tot;           // pyramid nodes per (batch, KV head) slab
+  int32_t planes;          // pyramid planes: 1 (fp32 problems) or 2 (bf16: + hi/lo split)
   int32_t B, Hq, Hk, G, D; // batch, heads, group size Hq/Hk, head dim
   int32_t nb;              // finest-level blocks: ceil(Tk / 64)
   int32_t nqb;             // query blocks per (batch, KV head)

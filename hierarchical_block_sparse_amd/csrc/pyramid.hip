@@ -4,8 +4,11 @@
 // coarse-to-fine hierarchy of O(log N) levels.  PHBA (Prefix-State Hybrid
 // Block Attention), §A.1.2: a block summary is the mean of the block's valid
 // key rows, accumulated in fp32 registers.  Here node m of level l is the mean
-// of all key tokens under it; levels are stored finest first in one fp32 slab
-// per (batch, KV head).
+// of all key tokens under it; levels are stored finest first in one fp32 plane
+// per (batch, KV head).  For bf16 problems a second plane repeats every mean
+// as a bf16 pair (hi = bf16(x), lo = bf16(x - hi)), the operands of the
+// selection's matrix-core scorer, so that the scorer can stream them into LDS
+// without converting.
 //
 // Two kernels:
 //  * build_chunk: one workgroup per chunk of `chunk` = b^s consecutive 64-token
@@ -27,6 +30,22 @@ constexpr int kThreads = 256;
 constexpr int kChunkMax = 16;  // finest blocks per workgroup (b^s <= 16)
 constexpr int kBatch = 4;      // blocks whose loads are in flight together
 
+// Store the mean x of column dcol of node `node` of a slab: plane 0 in fp32,
+// and for two-plane slabs the bf16 pair in plane 1 (the hi row, then the lo
+// row, in the node's 4D bytes).
+template <int D>
+__device__ __forceinline__ void put_node(const PyrGeom& g, float* slab, int64_t node, int dcol,
+                                         float x) {
+  slab[node * D + dcol] = x;
+  if (g.planes == 2) {
+    bf16_t* split = reinterpret_cast<bf16_t*>(slab + g.n_tot * D) + node * 2 * D;
+    const __bf16 hi = (__bf16)x;
+    const __bf16 lo = (__bf16)(x - (float)hi);
+    split[dcol] = __builtin_bit_cast(bf16_t, hi);
+    split[D + dcol] = __builtin_bit_cast(bf16_t, lo);
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
                                                         float* __restrict__ pyr, PyrGeom g,
@@ -47,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
   const int64_t blk0 = (int64_t)c * chunk;
   const int nblk = (int)min<int64_t>(chunk, g.nb - blk0);
   const T* kb = k + bh * g.Tk * D;
-  float* slab = pyr + bh * g.n_tot * D;
+  float* slab = pyr + bh * g.planes * g.n_tot * D;
 
   const int col = (tid % TPR) * VEC;
   const int r0 = tid / TPR;
@@ -90,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
         const int64_t m = blk0 + jb + u;
         const float mean = s / (float)pyr_node_tokens(g, 0, m);
         nodes[0][jb + u][dcol] = mean;
-        slab[(g.loff[0] + m) * D + dcol] = mean;
+        put_node<D>(g, slab, g.loff[0] + m, dcol, mean);
       }
     }
     __syncthreads();
@@ -117,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
       }
       const float mean = num / den;
       nodes[cur ^ 1][m][dcol] = mean;
-      slab[(g.loff[lvl] + first_here + m) * D + dcol] = mean;
+      put_node<D>(g, slab, g.loff[lvl] + first_here + m, dcol, mean);
     }
     __syncthreads();
     cur ^= 1;
@@ -129,13 +148,13 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
 template <int D>
 __global__ __launch_bounds__(kThreads) void build_top(float* __restrict__ pyr, PyrGeom g,
                                                       int first_level) {
-  float* slab = pyr + (int64_t)blockIdx.x * g.n_tot * D;
+  float* slab = pyr + (int64_t)blockIdx.x * g.planes * g.n_tot * D;
   const int b = g.branching;
   for (int lvl = first_level; lvl < g.L; ++lvl) {
     const int n_here = g.lsize[lvl];
     const int n_below = g.lsize[lvl - 1];
     const float* below = slab + g.loff[lvl - 1] * D;
-    float* here = slab + g.loff[lvl] * D;
+
     for (int idx = threadIdx.x; idx < n_here * D; idx += kThreads) {
       const int m = idx / D, dcol = idx % D;
       float num = 0.f, den = 0.f;
@@ -147,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void build_top(float* __restrict__ pyr, P
           den += w;
         }
       }
-      here[(int64_t)m * D + dcol] = num / den;
+      put_node<D>(g, slab, g.loff[lvl] + m, dcol, num / den);
     }
     __threadfence_block();
     __syncthreads();

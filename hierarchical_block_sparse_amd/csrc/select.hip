@@ -39,13 +39,14 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 32;   // candidates per LDS chunk (MFMA path): two 16-wide N tiles
 constexpr int kZbuf = 8192;  // fp32 scratch for the generic path
+constexpr int kSelStages = 3;  // candidate chunks in LDS (MFMA path): one computing, two loading
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Dynamic LDS layout shared by host (sizing) and device.
 struct SelLayout {
   int cmax;  // candidate capacity: b*K + b - 1, rounded up to the chunk size
-  int off_kept, off_kscore, off_cand, off_score, off_rank, off_part, off_hl, off_zbuf;
+  int off_kept, off_kscore, off_cand, off_score, off_rank, off_part, off_misc, off_hl, off_zbuf;
   int total;  // bytes
   __host__ __device__ SelLayout(int K, int b, int D, bool mfma) {
     cmax = (b * K + b - 1 + kChunk - 1) / kChunk * kChunk;
@@ -57,16 +58,33 @@ struct SelLayout {
     off_score = o;  o += 4 * cmax;  // 16-byte aligned: read as float4
     off_rank = o;   o += 4 * cmax;
     if (mfma) {
-      off_part = o;  o += 8 * kWaves * cmax;             // float2 [wave][candidate]
-      off_hl = o;    o += 2 * 2 * kChunk * (D + 8) * 2;  // bf16 [stage][hi, lo][cand][D + 8]
+      off_part = o;  o += 8 * kWaves * cmax;                // float2 [wave][candidate]
+      off_misc = o;  o += 4 * (PYR_MAX_LEVELS + 4);         // int ancestors, kept count
+      o = (o + 15) & ~15;
+      off_hl = o;    o += kSelStages * kChunk * 4 * D;      // bf16 [stage][cand][hi, lo][D]
       off_zbuf = o;
     } else {
-      off_part = off_hl = o;
+      off_part = off_hl = off_misc = o;
       off_zbuf = o;  o += 4 * kZbuf;
     }
     total = o;
   }
 };
+
+// Unit of this workgroup.  The dispatcher deals workgroups to the eight XCDs
+// in turn (workgroup w runs on XCD w % 8), so XCD x takes the contiguous run
+// of units [x * U8, (x + 1) * U8): its L2 then holds the pooled keys of only
+// the (batch, KV head) slabs of its run.  Within a run the units go from the
+// last (heaviest) query block down.  Returns false for the idle workgroups
+// past the end of a short run.
+__device__ __forceinline__ bool sel_unit(const PyrGeom& g, int64_t& unit) {
+  const int64_t U = (int64_t)g.B * g.Hk * g.nqb;
+  const int64_t U8 = (U + 7) / 8;
+  const int64_t x = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int64_t end = min<int64_t>((x + 1) * U8, U);
+  unit = end - 1 - k;
+  return unit >= x * U8;
+}
 
 // Ancestor of the diagonal block at every level: anc[l] = diag / b^l.
 __device__ void ancestors(const PyrGeom& g, int diag, int* s_anc) {
@@ -114,9 +132,10 @@ __device__ __forceinline__ void keep_chunk(int j, uint32_t kj, int C, uint32_t T
 // trace.  Candidates are ascending by node index, so "lower index wins a tie"
 // is "lower position wins": the kept set is every candidate with a score above
 // the K-th largest, T, plus the first (by position) of those equal to T until
-// there are K.  Wave 0 finds T bit by bit (the largest key with at least K
-// keys >= it) with ballots over the candidates, four per lane in registers
-// (more are re-read from LDS), then compacts the kept set in index order.
+// there are K.  Wave 0 finds T two bits at a time (the largest key with at
+// least K keys >= it) with ballots over the candidates, four per lane in
+// registers (more are re-read from LDS), then compacts the kept set in index
+// order.
 __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* cand,
                                 const float* score, int* rank, int* kept, float* kscore,
                                 int* nkept, int32_t* tr_ids, float* tr_scores) {
@@ -135,14 +154,25 @@ __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* c
       const int j = ch * 64 + l;
       keys[j] = j < C ? score_key(score[j]) : 0u;
     }
+    // two bits per step: the largest of T | (d << bit), d = 3, 2, 1, that
+    // still has at least K keys at or above it
     uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t t = T | (1u << bit);
-      int cnt = 0;
+    for (int bit = 30; bit >= 0; bit -= 2) {
+      const uint32_t t1 = T | (1u << bit), t2 = T | (2u << bit), t3 = T | (3u << bit);
+      int c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) cnt += __popcll(__ballot(kr[ch] >= t));
-      for (int ch = 4; ch < nch; ++ch) cnt += __popcll(__ballot(keys[ch * 64 + l] >= t));
-      if (cnt >= K) T = t;
+      for (int ch = 0; ch < 4; ++ch) {
+        c1 += __popcll(__ballot(kr[ch] >= t1));
+        c2 += __popcll(__ballot(kr[ch] >= t2));
+        c3 += __popcll(__ballot(kr[ch] >= t3));
+      }
+      for (int ch = 4; ch < nch; ++ch) {
+        const uint32_t kj = keys[ch * 64 + l];
+        c1 += __popcll(__ballot(kj >= t1));
+        c2 += __popcll(__ballot(kj >= t2));
+        c3 += __popcll(__ballot(kj >= t3));
+      }
+      T = c3 >= K ? t3 : (c2 >= K ? t2 : (c1 >= K ? t1 : T));
     }
     int above = 0;  // candidates strictly above T (fewer than K)
 #pragma unroll
@@ -224,78 +254,74 @@ __device__ __forceinline__ void write_route(const PyrGeom& g, int64_t unit, cons
 // bf16 prefill path: MFMA scoring.  MT = 16-row M tiles per wave.
 // ---------------------------------------------------------------------------
 
-// Pooled keys of chunk c (fp32 rows of the level) -> registers.  Slot s of a
-// thread is float4 number tid + s*kThreads of the chunk's kChunk x D block.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Split rows of chunk c's candidates (plane 1 of the pyramid: per node a bf16
+// hi row and a bf16 lo row, 4D bytes) into one LDS stage with direct 16-byte
+// loads, no register staging.  Load t of a thread fills stage chunk
+// p = t * kThreads + tid (the 64 lanes of a wave fill 1 KiB in lane order):
+// candidate p / CPC, row part (p % CPC) / CPR (hi, lo), stored chunk q =
+// p % CPR, which holds logical chunk q ^ (candidate % CPR) of that row, so the
+// 16 candidates of an MFMA B fragment lie in different banks.  Positions past
+// C load candidate 0 (finite values that are never scored).
 template <int D>
-__device__ __forceinline__ void load_chunk(const float* lvl, const int* cand, int C, int c,
-                                           float4* stg) {
-  constexpr int SLOTS = kChunk * (D / 4) / kThreads;
+__device__ __forceinline__ void issue_chunk(const unsigned char* split, const int* cand, int C,
+                                            int c, unsigned char* stage, int w, int l) {
+  constexpr int CPR = D / 8;       // 16-byte chunks per bf16 row
+  constexpr int CPC = 2 * CPR;     // per candidate (hi, lo)
+  constexpr int PER = kChunk * CPC / kThreads;
+  static_assert(kChunk * CPC % kThreads == 0, "chunk must split evenly");
 #pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    const int idx = threadIdx.x + s * kThreads;
-    const int cc = idx / (D / 4), d4 = idx % (D / 4);
+  for (int t = 0; t < PER; ++t) {
+    const int p = t * kThreads + w * 64 + l;
+    const int cc = p / CPC, part = (p % CPC) / CPR, q = p % CPR;
     const int j = c * kChunk + cc;
-    stg[s] = j < C ? *reinterpret_cast<const float4*>(lvl + (int64_t)cand[j] * D + d4 * 4)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int node = cand[j < C ? j : 0];
+    const unsigned char* src =
+        split + (int64_t)node * 4 * D + part * 2 * D + ((q ^ (cc % CPR)) << 4);
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (lds_void*)(stage + (t * kThreads + w * 64) * 16), 16, 0, 0);
   }
 }
 
-// Registers -> hi/lo bf16 rows of one LDS stage.
-template <int D>
-__device__ __forceinline__ void store_chunk(const float4* stg, bf16_t* hi, bf16_t* lo) {
-  constexpr int SLOTS = kChunk * (D / 4) / kThreads;
-#pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    const int idx = threadIdx.x + s * kThreads;
-    const int cc = idx / (D / 4), d4 = idx % (D / 4);
-    const float4 x = stg[s];
-    bf16x4 h, r;
-    h[0] = (__bf16)x.x;
-    h[1] = (__bf16)x.y;
-    h[2] = (__bf16)x.z;
-    h[3] = (__bf16)x.w;
-    r[0] = (__bf16)(x.x - (float)h[0]);
-    r[1] = (__bf16)(x.y - (float)h[1]);
-    r[2] = (__bf16)(x.z - (float)h[2]);
-    r[3] = (__bf16)(x.w - (float)h[3]);
-    *reinterpret_cast<bf16x4*>(hi + cc * (D + 8) + d4 * 4) = h;
-    *reinterpret_cast<bf16x4*>(lo + cc * (D + 8) + d4 * 4) = r;
-  }
+// Combine a value with that of the lane's partner in the other 16-lane row
+// (xor 16) or the other 32-lane half (xor 32).  A swap hands each lane the
+// pair (even, odd) of the two lanes, so a symmetric combine needs no select.
+__device__ __forceinline__ float max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-// Values of a lane's partner in the other 16-lane row (xor 16) or the other
-// 32-lane half (xor 32): the swap hands each lane the pair (even, odd) of the
-// two lanes, so a symmetric merge of the pair needs no select.
-__device__ __forceinline__ void lse_swap_merge16(float& m, float& s) {
-  const auto rm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  const auto rs = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-  m = __uint_as_float(rm[0]);
-  s = __uint_as_float(rs[0]);
-  lse2_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
+__device__ __forceinline__ float max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ void lse_swap_merge32(float& m, float& s) {
-  const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-  m = __uint_as_float(rm[0]);
-  s = __uint_as_float(rs[0]);
-  lse2_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
+__device__ __forceinline__ float sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // LogSumExp (log2 domain: max m and sum s of 2^(x - m)) of one wave's rows for
 // the 16 candidates of an N tile; lane l ends with the value of candidate
-// l % 16.  Row j of M tile mt in the C layout is row 4*(l/16) + j; FULL skips
-// the per-row validity bits.
+// l % 16.  Row j of M tile mt in the C layout is row 4*(l/16) + j, so a
+// candidate's rows are spread over the four 16-lane rows: the maximum is
+// taken across them first, which makes the partial sums share one reference
+// and combine by plain addition.  FULL skips the per-row validity bits.
 template <int MT, bool FULL>
 __device__ __forceinline__ void tile_lse(const f32x4 (&acc)[MT], uint32_t rowvalid, float sl2,
                                          float& m, float& s) {
-  m = -INFINITY;
+  float mr = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (FULL || (rowvalid >> (mt * 4 + j) & 1u)) m = fmaxf(m, acc[mt][j]);
+      if (FULL || (rowvalid >> (mt * 4 + j) & 1u)) mr = fmaxf(mr, acc[mt][j]);
+  mr = max32(max16(mr));
+  m = mr * sl2;
   s = 0.f;
-  m *= sl2;
   if (m != -INFINITY) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -304,8 +330,7 @@ __device__ __forceinline__ void tile_lse(const f32x4 (&acc)[MT], uint32_t rowval
         if (FULL || (rowvalid >> (mt * 4 + j) & 1u))
           s += __builtin_amdgcn_exp2f(fmaf(acc[mt][j], sl2, -m));
   }
-  lse_swap_merge16(m, s);
-  lse_swap_merge32(m, s);
+  s = sum32(sum16(s));
 }
 
 template <int D, int MT>
@@ -315,9 +340,13 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
                                                         int32_t* __restrict__ trace_ids,
                                                         float* __restrict__ trace_scores,
                                                         PyrGeom g) {
-  static_assert(kChunk * (D / 4) % kThreads == 0, "chunk must split evenly");
-  constexpr int SLOTS = kChunk * (D / 4) / kThreads;
-  constexpr int STAGE = 2 * kChunk * (D + 8);  // bf16 elements per stage (hi then lo)
+  constexpr int CPR = D / 8;                               // 16-byte chunks per bf16 row
+  constexpr int STAGE = kChunk * 4 * D;                    // bytes per LDS stage
+  constexpr int PER = kChunk * 2 * CPR / kThreads;         // chunk loads per thread
+  constexpr int WAIT_ONE = 0x0F70 | (PER & 15) | ((PER >> 4) << 14);  // vmcnt(PER)
+  // All LDS is the one dynamic array: with a second __shared__ variable the
+  // compiler would give each its own alias scope and wait for every chunk load
+  // in flight before any LDS read, undoing the prefetch.
   extern __shared__ __align__(16) unsigned char smem[];
   const SelLayout lay(g.K, g.branching, D, true);
   int* kept = reinterpret_cast<int*>(smem + lay.off_kept);
@@ -326,12 +355,14 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
   float* score = reinterpret_cast<float*>(smem + lay.off_score);
   int* rank = reinterpret_cast<int*>(smem + lay.off_rank);
   float2* part = reinterpret_cast<float2*>(smem + lay.off_part);
-  bf16_t* hl = reinterpret_cast<bf16_t*>(smem + lay.off_hl);
-  __shared__ int s_nkept;
-  __shared__ int s_anc[PYR_MAX_LEVELS];
+  int* s_anc = reinterpret_cast<int*>(smem + lay.off_misc);
+  int& s_nkept = s_anc[PYR_MAX_LEVELS];
+  unsigned char* stages = smem + lay.off_hl;
 
-  const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
-  const int64_t unit = blockIdx.x;
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  int64_t unit;
+  if (!sel_unit(g, unit)) return;
   const int i = (int)(unit % g.nqb);
   const int64_t bhk = unit / g.nqb;  // b * Hk + hk
   const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
@@ -363,7 +394,9 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
   }
 
   const bool full = (int64_t)(i + 1) * PYR_BLOCK <= g.Tq;  // every row of the unit is real
-  const float* slab = pyr + bhk * g.n_tot * D;
+  // plane 1 of the slab: the split rows
+  const unsigned char* split =
+      reinterpret_cast<const unsigned char*>(pyr + (bhk * g.planes + 1) * g.n_tot * D);
   int32_t* tr_ids = trace_ids ? trace_ids + unit * g.L * g.K : nullptr;
   float* tr_sc = trace_scores ? trace_scores + unit * g.L * (g.K + 1) : nullptr;
   __syncthreads();
@@ -374,48 +407,68 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
       keep_all(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
       continue;
     }
-    const float* lvl = slab + g.loff[level] * D;
+    const unsigned char* lvl = split + g.loff[level] * 4 * D;
     const int nchunks = (C + kChunk - 1) / kChunk;
-    float4 stg[SLOTS];
-    load_chunk<D>(lvl, cand, C, 0, stg);
-    store_chunk<D>(stg, hl, hl + kChunk * (D + 8));
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      if (c + 1 < nchunks) load_chunk<D>(lvl, cand, C, c + 1, stg);  // in flight during the MFMAs
-      const bf16_t* hi = hl + (c & 1) * STAGE;
-      const bf16_t* lo = hi + kChunk * (D + 8);
+    // chunks c and c+1 load while chunk c-1 is scored; stage of chunk c is c % 3
+    issue_chunk<D>(lvl, cand, C, 0, stages, w, l);
+    if (nchunks > 1) issue_chunk<D>(lvl, cand, C, 1, stages + STAGE, w, l);
+    // Chunks go in groups of four whose per-tile partials stay in registers
+    // until the group ends: an LDS write while chunk loads are in flight
+    // would make the compiler wait for all of them.
+    for (int c0 = 0; c0 < nchunks; c0 += 4) {
+      float2 pbuf[8];
 #pragma unroll
-      for (int nt = 0; nt < kChunk / 16; ++nt) {
-        if (c * kChunk + nt * 16 >= C) break;  // uniform
-        f32x4 acc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const bf16_t* bh_row = hi + (nt * 16 + (l % 16)) * (D + 8) + 8 * (l / 16);
-        const bf16_t* bl_row = lo + (nt * 16 + (l % 16)) * (D + 8) + 8 * (l / 16);
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const bf16x8 bhv = as_bf16x8(*reinterpret_cast<const uint4*>(bh_row + ks * 32));
-          const bf16x8 blv = as_bf16x8(*reinterpret_cast<const uint4*>(bl_row + ks * 32));
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), bhv, acc[mt], 0, 0, 0);
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), blv, acc[mt], 0, 0, 0);
-          }
-        }
-        // this wave's LogSumExp over its rows, per candidate (lane column l % 16)
-        float m, s;
-        if (full)
-          tile_lse<MT, true>(acc, rowvalid, sl2, m, s);
+      for (int cg = 0; cg < 4; ++cg) {
+        const int c = c0 + cg;
+        if (c >= nchunks) break;  // uniform
+        // this wave's loads of chunk c have landed once at most those of
+        // chunk c+1 are outstanding; after the barrier every wave's have, and
+        // the stage of chunk c-1 is free
+        if (c + 1 < nchunks)
+          __builtin_amdgcn_s_waitcnt(WAIT_ONE);
         else
-          tile_lse<MT, false>(acc, rowvalid, sl2, m, s);
-        if (l < 16) part[w * cmax + c * kChunk + nt * 16 + l] = make_float2(m, s);
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+        lds_barrier();
+        if (c + 2 < nchunks)
+          issue_chunk<D>(lvl, cand, C, c + 2, stages + ((c + 2) % kSelStages) * STAGE, w, l);
+        const unsigned char* st = stages + (c % kSelStages) * STAGE;
+#pragma unroll
+        for (int nt = 0; nt < kChunk / 16; ++nt) {
+          if (c * kChunk + nt * 16 >= C) break;  // uniform
+          f32x4 acc[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // B fragment: candidate r = nt*16 + l%16, logical chunk 4*ks + l/16
+          // of its hi and lo rows, stored at that chunk ^ (r % CPR)
+          const int r = nt * 16 + (l % 16);
+          const unsigned char* row = st + r * 4 * D;
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks) {
+            const int off = ((4 * ks + l / 16) ^ (r % CPR)) << 4;
+            const bf16x8 bhv = as_bf16x8(*reinterpret_cast<const uint4*>(row + off));
+            const bf16x8 blv = as_bf16x8(*reinterpret_cast<const uint4*>(row + 2 * D + off));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), bhv, acc[mt], 0, 0, 0);
+              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), blv, acc[mt], 0, 0, 0);
+            }
+          }
+          // this wave's LogSumExp over its rows, per candidate (lane column l % 16)
+          float m, s;
+          if (full)
+            tile_lse<MT, true>(acc, rowvalid, sl2, m, s);
+          else
+            tile_lse<MT, false>(acc, rowvalid, sl2, m, s);
+          pbuf[cg * 2 + nt] = make_float2(m, s);
+        }
       }
-      if (c + 1 < nchunks) {
-        bf16_t* nhi = hl + ((c + 1) & 1) * STAGE;
-        store_chunk<D>(stg, nhi, nhi + kChunk * (D + 8));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int cn = c0 * kChunk + e * 16;
+        if (cn < C && l < 16) part[w * cmax + cn + l] = pbuf[e];
       }
-      __syncthreads();
     }
+    __syncthreads();
     for (int j = tid; j < C; j += kThreads) {
       float m = -INFINITY, s = 0.f;
 #pragma unroll
@@ -455,7 +508,8 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
   __shared__ int s_anc[PYR_MAX_LEVELS];
 
   const int tid = threadIdx.x;
-  const int64_t unit = blockIdx.x;
+  int64_t unit;
+  if (!sel_unit(g, unit)) return;
   const int i = (int)(unit % g.nqb);
   const int64_t bhk = unit / g.nqb;
   const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
@@ -472,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
   }
   const int R = (int)(g.G * ntok);
   const float sl2 = g.scale * PYR_LOG2E;
-  const float* slab = pyr + bhk * g.n_tot * D;
+  const float* slab = pyr + bhk * g.planes * g.n_tot * D;  // plane 0: fp32 means
   int32_t* tr_ids = trace_ids ? trace_ids + unit * g.L * g.K : nullptr;
   float* tr_sc = trace_scores ? trace_scores + unit * g.L * (g.K + 1) : nullptr;
   const int chv = max(1, kZbuf / R);
@@ -537,7 +591,7 @@ hipError_t launch_select_d(const PyrGeom& g, int dtype, const void* q, const flo
   const int64_t units = (int64_t)g.B * g.Hk * g.nqb;
   if (units == 0) return hipSuccess;
   const int mt = mfma_tiles(g, dtype);
-  const dim3 grid((unsigned)units), block(kThreads);
+  const dim3 grid((unsigned)((units + 7) / 8 * 8)), block(kThreads);  // whole runs per XCD
   const size_t lds = SelLayout(g.K, g.branching, D, mt != 0).total;
   if (mt) {
     const bf16_t* qq = static_cast<const bf16_t*>(q);

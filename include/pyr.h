@@ -94,6 +94,9 @@ int32_t pyr_num_levels(const pyr_problem* p);
 int64_t pyr_level_offset(const pyr_problem* p, int32_t level);
 /* Nodes per (batch, KV head) slab: sum of all level sizes. */
 int64_t pyr_pyramid_nodes(const pyr_problem* p);
+/* Planes of a pyramid slab: 1 for float32 problems, 2 for bfloat16 problems
+ * (plane 1 repeats plane 0 split into bfloat16 pairs, see pyr_build_pyramid). */
+int32_t pyr_pyramid_planes(const pyr_problem* p);
 /* Query blocks per (batch, KV head): ceil(q_len/64) in prefill, 1 in decode. */
 int64_t pyr_num_query_blocks(const pyr_problem* p);
 /* Bytes of device workspace pyr_block_sparse_attn needs (0 if none). */
@@ -104,10 +107,15 @@ size_t pyr_attn_workspace_bytes(const pyr_problem* p);
 /* Pooled key pyramid (PISA abstract: pooling builds the coarse-to-fine key
  * levels; PHBA §A.1.2: block means over valid rows, fp32 accumulation).
  *   k        [B, Hk, kv_len, d] in p->dtype                          (input)
- *   pyramid  [B, Hk, pyr_pyramid_nodes(p), d] float32                (output)
- * Node m of level l is the mean of every key token it covers (blocks
+ *   pyramid  [B, Hk, P, pyr_pyramid_nodes(p), d] float32,
+ *            P = pyr_pyramid_planes(p)                                (output)
+ * Plane 0: node m of level l is the mean of every key token it covers (blocks
  * [m b^l, (m+1) b^l) clipped to the sequence); levels are concatenated finest
- * first at pyr_level_offset(p, l). */
+ * first at pyr_level_offset(p, l).  Plane 1 (bfloat16 problems only): the
+ * 4d bytes of node row m hold the same d means as two bfloat16 rows,
+ * hi = bf16(x) then lo = bf16(x - hi) (round to nearest even), which the
+ * matrix-core scorer of pyr_select_topk reads; hi + lo is x to within 2^-17
+ * relative. */
 pyr_status pyr_build_pyramid(const pyr_problem* p, const void* k, float* pyramid,
                              hipStream_t stream);
 

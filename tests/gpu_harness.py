@@ -64,8 +64,27 @@ def oracle_levels(k64, cfg, bh=None):
     return out
 
 
+def check_split_plane(dev_pyr):
+    """Plane 1 of a two-plane (bf16 problem) pyramid must hold, bit for bit,
+    hi = bf16(x) and lo = bf16(x - hi) of plane 0's fp32 means x (round to
+    nearest even, as torch converts)."""
+    if dev_pyr.shape[2] < 2:
+        return
+    x = dev_pyr[:, :, 0]
+    split = dev_pyr[:, :, 1].contiguous().view(torch.bfloat16)      # [..., 2d]
+    d = x.shape[-1]
+    hi_ref = x.to(torch.bfloat16)
+    lo_ref = (x - hi_ref.float()).to(torch.bfloat16)
+    assert torch.equal(split[..., :d].view(torch.int16), hi_ref.view(torch.int16))
+    assert torch.equal(split[..., d:].view(torch.int16), lo_ref.view(torch.int16))
+
+
 def check_pyramid(dev_pyr, levels, k_absmax):
-    dev = dev_pyr.detach().cpu().numpy().astype(np.float64)
+    """dev_pyr: [B, Hk, planes, nodes, d] from the device; levels: the
+    oracle's per-level means.  Returns (max abs error of plane 0, tolerance)
+    after checking the split plane."""
+    check_split_plane(dev_pyr)
+    dev = dev_pyr[:, :, 0].detach().cpu().numpy().astype(np.float64)
     ref = reference.concat_levels(levels)
     err = np.abs(dev - ref).max() if ref.size else 0.0
     return err, 1e-5 * max(k_absmax, 1.0)

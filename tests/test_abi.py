@@ -54,6 +54,21 @@ def test_geometry_matches_oracle(kv_len, b):
     assert H.pyr_attn_workspace_bytes(p) == 0
 
 
+def test_pyramid_planes_and_buffer_shape():
+    """bf16 problems carry the fp32 plane plus the bf16 hi/lo plane, fp32
+    problems only the fp32 plane; the allocation helper sizes the buffer from
+    the library's own answer."""
+    pb = _p()
+    pf = _p(dtype=torch.float32)
+    assert H.pyr_pyramid_planes(pb) == 2
+    assert H.pyr_pyramid_planes(pf) == 1
+    nodes = H.pyr_pyramid_nodes(pb)
+    assert H.pyramid_shape(pb) == (pb.batch, pb.n_kv_heads, 2, nodes, pb.head_dim)
+    assert H.pyramid_shape(pf) == (pb.batch, pb.n_kv_heads, 1, nodes, pb.head_dim)
+    t = H.alloc_pyramid(pb, device="cpu")
+    assert tuple(t.shape) == H.pyramid_shape(pb) and t.dtype == torch.float32
+
+
 def test_decode_geometry():
     p = _p(batch=64, n_q_heads=32, n_kv_heads=8, q_len=1, kv_len=262144, top_k=64)
     assert H.pyr_num_query_blocks(p) == 1

@@ -61,7 +61,7 @@ def test_fullsize_sampled(name, n_slabs, n_per_slab):
         k64 = GH.f64(k[bi:bi + 1, hk:hk + 1])
         v64 = GH.f64(v[bi:bi + 1, hk:hk + 1])
         levels = [x[0, 0] for x in reference.build_pyramid(k64, cfg.block, cfg.branching)]
-        dev_pyr = dev["pyr"][bi, hk].double().cpu().numpy()
+        dev_pyr = dev["pyr"][bi, hk, 0].double().cpu().numpy()
         ref_pyr = np.concatenate(levels, axis=0)
         e_p = max(e_p, float(np.abs(dev_pyr - ref_pyr).max()))
         assert e_p <= 1e-5 * max(float(np.abs(k64).max()), 1.0)

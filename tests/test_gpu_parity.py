@@ -168,7 +168,7 @@ def test_empty_inputs_are_noops():
     p = H.Problem(0, 4, 2, 128, 128, 128, 4, 4, torch.bfloat16)
     e = torch.empty((0, 4, 128, 128), dtype=torch.bfloat16, device="cuda")
     ek = torch.empty((0, 2, 128, 128), dtype=torch.bfloat16, device="cuda")
-    H.pyr_build_pyramid(p, ek, torch.empty((0, 2, H.pyr_pyramid_nodes(p), 128), device="cuda"))
+    H.pyr_build_pyramid(p, ek, torch.empty(H.pyramid_shape(p), device="cuda"))
     p0 = H.Problem(1, 4, 2, 128, 0, 0, 4, 4, torch.bfloat16)
     assert H.pyr_pyramid_nodes(p0) == 0
     torch.cuda.synchronize()
@@ -184,8 +184,9 @@ def test_deterministic_and_in_bounds():
     pad = 4096
     outs = []
     for _ in range(2):
-        pyr_buf = torch.full((H.pyr_pyramid_nodes(p) * 2 * 128 + pad,), 7.0, device="cuda")
-        pyr = pyr_buf[:-pad].view(1, 2, -1, 128)
+        shape = H.pyramid_shape(p)
+        pyr_buf = torch.full((math.prod(shape) + pad,), 7.0, device="cuda")
+        pyr = pyr_buf[:-pad].view(shape)
         H.pyr_build_pyramid(p, k, pyr)
         nqb = H.pyr_num_query_blocks(p)
         sel_buf = torch.full((2 * nqb * 7 + pad,), -77, dtype=torch.int32, device="cuda")
