@@ -190,6 +190,15 @@ def cpu_baseline(cfg, q, k, v, n_units):
     }
 
 
+def attn_kernel_name(cfg):
+    """The attention kernel the library runs for this workload."""
+    if cfg.decode:
+        return "attn_decode_split+combine"
+    if cfg.dtype.itemsize != 2:
+        return "attn_prefill_valu"
+    return "attn_prefill_ilv" if cfg.group % 4 == 0 else "attn_prefill_mfma"
+
+
 def kernel_traffic(workload):
     """HBM bytes per attention dispatch from the committed rocprofv3 counter
     summary, if it was taken on the current attention source."""
@@ -300,7 +309,7 @@ def main():
                                          else "build+select+attn"),
         },
         "roofline": {
-            "kernel": "attn_prefill_mfma" if not cfg.decode else "attn_decode_split+combine",
+            "kernel": attn_kernel_name(cfg),
             "bound": "mfma" if not cfg.decode else "hbm",
             "achieved": round(achieved, 2) if not cfg.decode else round(a_bytes / t_attn / 1e9, 1),
             "peak": PEAK_BF16_TFLOPS if not cfg.decode else PEAK_HBM_GBS,
