@@ -40,6 +40,10 @@ Readings of the pages this oracle rests on (the pages leave these open):
       in the cache; its diagonal block is (Tk-1) // block.
   R11 Attention is token-causal: a query at position t sees key positions
       s <= t of its selected blocks only (this masks the diagonal block alone).
+  R12 The backward treats the route table as fixed (a discrete choice with no
+      gradient): q, k and v receive the gradient of the attention over the
+      selected blocks only, and the pyramid and the scores receive none.  It
+      recomputes the probabilities from the forward's log-sum-exp (PHBA §A.1.4).
 """
 
 from __future__ import annotations
@@ -306,3 +310,76 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, bloc
             o[bi, h, toks, :] = oo
             lse[bi, h, toks] = ll
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Backward of the block-sparse attention for a fixed route table (PHBA §A.1.4:
+# probabilities recomputed from the forward's log-sum-exp; reading R12)
+# ---------------------------------------------------------------------------
+
+def attend_rows_backward(rows: np.ndarray, row_pos: np.ndarray, k_bh: np.ndarray,
+                         v_bh: np.ndarray, blocks: list[int], block: int, scale: float,
+                         d_out: np.ndarray, lse: np.ndarray):
+    """Gradients of o = softmax(scale * rows k^T) v over the visible keys of
+    `blocks` (the same visibility as attend_rows), given d_out = dL/do and the
+    forward's lse.  With P the probabilities, dP = d_out v^T,
+    D = rowsum(d_out * o) = rowsum(P * dP) and dS = P * (dP - D):
+      d_rows = scale * dS k,  dk = scale * dS^T rows,  dv = P^T d_out.
+    Returns (d_rows [R, d], key_pos [S], dk [S, d], dv [S, d]) in float64; the
+    key rows dk and dv belong to the key positions key_pos.
+    """
+    Tk = k_bh.shape[0]
+    key_pos = np.concatenate([np.arange(j * block, min((j + 1) * block, Tk)) for j in blocks])
+    kk = np.asarray(k_bh[key_pos], dtype=np.float64)
+    vv = np.asarray(v_bh[key_pos], dtype=np.float64)
+    z = scale * (rows @ kk.T)                                  # [R, S]
+    visible = key_pos[None, :] <= row_pos[:, None]
+    p = np.where(visible, np.exp(z - lse[:, None]), 0.0)       # P from the log-sum-exp
+    o = p @ vv
+    dp = d_out @ vv.T
+    dsum = (d_out * o).sum(axis=1, keepdims=True)              # D
+    ds = p * (dp - dsum)
+    d_rows = scale * (ds @ kk)
+    dk = scale * (ds.T @ rows)
+    dv = p.T @ d_out
+    return d_rows, key_pos, dk, dv
+
+
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray,
+                       block: int, d_out: np.ndarray, scale: float | None = None,
+                       lse: np.ndarray | None = None):
+    """dq, dk, dv of block-sparse causal attention over a fixed route table.
+
+    q, d_out [B, Hq, Tq, d]; k, v [B, Hk, Tk, d]; sel [B, Hk, nqb, K+1].  The
+    gradients of the G query heads of a KV group add up in dk and dv.  lse is
+    the forward's [B, Hq, Tq] log-sum-exp (recomputed when not given).  Returns
+    float64 arrays shaped like q, k and v.  Prefill only (q_len == kv_len).
+    """
+    B, Hq, Tq, d = q.shape
+    _, Hk, Tk, _ = k.shape
+    if Tq != Tk:
+        raise ValueError("the backward is defined for prefill (q_len == kv_len)")
+    group = Hq // Hk
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if lse is None:
+        _, lse = attention(q, k, v, sel, block, scale)
+    nqb = num_query_blocks(Tq, Tk, block)
+    pos = query_positions(Tq, Tk)
+    dq = np.zeros((B, Hq, Tq, d))
+    dk = np.zeros((B, Hk, Tk, d))
+    dv = np.zeros((B, Hk, Tk, d))
+    for bi in range(B):
+        for hk in range(Hk):
+            for i in range(nqb):
+                toks, _ = unit_tokens(i, Tq, Tk, block)
+                blocks = [int(x) for x in sel[bi, hk, i] if x >= 0]
+                for h in range(hk * group, (hk + 1) * group):
+                    rows = np.asarray(q[bi, h, toks, :], dtype=np.float64)
+                    g = np.asarray(d_out[bi, h, toks, :], dtype=np.float64)
+                    dr, kp, dkk, dvv = attend_rows_backward(
+                        rows, pos[toks], k[bi, hk], v[bi, hk], blocks, block, scale, g,
+                        np.asarray(lse[bi, h, toks], dtype=np.float64))
+                    dq[bi, h, toks, :] = dr
+                    np.add.at(dk[bi, hk], kp, dkk)
+                    np.add.at(dv[bi, hk], kp, dvv)
+    return dq, dk, dv
