@@ -65,6 +65,9 @@ def lib():
             ("pyr_build_pyramid", st, [P, vp, vp, vp]),
             ("pyr_select_topk", st, [P, vp, vp, vp, vp, vp, vp]),
             ("pyr_block_sparse_attn", st, [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+            ("pyr_attn_bwd_workspace_bytes", ctypes.c_size_t, [P]),
+            ("pyr_block_sparse_attn_bwd", st,
+             [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
             ("pyr_status_string", ctypes.c_char_p, [st]),
             ("pyr_last_error", ctypes.c_char_p, []),
             ("pyr_abi_version", ctypes.c_int32, []),
@@ -208,6 +211,34 @@ def pyr_block_sparse_attn(p: Problem, q, k, v, sel, o, lse=None, workspace=None,
                                        _stream(stream)))
 
 
+def pyr_attn_bwd_workspace_bytes(p: Problem) -> int:
+    return lib().pyr_attn_bwd_workspace_bytes(ctypes.byref(p.c()))
+
+
+def _workspace_bytes(workspace) -> int:
+    if workspace is None:
+        return 0
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous cuda tensor")
+    return workspace.numel() * workspace.element_size()
+
+
+def pyr_block_sparse_attn_bwd(p: Problem, q, k, v, sel, o, lse, dout, dq, dk, dv, workspace,
+                              stream=None):
+    nqb = pyr_num_query_blocks(p)
+    qs = (p.batch, p.n_q_heads, p.q_len, p.head_dim)
+    ks = (p.batch, p.n_kv_heads, p.kv_len, p.head_dim)
+    for t, name, shape in ((q, "q", qs), (k, "k", ks), (v, "v", ks), (o, "o", qs),
+                           (dout, "dout", qs), (dq, "dq", qs), (dk, "dk", ks), (dv, "dv", ks)):
+        _expect(t, name, shape, p.dtype)
+    _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
+    _expect(lse, "lse", (p.batch, p.n_q_heads, p.q_len), torch.float32)
+    _check(lib().pyr_block_sparse_attn_bwd(
+        ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(o), _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _workspace_bytes(workspace),
+        _stream(stream)))
+
+
 # ---- allocating conveniences (torch allocates; the library computes) ----
 
 def alloc_pyramid(p: Problem, device="cuda"):
@@ -230,6 +261,20 @@ def alloc_trace(p: Problem, device="cuda"):
 def alloc_workspace(p: Problem, device="cuda"):
     n = pyr_attn_workspace_bytes(p)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device) if n else None
+
+
+def alloc_bwd_workspace(p: Problem, device="cuda"):
+    n = pyr_attn_bwd_workspace_bytes(p)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def backward(q, k, v, sel, o, lse, dout, branching: int, top_k: int, scale: float = 0.0):
+    """dq, dk, dv of the attention for the forward's route rows (fixed routes)."""
+    p = problem_for(q, k, branching, top_k, scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    pyr_block_sparse_attn_bwd(p, q, k, v, sel, o, lse, dout, dq, dk, dv,
+                              alloc_bwd_workspace(p, q.device))
+    return dq, dk, dv
 
 
 def problem_for(q, k, branching: int, top_k: int, scale: float = 0.0) -> Problem:

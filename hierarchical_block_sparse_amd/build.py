@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpyr.so")
-SOURCES = ["pyr_api.cpp", "pyramid.hip", "select.hip", "attn.hip"]
+SOURCES = ["pyr_api.cpp", "pyramid.hip", "select.hip", "attn.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-x", "hip",

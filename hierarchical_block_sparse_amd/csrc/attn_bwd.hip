@@ -1,0 +1,574 @@
+// Backward of the block-sparse causal attention for a fixed route table, on
+// gfx950.
+//
+// PHBA (Prefix-State Hybrid Block Attention) §A.1.4: the sparse backward
+// enumerates, block-major, the query rows that access each key block and
+// recomputes the sparse scores and probabilities on chip from the forward's
+// log-sum-exp, with no stored probability tensor; §A.1: during training the
+// routing decisions are reformatted as block-major integer metadata.  The route
+// itself is a discrete choice and gets no gradient.  With P = exp(scale q k^T -
+// lse) over the visible keys of the selected blocks:
+//   dP = dO v^T,  D = rowsum(dO * O),  dS = P (dP - D),
+//   dQ = scale dS k,  dK = scale dS^T q,  dV = P^T dO   (dK, dV summed over
+//   the G query heads of the KV group).
+//
+// Kernels (bf16 tensors, fp32 accumulation):
+//  * bwd_dsum: a record per (query head, query block) of the rows' log-sum-exp
+//    (log2 domain) and D.
+//  * bwd_route_clear + bwd_route_bits: the block-major route metadata, a bitmap
+//    per (batch, KV head) slab with one row per key block and bit i of row j
+//    set when query block i routes to key block j.  OR-ing bits does not depend
+//    on the order of the writes, so the metadata, the order in which a key
+//    block visits its query blocks, and the gradients are deterministic.
+//  * bwd_dq: one workgroup per (unit, group of heads), 32 query rows per wave,
+//    Q and dO of its rows held as MFMA B fragments in VGPRs.  For every
+//    selected block the K and V tiles stream global -> LDS (direct loads, two
+//    stages); S^T = K Q^T and dP^T = V dO^T read row fragments of the tiles,
+//    and dQ^T += K^T dS^T reads K^T fragments with transposed LDS reads.
+//  * bwd_dkdv: one workgroup per (slab, key block), four waves: wave w takes
+//    the 32 keys (w & 1) of the block against the 32 query rows (w >> 1) of
+//    each visiting (query block, head).  The wave keeps its keys' K and V as B
+//    fragments in VGPRs and dK^T, dV^T accumulators, streams the Q and dO
+//    tiles (and the rows' record) of each visitor, and computes S = Q K^T,
+//    dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS with transposed reads
+//    of the tiles.  The two row halves of a key tile are summed through LDS at
+//    the end.
+#include <math.h>
+
+#include "pyr_device.h"
+#include "pyr_internal.h"
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxSelB = PYR_BWD_MAX_SLOTS;  // route-row capacity staged in LDS
+
+// A 64-row tile of bf16 rows of length D in LDS: row-major, the 16-byte chunks
+// of row r XOR-swizzled by swz(r) so that row-per-lane 16-byte reads are free
+// of bank conflicts.
+template <int D>
+struct BTile {
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
+  static constexpr int ROW = 2 * D;      // bytes per row
+  static constexpr int TILE = 64 * ROW;  // bytes per tile
+  static constexpr int RP = 256 / ROW;   // rows per 256-byte bank sweep
+  __device__ static int swz(int r) { return (r / RP) % CPR; }
+  // byte offset of logical 16-byte chunk c of row r
+  __device__ static int off(int r, int c) { return r * ROW + ((c ^ swz(r)) << 4); }
+};
+
+// Load 64 rows (row0 .. row0 + 63, clamped to `last`) of a [rows, D] bf16
+// matrix into a tile with direct 16-byte global->LDS loads.  Load t of a thread
+// fills stored chunk p = t * NT + tid (a wave's 64 lanes fill 1 KiB in lane
+// order): row p / CPR, stored chunk p % CPR, which holds logical chunk
+// (p % CPR) ^ swz(row).
+template <int D, int NT>
+__device__ __forceinline__ void load_tile(const bf16_t* base, int64_t row0, int64_t last,
+                                          unsigned char* tile, int w, int l) {
+  using TG = BTile<D>;
+  static_assert(64 * TG::CPR % NT == 0, "tile must split evenly");
+#pragma unroll
+  for (int t = 0; t < 64 * TG::CPR / NT; ++t) {
+    const int p = t * NT + w * 64 + l;
+    const int row = p / TG::CPR, sc = p % TG::CPR;
+    const int64_t r = min<int64_t>(row0 + row, last);
+    const bf16_t* src = base + r * D + (sc ^ TG::swz(row)) * 8;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(tile + (t * NT + w * 64) * 16),
+                                     16, 0, 0);
+  }
+}
+
+// A fragment of a 32x32x16 MFMA whose M index is a tile row (rows rb .. rb+31,
+// lane's row rb + l%32) and whose K index is d (16 at ks*16): 8 consecutive d.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const unsigned char* tile, int rb, int ks, int l) {
+  using TG = BTile<D>;
+  return as_bf16x8(*reinterpret_cast<const uint4*>(tile + TG::off(rb + l % 32, 2 * ks + l / 32)));
+}
+
+// A fragment whose M index is d (32 at dt*32) and whose K index runs over 16
+// tile rows starting at rb: two transposed reads.  MFMA k index 8*half + jj
+// maps to tile row rb + 4*half + jj (jj < 4) or rb + 8 + 4*half + (jj - 4)
+// (jj >= 4), the order in which a 32x32 C fragment holds its rows (per
+// 16-lane group, lane i of a transposed read receives element i % 4 of the
+// 8-byte chunk that lane 4j + i/4 addresses).
+template <int D>
+__device__ __forceinline__ bf16x8 trans_frag(const unsigned char* tile, int rb, int dt, int l) {
+  using TG = BTile<D>;
+  const int half = l / 32, g16 = l / 16, s16 = l % 16;
+  const int r1 = rb + 4 * half + s16 / 4;
+  const int c = dt * 32 + (g16 % 2) * 16 + 4 * (s16 % 4);  // first of the lane's 4 d
+  const unsigned char* p1 = tile + TG::off(r1, c >> 3) + (c & 7) * 2;
+  const unsigned char* p2 = tile + TG::off(r1 + 8, c >> 3) + (c & 7) * 2;
+  const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+  const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p2);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Pack the lane's 16 fp32 values of a 32x32 C fragment (column l%32, rows
+// (e/4)*8 + half*4 + e%4) into the two bf16 B fragments (K index = those rows,
+// in trans_frag's order) of the next product.
+__device__ __forceinline__ void pack_b(const f32x16& x, bf16x8 (&b)[2]) {
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[k2][e] = (__bf16)x[k2 * 8 + e];
+}
+
+// ---------------------------------------------------------------------------
+// Per-row record of the backward: for every (batch, query head, query block) a
+// 512-byte record of 64 log2-domain log-sum-exps (lse * log2 e) followed by 64
+// values of D = rowsum(dO * O).  Rows past q_len, and rows whose log-sum-exp
+// is not finite (they saw no key), get +inf and 0: their probabilities
+// evaluate to exactly 0, so they contribute nothing and get zero gradients.
+// ---------------------------------------------------------------------------
+constexpr int kRec = 128;  // floats per record
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dsum(const bf16_t* __restrict__ o,
+                                                const bf16_t* __restrict__ dout,
+                                                const float* __restrict__ lse,
+                                                float* __restrict__ rec, PyrGeom g) {
+  constexpr int TPR = D / 8;  // threads per row, 8 elements each
+  const int64_t rows = (int64_t)g.B * g.Hq * g.nqb * PYR_BLOCK;  // padded rows
+  const int64_t r = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c = (threadIdx.x % TPR) * 8;
+  const int64_t padded = (int64_t)g.nqb * PYR_BLOCK;
+  const int64_t bh = r / padded, t = r % padded;
+  const bool live = r < rows && t < g.Tq;
+  float s = 0.f;
+  if (live) {
+    const int64_t row = bh * g.Tq + t;
+    const uint4 a = ld16(o + row * D + c), b = ld16(dout + row * D + c);
+    float x[8], y[8];
+    unpack16<bf16_t>(a, x);
+    unpack16<bf16_t>(b, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(x[e], y[e], s);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (r < rows && threadIdx.x % TPR == 0) {
+    float l2 = __builtin_inff(), dd = 0.f;
+    if (live) {
+      const float lv = lse[bh * g.Tq + t];
+      if (__builtin_isfinite(lv)) {
+        l2 = lv * PYR_LOG2E;
+        dd = s;
+      }
+    }
+    float* out = rec + (r / PYR_BLOCK) * kRec + r % PYR_BLOCK;
+    out[0] = l2;
+    out[PYR_BLOCK] = dd;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-major route metadata
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_route_clear(uint32_t* __restrict__ bits, int64_t n) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256)
+    bits[x] = 0u;
+}
+
+__global__ __launch_bounds__(256) void bwd_route_bits(const int32_t* __restrict__ sel,
+                                                      uint32_t* __restrict__ bits, PyrGeom g,
+                                                      int words) {
+  const int64_t n = (int64_t)g.B * g.Hk * g.nqb * (g.K + 1);
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= n) return;
+  const int64_t unit = x / (g.K + 1);
+  const int j = sel[x];
+  if (j < 0 || j >= g.nb) return;
+  const int64_t slab = unit / g.nqb;
+  const int i = (int)(unit % g.nqb);
+  atomicOr(bits + (slab * g.nb + j) * words + i / 32, 1u << (i % 32));
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (unit, group of NH heads); two waves per head.
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int32_t* __restrict__ sel, const bf16_t* __restrict__ dout,
+    const float* __restrict__ rec, bf16_t* __restrict__ dq, PyrGeom g, int wg_per_unit) {
+  using TG = BTile<D>;
+  constexpr int NT = NW * 64;
+  constexpr int NH = NW / 2;  // heads per workgroup
+  __shared__ __align__(16) unsigned char tiles[2][2][TG::TILE];  // [stage][K, V]
+  __shared__ int s_sel[kMaxSelB];
+  __shared__ int s_n;
+
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int half = l / 32, lr = l % 32;
+  const int64_t ublk = blockIdx.x / wg_per_unit;
+  const int sub = (int)(blockIdx.x % wg_per_unit);
+  const int i = (int)(ublk % g.nqb);
+  const int64_t slab = ublk / g.nqb;
+  const int bi = (int)(slab / g.Hk), hk = (int)(slab % g.Hk);
+  const int h = hk * g.G + sub * NH + w / 2;
+  const int64_t row0 = (int64_t)i * PYR_BLOCK + (w % 2) * 32;  // first query token of the wave
+  const float sl2 = g.scale * PYR_LOG2E;
+  const bf16_t* kh = k + slab * g.Tk * D;
+  const bf16_t* vh = v + slab * g.Tk * D;
+
+  // compact route row (entries outside [0, nb) are skipped)
+  if (tid == 0) {
+    int n = 0;
+    for (int jj = 0; jj <= g.K; ++jj) {
+      const int j = sel[ublk * (g.K + 1) + jj];
+      if (j >= 0 && j < g.nb) s_sel[n++] = j;
+    }
+    s_n = n;
+  }
+  __syncthreads();
+  const int nsel = s_n;
+  if (nsel > 0)
+    load_tile<D, NT>(kh, (int64_t)s_sel[0] * PYR_BLOCK, g.Tk - 1, tiles[0][0], w, l);
+  if (nsel > 0)
+    load_tile<D, NT>(vh, (int64_t)s_sel[0] * PYR_BLOCK, g.Tk - 1, tiles[0][1], w, l);
+
+  // Q^T and dO^T B fragments: lane holds query row row0 + lr, d = ks*16 + 8*half .. +7;
+  // rows past the end load the last row (never stored).
+  const int64_t tok = min<int64_t>(row0 + lr, g.Tq - 1);
+  const int64_t qrow = ((int64_t)bi * g.Hq + h) * g.Tq + tok;
+  uint4 qb[D / 16], ob[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qb[ks] = ld16(q + qrow * D + ks * 16 + 8 * half);
+    ob[ks] = ld16(dout + qrow * D + ks * 16 + 8 * half);
+  }
+  const float* rrow = rec + (((int64_t)bi * g.Hq + h) * g.nqb + i) * kRec + (w % 2) * 32 + lr;
+  const float lse2 = rrow[0];
+  const float dsr = rrow[PYR_BLOCK];
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+
+  for (int jj = 0; jj < nsel; ++jj) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block jj
+    __syncthreads();                     // everyone's; the other stage is free
+    if (jj + 1 < nsel) {
+      const int64_t key1 = (int64_t)s_sel[jj + 1] * PYR_BLOCK;
+      load_tile<D, NT>(kh, key1, g.Tk - 1, tiles[(jj + 1) & 1][0], w, l);
+      load_tile<D, NT>(vh, key1, g.Tk - 1, tiles[(jj + 1) & 1][1], w, l);
+    }
+    const unsigned char* Kt = tiles[jj & 1][0];
+    const unsigned char* Vt = tiles[jj & 1][1];
+    const int64_t key0 = (int64_t)s_sel[jj] * PYR_BLOCK;
+    const bool need_mask = key0 + PYR_BLOCK - 1 > row0;
+    const int rel = (int)(row0 - key0) + lr;  // row position in the block's key coordinates
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[e] = 0.f;
+        dp[e] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Kt, kt * 32, ks, l),
+                                                    as_bf16x8(qb[ks]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Vt, kt * 32, ks, l),
+                                                     as_bf16x8(ob[ks]), dp, 0, 0, 0);
+      }
+      // S^T element e of the lane: key kt*32 + (e/4)*8 + half*4 + e%4, row lr
+      f32x16 ds;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kt * 32 + (e / 4) * 8 + half * 4 + (e % 4);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -lse2));
+        ds[e] = (need_mask && key > rel) ? 0.f : p * (dp[e] - dsr);
+      }
+      bf16x8 dsb[2];
+      pack_b(ds, dsb);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(Kt, kt * 32 + 16 * k2, dt, l),
+                                                            dsb[k2], acc[dt], 0, 0, 0);
+    }
+  }
+
+  // dQ = scale * acc; lane's row = lr, dims of acc[dt][e] = dt*32 + (e/4)*8 + half*4 + e%4
+  if (row0 + lr >= g.Tq) return;
+  bf16_t* out = dq + qrow * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4_t pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[dt][g4 * 4 + e] * g.scale);
+      *reinterpret_cast<bf16x4_t*>(out + dt * 32 + g4 * 8 + half * 4) = pk;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (slab, key block), four waves.
+// ---------------------------------------------------------------------------
+
+// Walks the set bits of one bitmap row in ascending order.
+struct BitWalk {
+  const uint32_t* row;
+  int words, wi;
+  uint32_t cur;
+  __device__ void start(const uint32_t* r, int n) {
+    row = r;
+    words = n;
+    wi = 0;
+    cur = n > 0 ? __builtin_amdgcn_readfirstlane(r[0]) : 0u;
+  }
+  // next query block, or -1 when none is left
+  __device__ int next() {
+    while (cur == 0u) {
+      if (++wi >= words) return -1;
+      cur = __builtin_amdgcn_readfirstlane(row[wi]);
+    }
+    const int b = __builtin_ctz(cur);
+    cur &= cur - 1u;
+    return wi * 32 + b;
+  }
+};
+
+template <int D>
+struct DkdvStage {
+  static constexpr int TILE = BTile<D>::TILE;
+  static constexpr int AUX = 1024;  // the visitor's record (512 bytes), loaded twice
+  static constexpr int BYTES = 2 * TILE + AUX;
+};
+
+// Stage the Q and dO tiles and the row record of visitor (query block i, head
+// h).  Wave 0 copies the record: lanes l and l + 32 both load its 16-byte chunk
+// l, so the second half of the aux kilobyte repeats the first (unused).
+template <int D>
+__device__ __forceinline__ void load_visitor(const bf16_t* q, const bf16_t* dout, const float* rec,
+                                             const PyrGeom& g, int bi, int h, int i,
+                                             unsigned char* st, int w, int l) {
+  using TG = BTile<D>;
+  const int64_t bh = (int64_t)bi * g.Hq + h;
+  const int64_t r0 = (int64_t)i * PYR_BLOCK;
+  load_tile<D, 256>(q + bh * g.Tq * D, r0, g.Tq - 1, st, w, l);
+  load_tile<D, 256>(dout + bh * g.Tq * D, r0, g.Tq - 1, st + TG::TILE, w, l);
+  if (w == 0) {
+    const float* src = rec + (bh * g.nqb + i) * kRec + (l % 32) * 4;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(st + 2 * TG::TILE), 16, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ rec,
+    const uint32_t* __restrict__ bits, bf16_t* __restrict__ dk,
+    bf16_t* __restrict__ dv, PyrGeom g, int words) {
+  using TG = BTile<D>;
+  using SG = DkdvStage<D>;
+  __shared__ __align__(16) unsigned char stage[2][SG::BYTES];
+
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int half = l / 32, lr = l % 32;
+  const int kt = w & 1, rh = w >> 1;  // key tile and row half of this wave
+  const int64_t slab = blockIdx.x / g.nb;
+  const int j = (int)(blockIdx.x % g.nb);
+  const int bi = (int)(slab / g.Hk), hk = (int)(slab % g.Hk);
+  const float sl2 = g.scale * PYR_LOG2E;
+  const int64_t kbase = slab * g.Tk;
+  const int kpos = j * PYR_BLOCK + kt * 32 + lr;  // the lane's key (B fragment column)
+
+  // K and V B fragments of the wave's 32 keys: lane key kpos, d = ks*16 + 8*half .. +7
+  uint4 kb[D / 16], vb[D / 16];
+  {
+    const int64_t kr = kbase + min<int64_t>(kpos, g.Tk - 1);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kb[ks] = ld16(k + kr * D + ks * 16 + 8 * half);
+      vb[ks] = ld16(v + kr * D + ks * 16 + 8 * half);
+    }
+  }
+  f32x16 dka[D / 32], dva[D / 32];  // dK^T, dV^T: column key kpos, d = dt*32 + (e/4)*8 + half*4 + e%4
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dka[dt][e] = 0.f;
+      dva[dt][e] = 0.f;
+    }
+
+  BitWalk bw;
+  bw.start(bits + (slab * g.nb + j) * words, words);
+  int icur = bw.next();
+  int hcur = 0;
+  if (icur >= 0) load_visitor<D>(q, dout, rec, g, bi, hk * g.G, icur, stage[0], w, l);
+  int st = 0;
+  while (icur >= 0) {
+    // next visitor: the next head of this query block, else the next block
+    int inext = icur, hnext = hcur + 1;
+    if (hnext == g.G) {
+      hnext = 0;
+      inext = bw.next();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the visitor
+    __syncthreads();                     // everyone's; the other stage is free
+    if (inext >= 0)
+      load_visitor<D>(q, dout, rec, g, bi, hk * g.G + hnext, inext, stage[st ^ 1], w, l);
+    const unsigned char* Qt = stage[st];
+    const unsigned char* Ot = stage[st] + TG::TILE;
+    const float* aux = reinterpret_cast<const float*>(stage[st] + 2 * TG::TILE);
+    // S = Q K^T and dP = dO V^T for rows rh*32 .. +31 (M) and the wave's keys (N)
+    f32x16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s[e] = 0.f;
+      dp[e] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Qt, rh * 32, ks, l), as_bf16x8(kb[ks]),
+                                                  s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Ot, rh * 32, ks, l), as_bf16x8(vb[ks]),
+                                                   dp, 0, 0, 0);
+    }
+    // element e of the lane: row rh*32 + (e/4)*8 + half*4 + e%4 of the block, key kpos
+    const int64_t qpos0 = (int64_t)icur * PYR_BLOCK;
+    f32x16 pf, dsf;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int rr = rh * 32 + g4 * 8 + half * 4;  // first of the lane's 4 rows in this group
+      const float4 ls = *reinterpret_cast<const float4*>(aux + rr);
+      const float4 dd = *reinterpret_cast<const float4*>(aux + 64 + rr);
+      const float lv[4] = {ls.x, ls.y, ls.z, ls.w};
+      const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int e = g4 * 4 + e4;
+        const int64_t qp = qpos0 + rr + e4;  // the row's position
+        const bool vis = kpos <= qp && qp < g.Tq;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -lv[e4]));
+        pf[e] = vis ? p : 0.f;
+        dsf[e] = vis ? p * (dp[e] - dv4[e4]) : 0.f;
+      }
+    }
+    bf16x8 pb[2], dsb[2];
+    pack_b(pf, pb);
+    pack_b(dsf, dsb);
+    // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 rows
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(Ot, rh * 32 + 16 * k2, dt, l),
+                                                          pb[k2], dva[dt], 0, 0, 0);
+        dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(Qt, rh * 32 + 16 * k2, dt, l),
+                                                          dsb[k2], dka[dt], 0, 0, 0);
+      }
+    icur = inext;
+    hcur = hnext;
+    st ^= 1;
+  }
+
+  // the two row halves of a key tile add up: waves with rh = 1 hand their sums
+  // to the waves with rh = 0 through LDS (the stages are free now)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&stage[0][0]);  // [kt][dt][k or v][e][lane]
+  static_assert(2 * (D / 32) * 2 * 16 * 64 * 4 <= 2 * SG::BYTES, "reduction must fit the stages");
+  if (rh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        red[(((kt * (D / 32) + dt) * 2 + 0) * 16 + e) * 64 + l] = dka[dt][e];
+        red[(((kt * (D / 32) + dt) * 2 + 1) * 16 + e) * 64 + l] = dva[dt][e];
+      }
+  }
+  __syncthreads();
+  if (rh == 1 || kpos >= g.Tk) return;
+  bf16_t* dko = dk + (kbase + kpos) * D;
+  bf16_t* dvo = dv + (kbase + kpos) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4_t pk, pv;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int e = g4 * 4 + e4;
+        const float sk = dka[dt][e] + red[(((kt * (D / 32) + dt) * 2 + 0) * 16 + e) * 64 + l];
+        const float sv = dva[dt][e] + red[(((kt * (D / 32) + dt) * 2 + 1) * 16 + e) * 64 + l];
+        pk[e4] = (__bf16)(sk * g.scale);
+        pv[e4] = (__bf16)sv;
+      }
+      *reinterpret_cast<bf16x4_t*>(dko + dt * 32 + g4 * 8 + half * 4) = pk;
+      *reinterpret_cast<bf16x4_t*>(dvo + dt * 32 + g4 * 8 + half * 4) = pv;
+    }
+}
+
+// workspace: D rows, then the route bitmap
+int bitmap_words(const PyrGeom& g) { return (g.nqb + 31) / 32; }
+size_t rec_bytes(const PyrGeom& g) { return (size_t)g.B * g.Hq * g.nqb * kRec * 4; }
+
+template <int D>
+hipError_t launch_bwd_d(const PyrGeom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                        const int32_t* sel, const bf16_t* o, const float* lse,
+                        const bf16_t* dout, bf16_t* dq, bf16_t* dk, bf16_t* dv, void* ws,
+                        hipStream_t st) {
+  float* rec = static_cast<float*>(ws);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) + rec_bytes(g));
+  const int words = bitmap_words(g);
+  const int64_t rows = (int64_t)g.B * g.Hq * g.nqb * PYR_BLOCK;
+  constexpr int TPR = D / 8;
+  hipLaunchKernelGGL((bwd_dsum<D>), dim3((unsigned)((rows + 256 / TPR - 1) / (256 / TPR))), dim3(256),
+                     0, st, o, dout, lse, rec, g);
+  const int64_t nbits = (int64_t)g.B * g.Hk * g.nb * words;
+  const int64_t clear_wgs = (nbits + 255) / 256 < 4096 ? (nbits + 255) / 256 : 4096;
+  hipLaunchKernelGGL(bwd_route_clear, dim3((unsigned)clear_wgs),
+                     dim3(256), 0, st, bits, nbits);
+  const int64_t nent = (int64_t)g.B * g.Hk * g.nqb * (g.K + 1);
+  hipLaunchKernelGGL(bwd_route_bits, dim3((unsigned)((nent + 255) / 256)), dim3(256), 0, st, sel,
+                     bits, g, words);
+  const int nh = g.G % 4 == 0 ? 4 : (g.G % 2 == 0 ? 2 : 1);
+  const int wpu = g.G / nh;
+  const dim3 grid((unsigned)((int64_t)g.B * g.Hk * g.nqb * wpu));
+  if (nh == 4)
+    hipLaunchKernelGGL((bwd_dq<D, 8>), grid, dim3(512), 0, st, q, k, v, sel, dout, rec, dq, g, wpu);
+  else if (nh == 2)
+    hipLaunchKernelGGL((bwd_dq<D, 4>), grid, dim3(256), 0, st, q, k, v, sel, dout, rec, dq, g, wpu);
+  else
+    hipLaunchKernelGGL((bwd_dq<D, 2>), grid, dim3(128), 0, st, q, k, v, sel, dout, rec, dq, g, wpu);
+  hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)((int64_t)g.B * g.Hk * g.nb)), dim3(256), 0, st,
+                     q, k, v, dout, rec, bits, dk, dv, g, words);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t pyr_attn_bwd_ws_bytes(const PyrGeom& g) {
+  return rec_bytes(g) + (size_t)g.B * g.Hk * g.nb * bitmap_words(g) * 4;
+}
+
+hipError_t pyr_launch_attn_bwd(const PyrGeom& g, const void* q, const void* k, const void* v,
+                               const int32_t* sel, const void* o, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, void* ws,
+                               hipStream_t st) {
+  const bf16_t* qq = static_cast<const bf16_t*>(q);
+  const bf16_t* kk = static_cast<const bf16_t*>(k);
+  const bf16_t* vv = static_cast<const bf16_t*>(v);
+  const bf16_t* oo = static_cast<const bf16_t*>(o);
+  const bf16_t* dd = static_cast<const bf16_t*>(dout);
+  bf16_t* dqq = static_cast<bf16_t*>(dq);
+  bf16_t* dkk = static_cast<bf16_t*>(dk);
+  bf16_t* dvv = static_cast<bf16_t*>(dv);
+  return g.D == 64 ? launch_bwd_d<64>(g, qq, kk, vv, sel, oo, lse, dd, dqq, dkk, dvv, ws, st)
+                   : launch_bwd_d<128>(g, qq, kk, vv, sel, oo, lse, dd, dqq, dkk, dvv, ws, st);
+}

@@ -197,6 +197,44 @@ pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void
                     "pyr_block_sparse_attn launch");
 }
 
+size_t pyr_attn_bwd_workspace_bytes(const pyr_problem* p) {
+  PyrGeom g;
+  return resolve(p, &g) == PYR_OK ? pyr_attn_bwd_ws_bytes(g) : 0;
+}
+
+pyr_status pyr_block_sparse_attn_bwd(const pyr_problem* p, const void* q, const void* k,
+                                     const void* v, const int32_t* sel, const void* o,
+                                     const float* lse, const void* dout, void* dq, void* dk,
+                                     void* dv, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  g_err[0] = 0;
+  PyrGeom g;
+  pyr_status s = resolve(p, &g);
+  if (s != PYR_OK) return s;
+  if (g.decode) return fail(PYR_ERR_UNSUPPORTED, "the backward is implemented for prefill only");
+  if (p->dtype != PYR_BF16)
+    return fail(PYR_ERR_UNSUPPORTED, "the backward is implemented for bfloat16 only");
+  if (g.K + 1 > PYR_BWD_MAX_SLOTS)
+    return fail(PYR_ERR_UNSUPPORTED, "route rows of %d slots (at most %d)", g.K + 1,
+                PYR_BWD_MAX_SLOTS);
+  const bool empty = (int64_t)g.B * g.Hk == 0 || g.Tq == 0;
+  if (!empty && (!q || !k || !v || !sel || !o || !lse || !dout || !dq || !dk || !dv))
+    return fail(PYR_ERR_NULL, "q, k, v, sel, o, lse, dout, dq, dk or dv is NULL");
+  if (!empty && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) ||
+                 !aligned16(o) || !aligned16(lse) || !aligned16(dout) || !aligned16(dq) ||
+                 !aligned16(dk) || !aligned16(dv)))
+    return fail(PYR_ERR_MISALIGNED, "tensors must be 16-byte aligned");
+  const size_t need = pyr_attn_bwd_ws_bytes(g);
+  if (!empty && (!workspace || workspace_bytes < need))
+    return fail(PYR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!empty && !aligned16(workspace))
+    return fail(PYR_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  if (empty) return PYR_OK;
+  return hip_status(pyr_launch_attn_bwd(g, q, k, v, sel, o, lse, dout, dq, dk, dv, workspace, stream),
+                    "pyr_block_sparse_attn_bwd launch");
+}
+
 const char* pyr_status_string(pyr_status s) {
   switch (s) {
     case PYR_OK: return "ok";

@@ -43,5 +43,13 @@ size_t pyr_attn_ws_bytes(const PyrGeom& g);
 hipError_t pyr_launch_attn(const PyrGeom& g, int dtype, const void* q, const void* k,
                            const void* v, const int32_t* sel, void* o, float* lse, void* ws,
                            hipStream_t st);
+// Backward of the attention (bfloat16 prefill): workspace bytes and launcher.
+size_t pyr_attn_bwd_ws_bytes(const PyrGeom& g);
+hipError_t pyr_launch_attn_bwd(const PyrGeom& g, const void* q, const void* k, const void* v,
+                               const int32_t* sel, const void* o, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, void* ws,
+                               hipStream_t st);
+// Route-row capacity of the backward's dQ kernel (slots K+1 it stages on chip).
+#define PYR_BWD_MAX_SLOTS 1024
 // Selection kernels need this much dynamic LDS (bytes); validated on the host.
 size_t pyr_select_lds_bytes(const PyrGeom& g, int dtype);

@@ -174,3 +174,38 @@ def planted_blocks(cfg: Config):
                 out[(bi, hk, i)] = set(int(x) for x in rng.choice(i, size=min(cfg.n_planted, i),
                                                                   replace=False))
     return out
+
+
+def make_grad_out(cfg: Config, device="cpu"):
+    """dL/do for the backward: iid N(0, 1) of q's shape in the config's dtype."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(3000 + cfg.seed)
+    shape = (cfg.batch, cfg.n_q_heads, cfg.q_len, cfg.head_dim)
+    return _randn(shape, gen, device, torch.float32).to(cfg.dtype)
+
+
+def make_route(cfg: Config, with_invalid: bool = True):
+    """A synthetic prefill route table [B, Hk, nqb, K+1] int32 (CPU): every row
+    lists its diagonal block, then up to K distinct other blocks drawn uniformly
+    from all blocks (future ones included: they are fully masked), in random
+    order, -1 padded; with_invalid puts an out-of-range id (nb) into some rows.
+    Used to drive the attention and its backward over routes the selection
+    would not produce."""
+    rng = np.random.default_rng(4000 + cfg.seed)
+    nb = -(-cfg.kv_len // cfg.block)
+    nqb = -(-cfg.q_len // cfg.block)
+    K = cfg.top_k
+    out = np.full((cfg.batch, cfg.n_kv_heads, nqb, K + 1), -1, dtype=np.int32)
+    for bi in range(cfg.batch):
+        for hk in range(cfg.n_kv_heads):
+            for i in range(nqb):
+                others = [j for j in range(nb) if j != i]
+                n = int(rng.integers(0, min(K, len(others)) + 1))
+                row = [i] + [int(x) for x in rng.choice(others, size=n, replace=False)]
+                if with_invalid and n < K and rng.random() < 0.25:
+                    row.append(nb)
+                rng.shuffle(row)
+                out[bi, hk, i, :len(row)] = row
+    return torch.from_numpy(out)
+

@@ -159,6 +159,45 @@ pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void
                                  const void* v, const int32_t* sel, void* o, float* lse,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- training: backward of the attention for a fixed route table ---- */
+
+/* Bytes of device workspace pyr_block_sparse_attn_bwd needs (0 on invalid
+ * input): a 512-byte record per (batch, query head, query block) plus a
+ * [B, Hk, ceil(kv_len/64), ceil(nqb/32)] uint32 route bitmap. */
+size_t pyr_attn_bwd_workspace_bytes(const pyr_problem* p);
+
+/* Gradients of pyr_block_sparse_attn with respect to q, k and v (PHBA §A.1.4:
+ * the route is fixed, the sparse scores and probabilities are recomputed on
+ * chip from the forward's log-sum-exp, and the query rows that use each key
+ * block are enumerated block-major for the key gradients).  With P the
+ * forward's probabilities over each row's visible keys, dP = dout v^T,
+ * D = rowsum(dout * o) and dS = P * (dP - D):
+ *   dq = scale dS k,   dk = scale dS^T q,   dv = P^T dout,
+ * where dk and dv of a KV head sum the contributions of its G query heads.
+ * Prefill, bfloat16 only (else PYR_ERR_UNSUPPORTED); fp32 accumulation, one
+ * bfloat16 rounding per output.
+ *   q, k, v    the forward's inputs, shapes as in pyr_block_sparse_attn (input)
+ *   sel        the forward's route rows [B, Hk, nqb, K+1]; entries outside
+ *              [0, ceil(kv_len/64)) are ignored.  A block listed twice in one
+ *              row counts twice in dq but once in dk and dv, so rows must list
+ *              each block at most once (pyr_select_topk's rows do)     (input)
+ *   o, lse     the forward's output [B, Hq, q_len, d] and log-sum-exp
+ *              [B, Hq, q_len] float32 (both required)                  (input)
+ *   dout       dL/do, [B, Hq, q_len, d] bfloat16                       (input)
+ *   dq         [B, Hq, q_len, d] bfloat16                              (output)
+ *   dk, dv     [B, Hk, kv_len, d] bfloat16; keys no row sees get 0     (output)
+ *   workspace  device scratch of workspace_bytes >=
+ *              pyr_attn_bwd_workspace_bytes(p), 16-byte aligned; its
+ *              contents on entry do not matter.
+ * A row whose lse is not finite (it saw no key) gets a zero dq and adds
+ * nothing to dk and dv.  The result does not depend on scheduling: no
+ * gradient is accumulated with atomics, so repeated calls give identical bits. */
+pyr_status pyr_block_sparse_attn_bwd(const pyr_problem* p, const void* q, const void* k,
+                                     const void* v, const int32_t* sel, const void* o,
+                                     const float* lse, const void* dout, void* dq, void* dk,
+                                     void* dv, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* ---- diagnostics ---- */
 const char* pyr_status_string(pyr_status s);
 /* Thread-local detail of the last non-OK return on this thread ("" if none). */

@@ -152,3 +152,61 @@ def test_binding_rejects_wrong_shapes_on_host():
     k = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         H.pyr_build_pyramid(p, k, torch.zeros(1))
+
+
+def _bwd(p, ptrs, ws=None, nbytes=0):
+    """Call pyr_block_sparse_attn_bwd with the ten tensor pointers `ptrs`
+    (q, k, v, sel, o, lse, dout, dq, dk, dv)."""
+    return _status("pyr_block_sparse_attn_bwd", ctypes.byref(p.c()), *ptrs, ws, nbytes, None)
+
+
+def test_backward_validation_before_launch():
+    ptr = ctypes.c_void_p(16)
+    full = [ptr] * 10
+    p = _p()
+    need = H.pyr_attn_bwd_workspace_bytes(p)
+    nqb, nb = 4096 // 64, 4096 // 64
+    # records of 512 bytes per (batch, query head, query block) + the route bitmap
+    assert need == 1 * 4 * nqb * 512 + 1 * 2 * nb * ((nqb + 31) // 32) * 4
+    s, msg = _bwd(p, full)
+    assert s == 5 and "workspace" in msg
+    s, _ = _bwd(p, full, ptr, need - 1)
+    assert s == 5
+    s, _ = _bwd(p, full, ctypes.c_void_p(24), need)
+    assert s == 4
+    for i in range(10):      # each tensor is required
+        ptrs = list(full)
+        ptrs[i] = None
+        s, msg = _bwd(p, ptrs, ptr, need)
+        assert s == 1 and "NULL" in msg
+        ptrs[i] = ctypes.c_void_p(18)
+        s, _ = _bwd(p, ptrs, ptr, need)
+        assert s == 4
+    # bfloat16 prefill only
+    s, msg = _bwd(_p(dtype=torch.float32), full, ptr, need)
+    assert s == 3 and "bfloat16" in msg
+    s, msg = _bwd(_p(q_len=1, kv_len=4096), full, ptr, need)
+    assert s == 3 and "prefill" in msg
+    assert H.pyr_attn_bwd_workspace_bytes(_p(head_dim=96)) == 0
+
+
+def test_backward_empty_problems_are_noops():
+    for kw in (dict(batch=0), dict(q_len=0, kv_len=0)):
+        assert _bwd(_p(**kw), [None] * 10)[0] == 0
+
+
+def test_backward_binding_rejects_wrong_shapes_on_host(monkeypatch):
+    # host tensors stand in for device ones so that the shape checks are reached
+    orig = B._expect
+    monkeypatch.setattr(B, "_expect", lambda t, n, s, d, device_type="cuda": orig(t, n, s, d, "cpu"))
+    p = _p(q_len=128, kv_len=128)
+    q = torch.zeros((1, 4, 128, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, 128, 128), dtype=torch.bfloat16)
+    sel = torch.zeros((1, 2, 2, 9), dtype=torch.int32)
+    lse = torch.zeros((1, 4, 128))
+    with pytest.raises(ValueError, match="dk: shape"):
+        H.pyr_block_sparse_attn_bwd(p, q, k, k, sel, q, lse, q, q, q, k, None)
+    with pytest.raises(ValueError, match="lse: dtype"):
+        H.pyr_block_sparse_attn_bwd(p, q, k, k, sel, q, lse.double(), q, q, k, k, None)
+    with pytest.raises(ValueError, match="sel: shape"):
+        H.pyr_block_sparse_attn_bwd(p, q, k, k, sel[..., :4], q, lse, q, q, k, k, None)
