@@ -35,6 +35,8 @@
 //    the end.
 #include <math.h>
 
+#include <algorithm>
+
 #include "pyr_device.h"
 #include "pyr_internal.h"
 
@@ -176,7 +178,8 @@ __global__ __launch_bounds__(256) void bwd_route_clear(uint32_t* __restrict__ bi
 }
 
 __global__ __launch_bounds__(256) void bwd_route_bits(const int32_t* __restrict__ sel,
-                                                      uint32_t* __restrict__ bits, PyrGeom g,
+                                                      uint32_t* __restrict__ bits,
+                                                      int32_t* __restrict__ cnt, PyrGeom g,
                                                       int words) {
   const int64_t n = (int64_t)g.B * g.Hk * g.nqb * (g.K + 1);
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -186,7 +189,77 @@ __global__ __launch_bounds__(256) void bwd_route_bits(const int32_t* __restrict_
   if (j < 0 || j >= g.nb) return;
   const int64_t slab = unit / g.nqb;
   const int i = (int)(unit % g.nqb);
-  atomicOr(bits + (slab * g.nb + j) * words + i / 32, 1u << (i % 32));
+  const int64_t row = slab * g.nb + j;
+  const uint32_t bit = 1u << (i % 32);
+  // count each (query block, key block) pair once, even if a row lists it twice
+  if (!(atomicOr(bits + row * words + i / 32, bit) & bit)) atomicAdd(cnt + row, 1);
+}
+
+// Work list of the key-gradient kernel (count -> prefix sum -> scatter).  Key
+// block row r with cnt[r] visiting query blocks is one item when cnt[r] <= chq
+// ("light"), else ceil(cnt[r] / chq) items of chq query blocks each ("split"),
+// whose fp32 partial sums go to partial slots pslot[r] .. + items - 1 and are
+// added in slot order afterwards.  Split items are listed first, in row order
+// (hitems, slot = position), then the light rows (litems); hdr = {number of
+// split items, number of light rows}.  One workgroup scans all rows in tiles of
+// 1024.
+__global__ __launch_bounds__(1024) void bwd_route_plan(const int32_t* __restrict__ cnt,
+                                                       int32_t* __restrict__ pslot,
+                                                       int2* __restrict__ hitems,
+                                                       int2* __restrict__ litems,
+                                                       int32_t* __restrict__ hdr, int64_t rows,
+                                                       int chq) {
+  __shared__ int s_w[16][2];
+  __shared__ int s_carry[2];
+  const int tid = threadIdx.x, l = tid % 64, w = tid / 64;
+  if (tid == 0) {
+    s_carry[0] = 0;
+    s_carry[1] = 0;
+  }
+  __syncthreads();
+  for (int64_t base = 0; base < rows; base += 1024) {
+    const int64_t r = base + tid;
+    const int c = r < rows ? cnt[r] : 0;
+    const bool split = r < rows && c > chq;
+    const int hn = split ? (c + chq - 1) / chq : 0;
+    const int ln = (r < rows && !split) ? 1 : 0;
+    int hs = hn, ls = ln;  // inclusive scans within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int a = __shfl_up(hs, off, 64), b = __shfl_up(ls, off, 64);
+      if (l >= off) {
+        hs += a;
+        ls += b;
+      }
+    }
+    if (l == 63) {
+      s_w[w][0] = hs;
+      s_w[w][1] = ls;
+    }
+    __syncthreads();
+    int hpre = s_carry[0] + hs - hn, lpre = s_carry[1] + ls - ln;
+    for (int x = 0; x < w; ++x) {
+      hpre += s_w[x][0];
+      lpre += s_w[x][1];
+    }
+    if (split) {
+      pslot[r] = hpre;
+      for (int k2 = 0; k2 < hn; ++k2) hitems[hpre + k2] = make_int2((int)r, k2);
+    } else if (r < rows) {
+      pslot[r] = -1;
+      litems[lpre] = make_int2((int)r, 0);
+    }
+    __syncthreads();  // s_w and s_carry are read
+    if (tid == 1023) {
+      s_carry[0] = hpre + hn;
+      s_carry[1] = lpre + ln;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    hdr[0] = s_carry[0];
+    hdr[1] = s_carry[1];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -323,11 +396,23 @@ struct BitWalk {
   const uint32_t* row;
   int words, wi;
   uint32_t cur;
-  __device__ void start(const uint32_t* r, int n) {
+  // start at the row's set bit number `skip` (0-based)
+  __device__ void start(const uint32_t* r, int n, int skip) {
     row = r;
     words = n;
     wi = 0;
     cur = n > 0 ? __builtin_amdgcn_readfirstlane(r[0]) : 0u;
+    while (skip > 0) {  // whole words first
+      const int pc = __builtin_popcount(cur);
+      if (pc > skip) break;
+      skip -= pc;
+      if (++wi >= words) {
+        cur = 0u;
+        break;
+      }
+      cur = __builtin_amdgcn_readfirstlane(row[wi]);
+    }
+    for (; skip > 0 && cur != 0u; --skip) cur &= cur - 1u;
   }
   // next query block, or -1 when none is left
   __device__ int next() {
@@ -366,22 +451,42 @@ __device__ __forceinline__ void load_visitor(const bf16_t* q, const bf16_t* dout
   }
 }
 
+// Work-list metadata of the key-gradient kernel.
+struct BwdList {
+  const uint32_t* bits;  // route bitmap, `words` words per key block row
+  const int32_t* cnt;    // visiting query blocks per row
+  const int2* hitems;    // split items (row, chunk), slot = position
+  const int2* litems;    // light rows (row, 0)
+  const int32_t* hdr;    // {split items, light rows}
+  float* part;           // [slot][dK, dV][64 keys][D] fp32 partial sums
+  int words, chq;
+};
+
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const bf16_t* __restrict__ dout, const float* __restrict__ rec,
-    const uint32_t* __restrict__ bits, bf16_t* __restrict__ dk,
-    bf16_t* __restrict__ dv, PyrGeom g, int words) {
+    const bf16_t* __restrict__ dout, const float* __restrict__ rec, BwdList wl,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, PyrGeom g) {
   using TG = BTile<D>;
   using SG = DkdvStage<D>;
   __shared__ __align__(16) unsigned char stage[2][SG::BYTES];
+
+  const int nsplit = wl.hdr[0], nlight = wl.hdr[1];
+  const int item = blockIdx.x;
+  if (item >= nsplit + nlight) return;
+  const int2 it = item < nsplit ? wl.hitems[item] : wl.litems[item - nsplit];
+  const int64_t krow = it.x;
+  const int ncnt = wl.cnt[krow];
+  const bool split = item < nsplit;
+  const int first = split ? it.y * wl.chq : 0;
+  const int nq = split ? min(wl.chq, ncnt - first) : ncnt;  // query blocks of this item
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int half = l / 32, lr = l % 32;
   const int kt = w & 1, rh = w >> 1;  // key tile and row half of this wave
-  const int64_t slab = blockIdx.x / g.nb;
-  const int j = (int)(blockIdx.x % g.nb);
+  const int64_t slab = krow / g.nb;
+  const int j = (int)(krow % g.nb);
   const int bi = (int)(slab / g.Hk), hk = (int)(slab % g.Hk);
   const float sl2 = g.scale * PYR_LOG2E;
   const int64_t kbase = slab * g.Tk;
@@ -407,8 +512,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
     }
 
   BitWalk bw;
-  bw.start(bits + (slab * g.nb + j) * words, words);
-  int icur = bw.next();
+  bw.start(wl.bits + krow * wl.words, wl.words, first);
+  int left = nq;
+  int icur = left > 0 ? bw.next() : -1;
   int hcur = 0;
   if (icur >= 0) load_visitor<D>(q, dout, rec, g, bi, hk * g.G, icur, stage[0], w, l);
   int st = 0;
@@ -417,7 +523,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
     int inext = icur, hnext = hcur + 1;
     if (hnext == g.G) {
       hnext = 0;
-      inext = bw.next();
+      inext = --left > 0 ? bw.next() : -1;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the visitor
     __syncthreads();                     // everyone's; the other stage is free
@@ -493,7 +599,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
       }
   }
   __syncthreads();
-  if (rh == 1 || kpos >= g.Tk) return;
+  if (rh == 1) return;
+  if (split) {  // unscaled fp32 sums into the item's slot
+    float* pk = wl.part + (int64_t)item * 2 * PYR_BLOCK * D + (kt * 32 + lr) * D;
+    float* pv = pk + PYR_BLOCK * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float4 a, b;
+        float* av = reinterpret_cast<float*>(&a);
+        float* bv = reinterpret_cast<float*>(&b);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int e = g4 * 4 + e4;
+          av[e4] = dka[dt][e] + red[(((kt * (D / 32) + dt) * 2 + 0) * 16 + e) * 64 + l];
+          bv[e4] = dva[dt][e] + red[(((kt * (D / 32) + dt) * 2 + 1) * 16 + e) * 64 + l];
+        }
+        *reinterpret_cast<float4*>(pk + dt * 32 + g4 * 8 + half * 4) = a;
+        *reinterpret_cast<float4*>(pv + dt * 32 + g4 * 8 + half * 4) = b;
+      }
+    return;
+  }
+  if (kpos >= g.Tk) return;
   bf16_t* dko = dk + (kbase + kpos) * D;
   bf16_t* dvo = dv + (kbase + kpos) * D;
 #pragma unroll
@@ -514,29 +642,114 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
     }
 }
 
-// workspace: D rows, then the route bitmap
-int bitmap_words(const PyrGeom& g) { return (g.nqb + 31) / 32; }
-size_t rec_bytes(const PyrGeom& g) { return (size_t)g.B * g.Hq * g.nqb * kRec * 4; }
+// Sum the partial slots of every split key block row in slot order, then
+// scale dK and round both to bfloat16.  One workgroup per row; light rows exit.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce(const int32_t* __restrict__ cnt,
+                                                       const int32_t* __restrict__ pslot,
+                                                       const float* __restrict__ part,
+                                                       bf16_t* __restrict__ dk,
+                                                       bf16_t* __restrict__ dv, PyrGeom g,
+                                                       int chq) {
+  const int64_t krow = blockIdx.x;
+  const int ps = pslot[krow];
+  if (ps < 0) return;
+  const int nch = (cnt[krow] + chq - 1) / chq;
+  const int64_t slab = krow / g.nb;
+  const int j = (int)(krow % g.nb);
+  constexpr int N4 = PYR_BLOCK * D / 4;  // float4 per slot half
+  for (int x = threadIdx.x; x < 2 * N4; x += 256) {
+    const int kv = x / N4, rem = x % N4;
+    const int key = rem / (D / 4), d4 = rem % (D / 4);
+    const int64_t kpos = (int64_t)j * PYR_BLOCK + key;
+    if (kpos >= g.Tk) continue;
+    const float4* src = reinterpret_cast<const float4*>(part) + ((int64_t)ps * 2 + kv) * N4 + rem;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < nch; ++c) {
+      const float4 b = src[(int64_t)c * 2 * N4];
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    const float sc = kv == 0 ? g.scale : 1.f;
+    bf16x4_t o4;
+    o4[0] = (__bf16)(a.x * sc);
+    o4[1] = (__bf16)(a.y * sc);
+    o4[2] = (__bf16)(a.z * sc);
+    o4[3] = (__bf16)(a.w * sc);
+    *reinterpret_cast<bf16x4_t*>((kv == 0 ? dk : dv) + (slab * g.Tk + kpos) * D + d4 * 4) = o4;
+  }
+}
+
+// Workspace plan: row records, route bitmap + counts (cleared together), then
+// the work list and the partial slots.
+struct BwdPlan {
+  int words, chq;
+  int64_t rows, slots;
+  size_t off_bits, off_cnt, off_pslot, off_hitems, off_litems, off_hdr, off_part, total;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+BwdPlan bwd_plan(const PyrGeom& g) {
+  BwdPlan p;
+  p.words = (g.nqb + 31) / 32;
+  p.rows = (int64_t)g.B * g.Hk * g.nb;
+  // visitors (query block, head) per item: about 1/4096 of the route's upper
+  // bound, between G and 256, so large problems get >= ~4096 items of at most
+  // 256 visitors and small ones split rows finely
+  const int64_t entries = (int64_t)g.B * g.Hk * g.nqb * (g.K + 1);
+  const int64_t budget = std::min<int64_t>(std::max<int64_t>(entries * g.G / 4096, g.G),
+                                           std::max(256, g.G));
+  p.chq = (int)std::max<int64_t>(1, budget / g.G);
+  // a split row with c > chq visitors has ceil(c / chq) < 2c / chq items
+  p.slots = (2 * entries + p.chq - 1) / p.chq;
+  size_t off = align256((size_t)g.B * g.Hq * g.nqb * kRec * 4);
+  p.off_bits = off;
+  p.off_cnt = off + (size_t)p.rows * p.words * 4;
+  off = align256(p.off_cnt + (size_t)p.rows * 4);
+  p.off_pslot = off;
+  off = align256(off + (size_t)p.rows * 4);
+  p.off_hitems = off;
+  off = align256(off + (size_t)p.slots * 8);
+  p.off_litems = off;
+  off = align256(off + (size_t)p.rows * 8);
+  p.off_hdr = off;
+  off = align256(off + 16);
+  p.off_part = off;
+  p.total = off + (size_t)p.slots * 2 * PYR_BLOCK * g.D * 4;
+  return p;
+}
 
 template <int D>
 hipError_t launch_bwd_d(const PyrGeom& g, const bf16_t* q, const bf16_t* k, const bf16_t* v,
                         const int32_t* sel, const bf16_t* o, const float* lse,
                         const bf16_t* dout, bf16_t* dq, bf16_t* dk, bf16_t* dv, void* ws,
                         hipStream_t st) {
-  float* rec = static_cast<float*>(ws);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) + rec_bytes(g));
-  const int words = bitmap_words(g);
+  const BwdPlan pl = bwd_plan(g);
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  float* rec = reinterpret_cast<float*>(base);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(base + pl.off_bits);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + pl.off_cnt);
+  int32_t* pslot = reinterpret_cast<int32_t*>(base + pl.off_pslot);
+  int2* hitems = reinterpret_cast<int2*>(base + pl.off_hitems);
+  int2* litems = reinterpret_cast<int2*>(base + pl.off_litems);
+  int32_t* hdr = reinterpret_cast<int32_t*>(base + pl.off_hdr);
+  float* part = reinterpret_cast<float*>(base + pl.off_part);
+
   const int64_t rows = (int64_t)g.B * g.Hq * g.nqb * PYR_BLOCK;
   constexpr int TPR = D / 8;
   hipLaunchKernelGGL((bwd_dsum<D>), dim3((unsigned)((rows + 256 / TPR - 1) / (256 / TPR))), dim3(256),
                      0, st, o, dout, lse, rec, g);
-  const int64_t nbits = (int64_t)g.B * g.Hk * g.nb * words;
-  const int64_t clear_wgs = (nbits + 255) / 256 < 4096 ? (nbits + 255) / 256 : 4096;
-  hipLaunchKernelGGL(bwd_route_clear, dim3((unsigned)clear_wgs),
-                     dim3(256), 0, st, bits, nbits);
+  const int64_t nclear = pl.rows * pl.words + pl.rows;  // bitmap and counts
+  const int64_t clear_wgs = std::min<int64_t>((nclear + 255) / 256, 4096);
+  hipLaunchKernelGGL(bwd_route_clear, dim3((unsigned)clear_wgs), dim3(256), 0, st, bits, nclear);
   const int64_t nent = (int64_t)g.B * g.Hk * g.nqb * (g.K + 1);
   hipLaunchKernelGGL(bwd_route_bits, dim3((unsigned)((nent + 255) / 256)), dim3(256), 0, st, sel,
-                     bits, g, words);
+                     bits, cnt, g, pl.words);
+  hipLaunchKernelGGL(bwd_route_plan, dim3(1), dim3(1024), 0, st, cnt, pslot, hitems, litems, hdr,
+                     pl.rows, pl.chq);
   const int nh = g.G % 4 == 0 ? 4 : (g.G % 2 == 0 ? 2 : 1);
   const int wpu = g.G / nh;
   const dim3 grid((unsigned)((int64_t)g.B * g.Hk * g.nqb * wpu));
@@ -546,15 +759,29 @@ hipError_t launch_bwd_d(const PyrGeom& g, const bf16_t* q, const bf16_t* k, cons
     hipLaunchKernelGGL((bwd_dq<D, 4>), grid, dim3(256), 0, st, q, k, v, sel, dout, rec, dq, g, wpu);
   else
     hipLaunchKernelGGL((bwd_dq<D, 2>), grid, dim3(128), 0, st, q, k, v, sel, dout, rec, dq, g, wpu);
-  hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)((int64_t)g.B * g.Hk * g.nb)), dim3(256), 0, st,
-                     q, k, v, dout, rec, bits, dk, dv, g, words);
+  BwdList wl;
+  wl.bits = bits;
+  wl.cnt = cnt;
+  wl.hitems = hitems;
+  wl.litems = litems;
+  wl.hdr = hdr;
+  wl.part = part;
+  wl.words = pl.words;
+  wl.chq = pl.chq;
+  hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)(pl.rows + pl.slots)), dim3(256), 0, st, q, k, v,
+                     dout, rec, wl, dk, dv, g);
+  hipLaunchKernelGGL((bwd_dkdv_reduce<D>), dim3((unsigned)pl.rows), dim3(256), 0, st, cnt, pslot,
+                     part, dk, dv, g, pl.chq);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t pyr_attn_bwd_ws_bytes(const PyrGeom& g) {
-  return rec_bytes(g) + (size_t)g.B * g.Hk * g.nb * bitmap_words(g) * 4;
+size_t pyr_attn_bwd_ws_bytes(const PyrGeom& g) { return bwd_plan(g).total; }
+
+int64_t pyr_attn_bwd_items_bound(const PyrGeom& g) {
+  const BwdPlan p = bwd_plan(g);
+  return p.rows + p.slots;
 }
 
 hipError_t pyr_launch_attn_bwd(const PyrGeom& g, const void* q, const void* k, const void* v,

@@ -218,6 +218,8 @@ pyr_status pyr_block_sparse_attn_bwd(const pyr_problem* p, const void* q, const 
     return fail(PYR_ERR_UNSUPPORTED, "route rows of %d slots (at most %d)", g.K + 1,
                 PYR_BWD_MAX_SLOTS);
   const bool empty = (int64_t)g.B * g.Hk == 0 || g.Tq == 0;
+  if (!empty && pyr_attn_bwd_items_bound(g) > INT32_MAX)
+    return fail(PYR_ERR_UNSUPPORTED, "problem too large for the backward's work list");
   if (!empty && (!q || !k || !v || !sel || !o || !lse || !dout || !dq || !dk || !dv))
     return fail(PYR_ERR_NULL, "q, k, v, sel, o, lse, dout, dq, dk or dv is NULL");
   if (!empty && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) ||

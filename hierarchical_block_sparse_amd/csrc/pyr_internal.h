@@ -45,6 +45,8 @@ hipError_t pyr_launch_attn(const PyrGeom& g, int dtype, const void* q, const voi
                            hipStream_t st);
 // Backward of the attention (bfloat16 prefill): workspace bytes and launcher.
 size_t pyr_attn_bwd_ws_bytes(const PyrGeom& g);
+// Upper bound on the work items of the key-gradient kernel (its grid size).
+int64_t pyr_attn_bwd_items_bound(const PyrGeom& g);
 hipError_t pyr_launch_attn_bwd(const PyrGeom& g, const void* q, const void* k, const void* v,
                                const int32_t* sel, const void* o, const float* lse,
                                const void* dout, void* dq, void* dk, void* dv, void* ws,

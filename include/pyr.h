@@ -162,8 +162,13 @@ pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void
 /* ---- training: backward of the attention for a fixed route table ---- */
 
 /* Bytes of device workspace pyr_block_sparse_attn_bwd needs (0 on invalid
- * input): a 512-byte record per (batch, query head, query block) plus a
- * [B, Hk, ceil(kv_len/64), ceil(nqb/32)] uint32 route bitmap. */
+ * input): a 512-byte record per (batch, query head, query block), the
+ * block-major route metadata (a bitmap of ceil(nqb/32) uint32 per key block,
+ * counts and a work list) and fp32 partial sums for key blocks that many query
+ * blocks use; the partial area is sized for the worst case the route shape
+ * allows, 2 * B * Hk * nqb * (K+1) / c slots of 64 * d * 8 bytes, where c is
+ * the number of query blocks per work item (1 .. 256/G, larger for larger
+ * problems). */
 size_t pyr_attn_bwd_workspace_bytes(const pyr_problem* p);
 
 /* Gradients of pyr_block_sparse_attn with respect to q, k and v (PHBA §A.1.4:

@@ -166,8 +166,10 @@ def test_backward_validation_before_launch():
     p = _p()
     need = H.pyr_attn_bwd_workspace_bytes(p)
     nqb, nb = 4096 // 64, 4096 // 64
-    # records of 512 bytes per (batch, query head, query block) + the route bitmap
-    assert need == 1 * 4 * nqb * 512 + 1 * 2 * nb * ((nqb + 31) // 32) * 4
+    # at least the records of 512 bytes per (batch, query head, query block) and
+    # the route bitmap; at most that plus metadata and a partial slot per entry
+    base = 1 * 4 * nqb * 512 + 1 * 2 * nb * ((nqb + 31) // 32) * 4
+    assert base < need <= base + 2 * 1 * 2 * nqb * 9 * (64 * 128 * 8 + 64) + 8192
     s, msg = _bwd(p, full)
     assert s == 5 and "workspace" in msg
     s, _ = _bwd(p, full, ptr, need - 1)

@@ -45,6 +45,9 @@ CASES = [
     C("bwd_tiny", 1, 4, 2, 5, 5, 64, BF, 2, 1, 0, seed=36),
     # more than 32 query blocks (two bitmap words per key block), G=4, d=64
     C("bwd_two_words", 1, 4, 1, 64 * 70 + 9, 64 * 70 + 9, 64, BF, 4, 6, 2, seed=37),
+    # 400 query blocks: key block rows split into work items of 3 query blocks
+    # (multi-word rows, chunks across word boundaries, light and split rows)
+    C("bwd_chunked", 1, 8, 2, 64 * 400, 64 * 400, 64, BF, 4, 15, 4, seed=39),
 ]
 REL_MAX, REL_FRO = 2e-2, 1e-2
 
