@@ -11,6 +11,12 @@ recorded on the stream the library launches on.
 Prints one JSON line.  `value` is tokens/s of the whole path; `roofline`
 describes the dominant kernel (the attention); `cpu_baseline` is the float64
 CPU oracle timed on this host over a bounded sample of the same workload.
+
+With --backward (prefill workloads) a step is the training pass of the path:
+build -> select -> attention -> pyr_block_sparse_attn_bwd for a seeded dL/do,
+`value` is tokens/s of that pass and `roofline` describes the backward call
+(its flops counted as 10 d per visible (query row, key) pair per head: the
+recomputed scores, dP, dQ, dK and dV products).
 """
 
 from __future__ import annotations
@@ -28,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "select+sparse-attn tokens/s at T=128K; TFLOP/s & HBM GB/s as % of peak"
+METRIC_BWD = "training pass (select+sparse-attn forward + attention backward) tokens/s"
 
 
 def parse():
@@ -39,6 +46,8 @@ def parse():
                     choices=["gqa_128k", "mha_32k", "prefill_1m", "decode_256k", "tiny_fp32"])
     ap.add_argument("--cpu-baseline-units", type=int, default=2048,
                     help="units of the workload the oracle runs for the CPU baseline (0: skip)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the training pass (forward + backward of the attention)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (counter calibration)")
     return ap.parse_args()
@@ -135,7 +144,7 @@ def scored_candidates(cfg):
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(cfg, q, k, v, n_units):
+def cpu_baseline(cfg, q, k, v, n_units, backward=False):
     import math
 
     import numpy as np
@@ -174,7 +183,11 @@ def cpu_baseline(cfg, q, k, v, n_units):
                                        cfg.top_k, scale)
             pos = reference.query_positions(cfg.q_len, cfg.kv_len)[toks]
             for h in range(cfg.group):
-                reference.attend_rows(q64[0, h, toks], pos, k64[0, 0], v64[0, 0], us.sel, 64, scale)
+                o_h, lse_h = reference.attend_rows(q64[0, h, toks], pos, k64[0, 0], v64[0, 0],
+                                                   us.sel, 64, scale)
+                if backward:   # dL/do = o stands in for a gradient of the same shape
+                    reference.attend_rows_backward(q64[0, h, toks], pos, k64[0, 0], v64[0, 0],
+                                                   us.sel, 64, scale, o_h, lse_h)
         t_units = time.perf_counter() - t0
     n_bh = len(bh_pairs)
     # decode steps start from a prebuilt pyramid, as on the device
@@ -182,7 +195,8 @@ def cpu_baseline(cfg, q, k, v, n_units):
     tokens = cfg.batch * (1 if cfg.decode else cfg.q_len)
     return {
         "value": tokens / total, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-        "sample": (f"float64 NumPy oracle on {len(units)} of {nqb * n_bh} units (one batch/KV-head "
+        "sample": (("forward + backward: " if backward else "") +
+                   f"float64 NumPy oracle on {len(units)} of {nqb * n_bh} units (one batch/KV-head "
                    f"slab: pyramid {t_pyr:.2f}s, units {t_units:.2f}s; D2H copy {t_copy:.2f}s "
                    f"excluded); whole-workload time extrapolated as pyramid x {n_bh} slabs + "
                    f"mean unit time x {nqb * n_bh} units"),
@@ -199,11 +213,11 @@ def attn_kernel_name(cfg):
     return "attn_prefill_ilv" if cfg.group % 4 == 0 else "attn_prefill_mfma"
 
 
-def kernel_traffic(workload):
-    """HBM bytes per attention dispatch from the committed rocprofv3 counter
-    summary, if it was taken on the current attention source."""
-    path = os.path.join(ROOT, "profiles", f"attn_{workload}_pmc.json")
-    src = os.path.join(ROOT, "hierarchical_block_sparse_amd", "csrc", "attn.hip")
+def kernel_traffic(workload, kind="attn"):
+    """HBM bytes per dispatch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_pmc.json")
+    src = os.path.join(ROOT, "hierarchical_block_sparse_amd", "csrc", f"{kind}.hip")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -231,6 +245,9 @@ def main():
     from hierarchical_block_sparse_amd import workloads as W
 
     cfg = W.CONFIGS[args.workload]
+    if args.backward and (cfg.decode or cfg.dtype != torch.bfloat16):
+        print(json.dumps({"error": "the backward runs on bfloat16 prefill workloads"}), flush=True)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"# generating {cfg.name} inputs", file=sys.stderr, flush=True)
@@ -245,8 +262,12 @@ def main():
     stream = torch.cuda.current_stream()
     if cfg.decode:
         H.pyr_build_pyramid(p, k, pyr, stream)   # the cache's pyramid exists before decoding
+    if args.backward:
+        dout = W.make_grad_out(cfg, dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = H.alloc_bwd_workspace(p, dev)
 
-    n_stage = 3
+    n_stage = 4 if args.backward else 3
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stage + 1)]
           for _ in range(args.steps)]
 
@@ -263,6 +284,10 @@ def main():
         H.pyr_block_sparse_attn(p, q, k, v, sel, o, lse, ws, stream)
         if events:
             events[3].record(stream)
+        if args.backward:
+            H.pyr_block_sparse_attn_bwd(p, q, k, v, sel, o, lse, dout, dq, dk, dv, bws, stream)
+            if events:
+                events[4].record(stream)
 
     print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -285,7 +310,7 @@ def main():
     n_tot = H.pyr_pyramid_nodes(p)
     b_bytes = build_bytes(cfg, n_tot, H.pyr_pyramid_planes(p))
     s_flops, s_bytes = select_work(cfg, scored_candidates(cfg))
-    t_build, t_sel, t_attn = (x / 1e3 for x in stage_ms)
+    t_build, t_sel, t_attn = (x / 1e3 for x in stage_ms[:3])
     achieved = a_flops / t_attn / 1e12
     traffic = kernel_traffic(cfg.name)
     line = {
@@ -333,9 +358,29 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.backward:
+        t_bwd = stage_ms[3] / 1e3
+        b_flops = 5 * a_flops // 2
+        line["metric"] = METRIC_BWD
+        line["config"]["step"] = "build+select+attn+attn_bwd"
+        line["roofline"] = {
+            "kernel": "attn_bwd (dsum, route metadata, dq, dkdv, reduce)",
+            "bound": "mfma",
+            "achieved": round(b_flops / t_bwd / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(b_flops / t_bwd / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": kernel_traffic(cfg.name, "attn_bwd"),
+            "algorithmic_flops_per_launch": b_flops,
+            "avg_launch_ms": round(stage_ms[3], 4),
+        }
+        line["stages"]["attn_bwd"] = {"ms": round(stage_ms[3], 4),
+                                      "TFLOP/s": round(b_flops / t_bwd / 1e12, 2)}
     if args.cpu_baseline_units > 0:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_baseline_units)
+        # the backward costs the oracle about 2.5x the forward: a third of the units
+        n_units = max(4, args.cpu_baseline_units // 3) if args.backward else args.cpu_baseline_units
+        line["cpu_baseline"] = cpu_baseline(cfg, q, k, v, n_units, backward=args.backward)
     print(json.dumps(line), flush=True)
 
 

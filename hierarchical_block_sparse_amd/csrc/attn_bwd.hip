@@ -48,17 +48,21 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxSelB = PYR_BWD_MAX_SLOTS;  // route-row capacity staged in LDS
+constexpr int kMaxItemQ = 256;               // query blocks per key-gradient work item
 
 // A 64-row tile of bf16 rows of length D in LDS: row-major, the 16-byte chunks
-// of row r XOR-swizzled by swz(r) so that row-per-lane 16-byte reads are free
-// of bank conflicts.
+// of row r XOR-swizzled by swz(r), an even value that differs between the rows
+// of each group of 8 consecutive rows (per bank sweep).  Being even it keeps
+// the chunk pairs (2m, 2m+1) together, so both the row-per-lane 16-byte reads
+// (8 rows per pass) and the transposed 8-byte reads (4 rows x 32 bytes per 16
+// lanes) are free of bank conflicts.
 template <int D>
 struct BTile {
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int ROW = 2 * D;      // bytes per row
   static constexpr int TILE = 64 * ROW;  // bytes per tile
   static constexpr int RP = 256 / ROW;   // rows per 256-byte bank sweep
-  __device__ static int swz(int r) { return (r / RP) % CPR; }
+  __device__ static int swz(int r) { return 2 * ((r / RP) % (CPR / 2)); }
   // byte offset of logical 16-byte chunk c of row r
   __device__ static int off(int r, int c) { return r * ROW + ((c ^ swz(r)) << 4); }
 };
@@ -265,6 +269,106 @@ __global__ __launch_bounds__(1024) void bwd_route_plan(const int32_t* __restrict
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (unit, group of NH heads); two waves per head.
 // ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4v lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+// Row fragment (see row_frag) read through an LDS-typed pointer, which the
+// compiler does not order behind the global->LDS loads in flight.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag_l(const unsigned char* tile, int rb, int ks, int l) {
+  using TG = BTile<D>;
+  const lds_u8* p = (const lds_u8*)tile + TG::off(rb + l % 32, 2 * ks + l / 32);
+  return __builtin_bit_cast(bf16x8, *(const lds_u32x4*)p);
+}
+
+// Per-wave state of the dQ kernel.
+template <int D>
+struct DqWave {
+  uint4 qb[D / 16], ob[D / 16];  // Q^T, dO^T B fragments of the wave's 32 rows
+  f32x16 acc[D / 32];            // dQ^T
+  float lse2, dsr, sl2;
+  int64_t row0;
+};
+
+// One selected block: K and V tiles in `rd` (key block starting at key0).
+// First issues (if `wr`) the loads of block x+2 into `wr`: rd and wr are
+// distinct __shared__ arrays, so the compiler does not wait for those loads.
+template <int D, int NW>
+__device__ __forceinline__ void dq_step(DqWave<D>& s_, const unsigned char* rd, int64_t key0,
+                                        unsigned char* wr, int64_t key2, const bf16_t* kh,
+                                        const bf16_t* vh, int64_t Tk, int w, int lane) {
+  using TG = BTile<D>;
+  constexpr int NT = NW * 64;
+  int l = lane;
+  asm volatile("" : "+v"(l));  // LDS addresses are formed per step (not kept per stage)
+  const int half = l / 32, lr = l % 32;
+  if (wr) {
+    load_tile<D, NT>(kh, key2, Tk - 1, wr, w, l);
+    load_tile<D, NT>(vh, key2, Tk - 1, wr + TG::TILE, w, l);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned char* Kt = rd;
+  const unsigned char* Vt = rd + TG::TILE;
+  const bool need_mask = key0 + PYR_BLOCK - 1 > s_.row0;
+  const int rel = (int)(s_.row0 - key0) + lr;  // row position in the block's key coordinates
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    // row fragments of the K and V tiles, then S^T and dP^T, in PH phases
+    // (two when two waves share a SIMD and registers are scarce)
+    constexpr int PH = (D == 128 && NW == 8) ? 2 : 1;
+    constexpr int KS = D / 16 / PH;
+    f32x16 s, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s[e] = 0.f;
+      dp[e] = 0.f;
+    }
+#pragma unroll
+    for (int ph = 0; ph < PH; ++ph) {
+      bf16x8 fk[KS], fv[KS];
+#pragma unroll
+      for (int x = 0; x < KS; ++x) {
+        fk[x] = row_frag_l<D>(Kt, kt * 32, ph * KS + x, l);
+        fv[x] = row_frag_l<D>(Vt, kt * 32, ph * KS + x, l);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < KS; ++x) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[x], as_bf16x8(s_.qb[ph * KS + x]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[x], as_bf16x8(s_.ob[ph * KS + x]), dp, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // K^T fragments for dQ^T (independent of dS: in flight during the VALU work)
+    bf16x8 tk[2][D / 32];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) tk[k2][dt] = trans_frag<D>(Kt, kt * 32 + 16 * k2, dt, l);
+    __builtin_amdgcn_sched_barrier(0);
+    // S^T element e of the lane: key kt*32 + (e/4)*8 + half*4 + e%4, row lr
+    f32x16 ds;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kt * 32 + (e / 4) * 8 + half * 4 + (e % 4);
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[e], s_.sl2, -s_.lse2));
+      ds[e] = (need_mask && key > rel) ? 0.f : p * (dp[e] - s_.dsr);
+    }
+    bf16x8 dsb[2];
+    pack_b(ds, dsb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        s_.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tk[k2][dt], dsb[k2], s_.acc[dt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dq(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -273,9 +377,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq(
   using TG = BTile<D>;
   constexpr int NT = NW * 64;
   constexpr int NH = NW / 2;  // heads per workgroup
-  __shared__ __align__(16) unsigned char tiles[2][2][TG::TILE];  // [stage][K, V]
-  __shared__ int s_sel[kMaxSelB];
-  __shared__ int s_n;
+  constexpr int PER = 2 * (64 * TG::CPR / NT);  // global->LDS loads per block per wave
+  constexpr int WAIT_ONE = 0x0F70 | (PER & 15) | ((PER >> 4) << 14);  // vmcnt(PER)
+  // Three stages of K and V tiles, each its own __shared__ array, used in a
+  // fixed rotation (the loop is unrolled by three), so that the compiler can
+  // tell the stage a step reads from the one being loaded.
+  __shared__ __align__(16) unsigned char st0[2 * TG::TILE];
+  __shared__ __align__(16) unsigned char st1[2 * TG::TILE];
+  __shared__ __align__(16) unsigned char st2[2 * TG::TILE];
+  __shared__ int s_sel[kMaxSelB + 1];
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -286,95 +396,71 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq(
   const int64_t slab = ublk / g.nqb;
   const int bi = (int)(slab / g.Hk), hk = (int)(slab % g.Hk);
   const int h = hk * g.G + sub * NH + w / 2;
-  const int64_t row0 = (int64_t)i * PYR_BLOCK + (w % 2) * 32;  // first query token of the wave
-  const float sl2 = g.scale * PYR_LOG2E;
   const bf16_t* kh = k + slab * g.Tk * D;
   const bf16_t* vh = v + slab * g.Tk * D;
+  DqWave<D> s_;
+  s_.row0 = (int64_t)i * PYR_BLOCK + (w % 2) * 32;  // first query token of the wave
+  s_.sl2 = g.scale * PYR_LOG2E;
 
-  // compact route row (entries outside [0, nb) are skipped)
+  // compact route row (entries outside [0, nb) are skipped); count in s_sel[kMaxSelB]
   if (tid == 0) {
     int n = 0;
     for (int jj = 0; jj <= g.K; ++jj) {
       const int j = sel[ublk * (g.K + 1) + jj];
       if (j >= 0 && j < g.nb) s_sel[n++] = j;
     }
-    s_n = n;
+    s_sel[kMaxSelB] = n;
   }
   __syncthreads();
-  const int nsel = s_n;
-  if (nsel > 0)
-    load_tile<D, NT>(kh, (int64_t)s_sel[0] * PYR_BLOCK, g.Tk - 1, tiles[0][0], w, l);
-  if (nsel > 0)
-    load_tile<D, NT>(vh, (int64_t)s_sel[0] * PYR_BLOCK, g.Tk - 1, tiles[0][1], w, l);
+  const int nsel = s_sel[kMaxSelB];
+  if (nsel > 0) {
+    load_tile<D, NT>(kh, (int64_t)s_sel[0] * PYR_BLOCK, g.Tk - 1, st0, w, l);
+    load_tile<D, NT>(vh, (int64_t)s_sel[0] * PYR_BLOCK, g.Tk - 1, st0 + TG::TILE, w, l);
+  }
+  if (nsel > 1) {
+    load_tile<D, NT>(kh, (int64_t)s_sel[1] * PYR_BLOCK, g.Tk - 1, st1, w, l);
+    load_tile<D, NT>(vh, (int64_t)s_sel[1] * PYR_BLOCK, g.Tk - 1, st1 + TG::TILE, w, l);
+  }
 
   // Q^T and dO^T B fragments: lane holds query row row0 + lr, d = ks*16 + 8*half .. +7;
   // rows past the end load the last row (never stored).
-  const int64_t tok = min<int64_t>(row0 + lr, g.Tq - 1);
+  const int64_t tok = min<int64_t>(s_.row0 + lr, g.Tq - 1);
   const int64_t qrow = ((int64_t)bi * g.Hq + h) * g.Tq + tok;
-  uint4 qb[D / 16], ob[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    qb[ks] = ld16(q + qrow * D + ks * 16 + 8 * half);
-    ob[ks] = ld16(dout + qrow * D + ks * 16 + 8 * half);
+    s_.qb[ks] = ld16(q + qrow * D + ks * 16 + 8 * half);
+    s_.ob[ks] = ld16(dout + qrow * D + ks * 16 + 8 * half);
   }
   const float* rrow = rec + (((int64_t)bi * g.Hq + h) * g.nqb + i) * kRec + (w % 2) * 32 + lr;
-  const float lse2 = rrow[0];
-  const float dsr = rrow[PYR_BLOCK];
-  f32x16 acc[D / 32];
+  s_.lse2 = rrow[0];
+  s_.dsr = rrow[PYR_BLOCK];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+    for (int e = 0; e < 16; ++e) s_.acc[dt][e] = 0.f;
 
-  for (int jj = 0; jj < nsel; ++jj) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block jj
-    __syncthreads();                     // everyone's; the other stage is free
-    if (jj + 1 < nsel) {
-      const int64_t key1 = (int64_t)s_sel[jj + 1] * PYR_BLOCK;
-      load_tile<D, NT>(kh, key1, g.Tk - 1, tiles[(jj + 1) & 1][0], w, l);
-      load_tile<D, NT>(vh, key1, g.Tk - 1, tiles[(jj + 1) & 1][1], w, l);
-    }
-    const unsigned char* Kt = tiles[jj & 1][0];
-    const unsigned char* Vt = tiles[jj & 1][1];
-    const int64_t key0 = (int64_t)s_sel[jj] * PYR_BLOCK;
-    const bool need_mask = key0 + PYR_BLOCK - 1 > row0;
-    const int rel = (int)(row0 - key0) + lr;  // row position in the block's key coordinates
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[e] = 0.f;
-        dp[e] = 0.f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Kt, kt * 32, ks, l),
-                                                    as_bf16x8(qb[ks]), s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Vt, kt * 32, ks, l),
-                                                     as_bf16x8(ob[ks]), dp, 0, 0, 0);
-      }
-      // S^T element e of the lane: key kt*32 + (e/4)*8 + half*4 + e%4, row lr
-      f32x16 ds;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kt * 32 + (e / 4) * 8 + half * 4 + (e % 4);
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -lse2));
-        ds[e] = (need_mask && key > rel) ? 0.f : p * (dp[e] - dsr);
-      }
-      bf16x8 dsb[2];
-      pack_b(ds, dsb);
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(Kt, kt * 32 + 16 * k2, dt, l),
-                                                            dsb[k2], acc[dt], 0, 0, 0);
-    }
+  // step x reads stage `rd` and issues block x+2 into `wr`
+#define PYR_DQ_STEP(x, rd, wr)                                                                 \
+  {                                                                                            \
+    if ((x) + 1 < nsel)                                                                        \
+      __builtin_amdgcn_s_waitcnt(WAIT_ONE); /* this wave's loads of block x are done */        \
+    else                                                                                       \
+      __builtin_amdgcn_s_waitcnt(0x0F70);                                                      \
+    lds_barrier(); /* everyone's; the stage of block x-1 is free */                            \
+    const bool more = (x) + 2 < nsel;                                                          \
+    const int64_t key2 = more ? (int64_t)s_sel[(x) + 2] * PYR_BLOCK : 0;                        \
+    dq_step<D, NW>(s_, rd, (int64_t)s_sel[x] * PYR_BLOCK, more ? (wr) : nullptr, key2, kh, vh, \
+                   g.Tk, w, l);                                                                \
   }
+  for (int x = 0; x < nsel; x += 3) {
+    PYR_DQ_STEP(x, st0, st2);
+    if (x + 1 < nsel) PYR_DQ_STEP(x + 1, st1, st0);
+    if (x + 2 < nsel) PYR_DQ_STEP(x + 2, st2, st1);
+  }
+#undef PYR_DQ_STEP
 
   // dQ = scale * acc; lane's row = lr, dims of acc[dt][e] = dt*32 + (e/4)*8 + half*4 + e%4
-  if (row0 + lr >= g.Tq) return;
+  if (s_.row0 + lr >= g.Tq) return;
   bf16_t* out = dq + qrow * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -382,7 +468,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq(
     for (int g4 = 0; g4 < 4; ++g4) {
       bf16x4_t pk;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(acc[dt][g4 * 4 + e] * g.scale);
+      for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(s_.acc[dt][g4 * 4 + e] * g.scale);
       *reinterpret_cast<bf16x4_t*>(out + dt * 32 + g4 * 8 + half * 4) = pk;
     }
 }
@@ -429,13 +515,14 @@ struct BitWalk {
 template <int D>
 struct DkdvStage {
   static constexpr int TILE = BTile<D>::TILE;
-  static constexpr int AUX = 1024;  // the visitor's record (512 bytes), loaded twice
+  static constexpr int AUX = 512;  // the visitor's row record
   static constexpr int BYTES = 2 * TILE + AUX;
+  // global->LDS loads per visitor per wave: Q and dO tiles, and one for the record
+  static constexpr int PER = 2 * (64 * BTile<D>::CPR / 256) + 1;
 };
 
 // Stage the Q and dO tiles and the row record of visitor (query block i, head
-// h).  Wave 0 copies the record: lanes l and l + 32 both load its 16-byte chunk
-// l, so the second half of the aux kilobyte repeats the first (unused).
+// h).  The record's 32 16-byte chunks come from lanes 0..7 of each wave.
 template <int D>
 __device__ __forceinline__ void load_visitor(const bf16_t* q, const bf16_t* dout, const float* rec,
                                              const PyrGeom& g, int bi, int h, int i,
@@ -445,9 +532,10 @@ __device__ __forceinline__ void load_visitor(const bf16_t* q, const bf16_t* dout
   const int64_t r0 = (int64_t)i * PYR_BLOCK;
   load_tile<D, 256>(q + bh * g.Tq * D, r0, g.Tq - 1, st, w, l);
   load_tile<D, 256>(dout + bh * g.Tq * D, r0, g.Tq - 1, st + TG::TILE, w, l);
-  if (w == 0) {
-    const float* src = rec + (bh * g.nqb + i) * kRec + (l % 32) * 4;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(st + 2 * TG::TILE), 16, 0, 0);
+  if (l < 8) {
+    const float* src = rec + (bh * g.nqb + i) * kRec + (w * 8 + l) * 4;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(st + 2 * TG::TILE + w * 128), 16,
+                                     0, 0);
   }
 }
 
@@ -462,14 +550,152 @@ struct BwdList {
   int words, chq;
 };
 
+// Per-wave state of the key-gradient kernel.
+template <int D>
+struct DkdvWave {
+  uint4 kb[D / 16], vb[D / 16];  // K, V B fragments of the wave's 32 keys
+  f32x16 dka[D / 32], dva[D / 32];  // dK^T, dV^T accumulators
+  int roff[D / 16];  // lane's row-fragment offsets in a tile (rows rh*32 + l%32)
+  int toff[D / 32];  // lane's transposed-read offsets (rows rh*32 + 4*half + (l%16)/4)
+  int kl, rh, half, l;  // kl: the lane's key within the block
+  float sl2;
+};
+
+// One visitor: the tiles in `rd`, query block i, against key block j.  First
+// issues (if `wr`) the loads of visitor n+2 into `wr`; rd and wr are distinct
+// __shared__ arrays, so the compiler knows those loads do not touch what this
+// step reads and does not wait for them.  The work runs in three phases (S and
+// dP; P and dV; dS and dK), each reading its LDS operands just before use.
+template <int D>
+__device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* rd, int i, int j,
+                                          unsigned char* wr, int i2, int h2, const bf16_t* q,
+                                          const bf16_t* dout, const float* rec, const PyrGeom& g,
+                                          int bi, int w) {
+  using TG = BTile<D>;
+  const int l = s_.l, half = s_.half, rh = s_.rh;
+  if (wr) load_visitor<D>(q, dout, rec, g, bi, h2, i2, wr, w, l);
+  __builtin_amdgcn_sched_barrier(0);
+  if (i < j) return;  // a later key block: no pair is visible
+  // opaque copies of the lane offsets: the addresses are formed per step
+  // instead of being kept live for all three stages
+  int ro[D / 16], to[D / 32];
+#pragma unroll
+  for (int x = 0; x < D / 16; ++x) {
+    ro[x] = s_.roff[x];
+    asm volatile("" : "+v"(ro[x]));
+  }
+#pragma unroll
+  for (int x = 0; x < D / 32; ++x) {
+    to[x] = s_.toff[x];
+    asm volatile("" : "+v"(to[x]));
+  }
+  const lds_u8* Qt = (const lds_u8*)rd;
+  const lds_u8* Ot = Qt + TG::TILE;
+  const lds_u8* aux = Qt + 2 * TG::TILE;
+  // phase 1: S = Q K^T and dP = dO V^T for rows rh*32 .. +31 (M) and the
+  // wave's keys (N)
+  bf16x8 fq[D / 16], fo[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    fq[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Qt + ro[ks]));
+    fo[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Ot + ro[ks]));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s, dp;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    s[e] = 0.f;
+    dp[e] = 0.f;
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[ks], as_bf16x8(s_.kb[ks]), s, 0, 0, 0);
+    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo[ks], as_bf16x8(s_.vb[ks]), dp, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // phase 2: P, then dV^T += dO^T P.  Element e of the lane: row
+  // rr(e) = rh*32 + (e/4)*8 + half*4 + e%4 of the query block, key kl.
+  auto tread = [&](const lds_u8* t, int k2, int dt) {
+    const lds_u8* p1 = t + to[dt] + k2 * 16 * TG::ROW;
+    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+    const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1 + 8 * TG::ROW));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8 tf[2][D / 32];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) tf[k2][dt] = tread(Ot, k2, dt);
+  f32x4 ls4[4];
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4)
+    ls4[g4] = *(const lds_f32x4*)(aux + (rh * 32 + g4 * 8 + half * 4) * 4);
+  __builtin_amdgcn_sched_barrier(0);
+  // every pair is visible unless this is the diagonal block or the ragged last
+  // query block
+  const int qoff = (i - j) * PYR_BLOCK;  // row position minus key position base
+  const int64_t qpos0 = (int64_t)i * PYR_BLOCK;
+  const bool full = i > j && qpos0 + PYR_BLOCK <= g.Tq;
+  const int lim = (int)min<int64_t>(g.Tq - qpos0, PYR_BLOCK);  // valid rows of the block
+  f32x16 pf;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    pf[e] = __builtin_amdgcn_exp2f(fmaf(s[e], s_.sl2, -ls4[e / 4][e % 4]));
+  if (!full) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rr = rh * 32 + (e / 4) * 8 + half * 4 + e % 4;
+      if (s_.kl > qoff + rr || rr >= lim) pf[e] = 0.f;
+    }
+  }
+  bf16x8 pb[2];
+  pack_b(pf, pb);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      s_.dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[k2][dt], pb[k2], s_.dva[dt], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // phase 3: dS = P (dP - D) (zero where P is), then dK^T += Q^T dS
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) tf[k2][dt] = tread(Qt, k2, dt);
+  f32x4 dd4[4];
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4)
+    dd4[g4] = *(const lds_f32x4*)(aux + (64 + rh * 32 + g4 * 8 + half * 4) * 4);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 dsf;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) dsf[e] = pf[e] * (dp[e] - dd4[e / 4][e % 4]);
+  bf16x8 dsb[2];
+  pack_b(dsf, dsb);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      s_.dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[k2][dt], dsb[k2], s_.dka[dt], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ rec, BwdList wl,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, PyrGeom g) {
-  using TG = BTile<D>;
   using SG = DkdvStage<D>;
-  __shared__ __align__(16) unsigned char stage[2][SG::BYTES];
+  // Three visitor stages, each its own __shared__ array, used in a fixed
+  // rotation (the loop is unrolled by three): a step reads one stage while the
+  // loads of the visitor two steps ahead fill another, and the compiler can
+  // tell the arrays apart, so it does not wait for those loads before the
+  // step's LDS reads.
+  __shared__ __align__(16) unsigned char st0[SG::BYTES];
+  __shared__ __align__(16) unsigned char st1[SG::BYTES];
+  __shared__ __align__(16) unsigned char st2[SG::BYTES];
+  __shared__ int s_ids[kMaxItemQ];  // the item's query blocks, ascending
 
   const int nsplit = wl.hdr[0], nlight = wl.hdr[1];
   const int item = blockIdx.x;
@@ -481,125 +707,126 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
   const int first = split ? it.y * wl.chq : 0;
   const int nq = split ? min(wl.chq, ncnt - first) : ncnt;  // query blocks of this item
 
-  const int tid = threadIdx.x, l = tid % 64;
+  const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int half = l / 32, lr = l % 32;
-  const int kt = w & 1, rh = w >> 1;  // key tile and row half of this wave
+  const int kt = w & 1;  // key tile of this wave; w >> 1 is its row half
   const int64_t slab = krow / g.nb;
   const int j = (int)(krow % g.nb);
   const int bi = (int)(slab / g.Hk), hk = (int)(slab % g.Hk);
-  const float sl2 = g.scale * PYR_LOG2E;
   const int64_t kbase = slab * g.Tk;
-  const int kpos = j * PYR_BLOCK + kt * 32 + lr;  // the lane's key (B fragment column)
-
-  // K and V B fragments of the wave's 32 keys: lane key kpos, d = ks*16 + 8*half .. +7
-  uint4 kb[D / 16], vb[D / 16];
+  DkdvWave<D> s_;
+  s_.l = tid % 64;
+  s_.half = s_.l / 32;
+  s_.rh = w >> 1;
+  s_.sl2 = g.scale * PYR_LOG2E;
+  s_.kl = kt * 32 + s_.l % 32;  // the lane's key in the block (B fragment column)
+  const int l = s_.l, half = s_.half;
   {
-    const int64_t kr = kbase + min<int64_t>(kpos, g.Tk - 1);
+    using TG = BTile<D>;
+    const int s16 = l % 16, g16 = l / 16;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      kb[ks] = ld16(k + kr * D + ks * 16 + 8 * half);
-      vb[ks] = ld16(v + kr * D + ks * 16 + 8 * half);
+    for (int ks = 0; ks < D / 16; ++ks) s_.roff[ks] = TG::off(s_.rh * 32 + l % 32, 2 * ks + half);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      // transposed read (see trans_frag): rows rh*32 + 4*half + s16/4 (+8, +16 k2:
+      // the swizzle repeats every 8 rows), the lane's 4 d from c
+      const int c = dt * 32 + (g16 % 2) * 16 + 4 * (s16 % 4);
+      s_.toff[dt] = TG::off(s_.rh * 32 + 4 * half + s16 / 4, c >> 3) + (c & 7) * 2;
     }
   }
-  f32x16 dka[D / 32], dva[D / 32];  // dK^T, dV^T: column key kpos, d = dt*32 + (e/4)*8 + half*4 + e%4
+  const int kposl = j * PYR_BLOCK + s_.kl;  // the lane's key position
+
+  // K and V B fragments: lane key kpos, d = ks*16 + 8*half .. +7
+  {
+    const int64_t kr = kbase + min<int64_t>(kposl, g.Tk - 1);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s_.kb[ks] = ld16(k + kr * D + ks * 16 + 8 * half);
+      s_.vb[ks] = ld16(v + kr * D + ks * 16 + 8 * half);
+    }
+  }
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      dka[dt][e] = 0.f;
-      dva[dt][e] = 0.f;
+      s_.dka[dt][e] = 0.f;
+      s_.dva[dt][e] = 0.f;
     }
 
-  BitWalk bw;
-  bw.start(wl.bits + krow * wl.words, wl.words, first);
-  int left = nq;
-  int icur = left > 0 ? bw.next() : -1;
-  int hcur = 0;
-  if (icur >= 0) load_visitor<D>(q, dout, rec, g, bi, hk * g.G, icur, stage[0], w, l);
-  int st = 0;
-  while (icur >= 0) {
-    // next visitor: the next head of this query block, else the next block
-    int inext = icur, hnext = hcur + 1;
-    if (hnext == g.G) {
-      hnext = 0;
-      inext = --left > 0 ? bw.next() : -1;
+  // list the item's query blocks: set bits first .. first + nq - 1 of the row
+  if (w == 0) {
+    BitWalk bw;
+    bw.start(wl.bits + krow * wl.words, wl.words, first);
+    for (int x = 0; x < nq; ++x) {
+      const int ib = bw.next();
+      if (l == 0) s_ids[x] = ib;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the visitor
-    __syncthreads();                     // everyone's; the other stage is free
-    if (inext >= 0)
-      load_visitor<D>(q, dout, rec, g, bi, hk * g.G + hnext, inext, stage[st ^ 1], w, l);
-    const unsigned char* Qt = stage[st];
-    const unsigned char* Ot = stage[st] + TG::TILE;
-    const float* aux = reinterpret_cast<const float*>(stage[st] + 2 * TG::TILE);
-    // S = Q K^T and dP = dO V^T for rows rh*32 .. +31 (M) and the wave's keys (N)
-    f32x16 s, dp;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s[e] = 0.f;
-      dp[e] = 0.f;
-    }
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Qt, rh * 32, ks, l), as_bf16x8(kb[ks]),
-                                                  s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(Ot, rh * 32, ks, l), as_bf16x8(vb[ks]),
-                                                   dp, 0, 0, 0);
-    }
-    // element e of the lane: row rh*32 + (e/4)*8 + half*4 + e%4 of the block, key kpos
-    const int64_t qpos0 = (int64_t)icur * PYR_BLOCK;
-    f32x16 pf, dsf;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int rr = rh * 32 + g4 * 8 + half * 4;  // first of the lane's 4 rows in this group
-      const float4 ls = *reinterpret_cast<const float4*>(aux + rr);
-      const float4 dd = *reinterpret_cast<const float4*>(aux + 64 + rr);
-      const float lv[4] = {ls.x, ls.y, ls.z, ls.w};
-      const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int e = g4 * 4 + e4;
-        const int64_t qp = qpos0 + rr + e4;  // the row's position
-        const bool vis = kpos <= qp && qp < g.Tq;
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -lv[e4]));
-        pf[e] = vis ? p : 0.f;
-        dsf[e] = vis ? p * (dp[e] - dv4[e4]) : 0.f;
-      }
-    }
-    bf16x8 pb[2], dsb[2];
-    pack_b(pf, pb);
-    pack_b(dsf, dsb);
-    // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 rows
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(Ot, rh * 32 + 16 * k2, dt, l),
-                                                          pb[k2], dva[dt], 0, 0, 0);
-        dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trans_frag<D>(Qt, rh * 32 + 16 * k2, dt, l),
-                                                          dsb[k2], dka[dt], 0, 0, 0);
-      }
-    icur = inext;
-    hcur = hnext;
-    st ^= 1;
   }
+  __syncthreads();
+
+  const int G = g.G;
+  const int hk0 = hk * G;
+  const int nvis = nq * G;  // visitors: (query block, head), heads fastest
+  // cursor of the visitor whose loads are issued next
+  int ci = 0, ch = 0;
+  auto issue_next = [&](unsigned char* dst) {
+    load_visitor<D>(q, dout, rec, g, bi, hk0 + ch, s_ids[ci], dst, w, l);
+    if (++ch == G) {
+      ch = 0;
+      ++ci;
+    }
+  };
+  if (nvis > 0) issue_next(st0);
+  if (nvis > 1) issue_next(st1);
+  int vi = 0, vh = 0;  // the visitor of the current step
+  constexpr int WAIT_ONE = 0x0F70 | (SG::PER & 15) | ((SG::PER >> 4) << 14);  // vmcnt(PER)
+  // step n reads stage `rd` and issues visitor n+2 into `wr`
+#define PYR_DKDV_STEP(n, rd, wr)                                                            \
+  {                                                                                         \
+    if ((n) + 1 < nvis)                                                                     \
+      __builtin_amdgcn_s_waitcnt(WAIT_ONE); /* this wave's loads of visitor n are done */   \
+    else                                                                                    \
+      __builtin_amdgcn_s_waitcnt(0x0F70);                                                   \
+    lds_barrier(); /* everyone's; the stage of visitor n-1 is free */                       \
+    const bool more = (n) + 2 < nvis;                                                       \
+    const int i2 = more ? s_ids[ci] : 0, h2 = hk0 + ch;                                     \
+    dkdv_step<D>(s_, rd, s_ids[vi], j, more ? (wr) : nullptr, i2, h2, q, dout, rec, g, bi, w); \
+    if (more && ++ch == G) {                                                                \
+      ch = 0;                                                                               \
+      ++ci;                                                                                 \
+    }                                                                                       \
+    if (++vh == G) {                                                                        \
+      vh = 0;                                                                               \
+      ++vi;                                                                                 \
+    }                                                                                       \
+  }
+  // (guarded steps, not breaks: an exit in mid-body makes the register
+  // allocator copy the accumulators around the loop)
+  for (int n = 0; n < nvis; n += 3) {
+    PYR_DKDV_STEP(n, st0, st2);
+    if (n + 1 < nvis) PYR_DKDV_STEP(n + 1, st1, st0);
+    if (n + 2 < nvis) PYR_DKDV_STEP(n + 2, st2, st1);
+  }
+#undef PYR_DKDV_STEP
 
   // the two row halves of a key tile add up: waves with rh = 1 hand their sums
-  // to the waves with rh = 0 through LDS (the stages are free now)
+  // to the waves with rh = 0 through LDS (key tile 0 in st0, 1 in st1)
   __syncthreads();
-  float* red = reinterpret_cast<float*>(&stage[0][0]);  // [kt][dt][k or v][e][lane]
-  static_assert(2 * (D / 32) * 2 * 16 * 64 * 4 <= 2 * SG::BYTES, "reduction must fit the stages");
-  if (rh == 1) {
+  float* red = reinterpret_cast<float*>(kt == 0 ? st0 : st1);  // [dt][k or v][e][lane]
+  static_assert((D / 32) * 2 * 16 * 64 * 4 <= SG::BYTES, "reduction must fit a stage");
+  if (s_.rh == 1) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        red[(((kt * (D / 32) + dt) * 2 + 0) * 16 + e) * 64 + l] = dka[dt][e];
-        red[(((kt * (D / 32) + dt) * 2 + 1) * 16 + e) * 64 + l] = dva[dt][e];
+        red[((dt * 2 + 0) * 16 + e) * 64 + l] = s_.dka[dt][e];
+        red[((dt * 2 + 1) * 16 + e) * 64 + l] = s_.dva[dt][e];
       }
   }
   __syncthreads();
-  if (rh == 1) return;
+  if (s_.rh == 1) return;
+  const int kpos = kposl;
+  const int lr = l % 32;
   if (split) {  // unscaled fp32 sums into the item's slot
     float* pk = wl.part + (int64_t)item * 2 * PYR_BLOCK * D + (kt * 32 + lr) * D;
     float* pv = pk + PYR_BLOCK * D;
@@ -613,8 +840,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const int e = g4 * 4 + e4;
-          av[e4] = dka[dt][e] + red[(((kt * (D / 32) + dt) * 2 + 0) * 16 + e) * 64 + l];
-          bv[e4] = dva[dt][e] + red[(((kt * (D / 32) + dt) * 2 + 1) * 16 + e) * 64 + l];
+          av[e4] = s_.dka[dt][e] + red[((dt * 2 + 0) * 16 + e) * 64 + l];
+          bv[e4] = s_.dva[dt][e] + red[((dt * 2 + 1) * 16 + e) * 64 + l];
         }
         *reinterpret_cast<float4*>(pk + dt * 32 + g4 * 8 + half * 4) = a;
         *reinterpret_cast<float4*>(pv + dt * 32 + g4 * 8 + half * 4) = b;
@@ -632,8 +859,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int e = g4 * 4 + e4;
-        const float sk = dka[dt][e] + red[(((kt * (D / 32) + dt) * 2 + 0) * 16 + e) * 64 + l];
-        const float sv = dva[dt][e] + red[(((kt * (D / 32) + dt) * 2 + 1) * 16 + e) * 64 + l];
+        const float sk = s_.dka[dt][e] + red[((dt * 2 + 0) * 16 + e) * 64 + l];
+        const float sv = s_.dva[dt][e] + red[((dt * 2 + 1) * 16 + e) * 64 + l];
         pk[e4] = (__bf16)(sk * g.scale);
         pv[e4] = (__bf16)sv;
       }
@@ -702,7 +929,7 @@ BwdPlan bwd_plan(const PyrGeom& g) {
   const int64_t entries = (int64_t)g.B * g.Hk * g.nqb * (g.K + 1);
   const int64_t budget = std::min<int64_t>(std::max<int64_t>(entries * g.G / 4096, g.G),
                                            std::max(256, g.G));
-  p.chq = (int)std::max<int64_t>(1, budget / g.G);
+  p.chq = (int)std::max<int64_t>(1, budget / g.G);  // <= 256 = kMaxItemQ
   // a split row with c > chq visitors has ceil(c / chq) < 2c / chq items
   p.slots = (2 * entries + p.chq - 1) / p.chq;
   size_t off = align256((size_t)g.B * g.Hq * g.nqb * kRec * 4);
@@ -768,8 +995,8 @@ hipError_t launch_bwd_d(const PyrGeom& g, const bf16_t* q, const bf16_t* k, cons
   wl.part = part;
   wl.words = pl.words;
   wl.chq = pl.chq;
-  hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)(pl.rows + pl.slots)), dim3(256), 0, st, q, k, v,
-                     dout, rec, wl, dk, dv, g);
+  hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)(pl.rows + pl.slots)), dim3(256), 0, st, q, k,
+                     v, dout, rec, wl, dk, dv, g);
   hipLaunchKernelGGL((bwd_dkdv_reduce<D>), dim3((unsigned)pl.rows), dim3(256), 0, st, cnt, pslot,
                      part, dk, dv, g, pl.chq);
   return hipGetLastError();
