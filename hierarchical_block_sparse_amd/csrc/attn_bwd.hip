@@ -51,18 +51,22 @@ constexpr int kMaxSelB = PYR_BWD_MAX_SLOTS;  // route-row capacity staged in LDS
 constexpr int kMaxItemQ = 256;               // query blocks per key-gradient work item
 
 // A 64-row tile of bf16 rows of length D in LDS: row-major, the 16-byte chunks
-// of row r XOR-swizzled by swz(r), an even value that differs between the rows
-// of each group of 8 consecutive rows (per bank sweep).  Being even it keeps
-// the chunk pairs (2m, 2m+1) together, so both the row-per-lane 16-byte reads
-// (8 rows per pass) and the transposed 8-byte reads (4 rows x 32 bytes per 16
-// lanes) are free of bank conflicts.
+// of row r XOR-swizzled by swz(r).  With u = r / RP the bank sweep of the row
+// and n = CPR / 4, swz = 4 (u mod n) + (u / n) mod 4 takes every value over any
+// 16 aligned rows (so a row-per-lane 16-byte read, 16 rows per pass, hits 16
+// distinct 16-byte slots), and swz / 4 differs between the 4 rows of an
+// aligned group (so a transposed 8-byte read, 4 rows x 2 chunk pairs per 32
+// lanes, hits 8 distinct 32-byte slots): both are free of bank conflicts.
 template <int D>
 struct BTile {
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int ROW = 2 * D;      // bytes per row
   static constexpr int TILE = 64 * ROW;  // bytes per tile
   static constexpr int RP = 256 / ROW;   // rows per 256-byte bank sweep
-  __device__ static int swz(int r) { return 2 * ((r / RP) % (CPR / 2)); }
+  __device__ static int swz(int r) {
+    const int u = r / RP;
+    return 4 * (u % (CPR / 4)) + (u / (CPR / 4)) % 4;
+  }
   // byte offset of logical 16-byte chunk c of row r
   __device__ static int off(int r, int c) { return r * ROW + ((c ^ swz(r)) << 4); }
 };
@@ -557,6 +561,7 @@ struct DkdvWave {
   f32x16 dka[D / 32], dva[D / 32];  // dK^T, dV^T accumulators
   int roff[D / 16];  // lane's row-fragment offsets in a tile (rows rh*32 + l%32)
   int toff[D / 32];  // lane's transposed-read offsets (rows rh*32 + 4*half + (l%16)/4)
+  int toff8[D / 32];  // the same 8 rows further down
   int kl, rh, half, l;  // kl: the lane's key within the block
   float sl2;
 };
@@ -578,7 +583,7 @@ __device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* 
   if (i < j) return;  // a later key block: no pair is visible
   // opaque copies of the lane offsets: the addresses are formed per step
   // instead of being kept live for all three stages
-  int ro[D / 16], to[D / 32];
+  int ro[D / 16], to[D / 32], to8[D / 32];
 #pragma unroll
   for (int x = 0; x < D / 16; ++x) {
     ro[x] = s_.roff[x];
@@ -587,7 +592,8 @@ __device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* 
 #pragma unroll
   for (int x = 0; x < D / 32; ++x) {
     to[x] = s_.toff[x];
-    asm volatile("" : "+v"(to[x]));
+    to8[x] = s_.toff8[x];
+    asm volatile("" : "+v"(to[x]), "+v"(to8[x]));
   }
   const lds_u8* Qt = (const lds_u8*)rd;
   const lds_u8* Ot = Qt + TG::TILE;
@@ -616,9 +622,10 @@ __device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* 
   // phase 2: P, then dV^T += dO^T P.  Element e of the lane: row
   // rr(e) = rh*32 + (e/4)*8 + half*4 + e%4 of the query block, key kl.
   auto tread = [&](const lds_u8* t, int k2, int dt) {
-    const lds_u8* p1 = t + to[dt] + k2 * 16 * TG::ROW;
-    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
-    const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1 + 8 * TG::ROW));
+    const s16x4 t1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + to[dt] + k2 * 16 * TG::ROW));
+    const s16x4 t2 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + to8[dt] + k2 * 16 * TG::ROW));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   bf16x8 tf[2][D / 32];
@@ -728,10 +735,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
     for (int ks = 0; ks < D / 16; ++ks) s_.roff[ks] = TG::off(s_.rh * 32 + l % 32, 2 * ks + half);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      // transposed read (see trans_frag): rows rh*32 + 4*half + s16/4 (+8, +16 k2:
-      // the swizzle repeats every 8 rows), the lane's 4 d from c
+      // transposed reads (see trans_frag): rows rh*32 + 4*half + s16/4 and 8
+      // rows further (+16 for k2 = 1: the swizzle repeats every 16 rows), the
+      // lane's 4 d from c
       const int c = dt * 32 + (g16 % 2) * 16 + 4 * (s16 % 4);
-      s_.toff[dt] = TG::off(s_.rh * 32 + 4 * half + s16 / 4, c >> 3) + (c & 7) * 2;
+      const int r1 = s_.rh * 32 + 4 * half + s16 / 4;
+      s_.toff[dt] = TG::off(r1, c >> 3) + (c & 7) * 2;
+      s_.toff8[dt] = TG::off(r1 + 8, c >> 3) + (c & 7) * 2;
     }
   }
   const int kposl = j * PYR_BLOCK + s_.kl;  // the lane's key position
