@@ -129,6 +129,29 @@ __device__ __forceinline__ void pack_b(const f32x16& x, bf16x8 (&b)[2]) {
     for (int e = 0; e < 8; ++e) b[k2][e] = (__bf16)x[k2 * 8 + e];
 }
 
+// Lane offsets into a tile for the reads of a wave whose rows start at a
+// multiple of 16 (the swizzle repeats every 16 rows, so row shifts by 16 are
+// plain additions):
+//  * row reads: lane row l%32, chunk 2ks + l/32 lies at  r ^ (ks << 5);
+//  * transposed reads (trans_frag's rows 4*half + (l%16)/4 and 8 further, the
+//    lane's 4 d at dt*32 + (l/16 % 2)*16 + 4*(l%4)) lie at t ^ (dt << 6) and
+//    t8 ^ (dt << 6).
+// (XOR-ing the chunk index with 2ks or 4dt commutes with the swizzle XOR, and
+// the row term has no bits in the chunk field.)
+template <int D>
+struct TileLanes {
+  int r, t, t8;
+  __device__ explicit TileLanes(int l) {
+    using TG = BTile<D>;
+    const int half = l / 32, s16 = l % 16, g16 = l / 16;
+    r = TG::off(l % 32, half);
+    const int y = (g16 % 2) * 2 + (s16 % 4) / 2;  // chunk of dt = 0
+    const int b = (s16 % 2) * 8;                  // byte within the chunk
+    t = TG::off(4 * half + s16 / 4, y) + b;
+    t8 = TG::off(4 * half + s16 / 4 + 8, y) + b;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Per-row record of the backward: for every (batch, query head, query block) a
 // 512-byte record of 64 log2-domain log-sum-exps (lse * log2 e) followed by 64
@@ -293,6 +316,7 @@ template <int D>
 struct DqWave {
   uint4 qb[D / 16], ob[D / 16];  // Q^T, dO^T B fragments of the wave's 32 rows
   f32x16 acc[D / 32];            // dQ^T
+  int r, t, t8;                  // TileLanes of the lane
   float lse2, dsr, sl2;
   int64_t row0;
 };
@@ -303,19 +327,22 @@ struct DqWave {
 template <int D, int NW>
 __device__ __forceinline__ void dq_step(DqWave<D>& s_, const unsigned char* rd, int64_t key0,
                                         unsigned char* wr, int64_t key2, const bf16_t* kh,
-                                        const bf16_t* vh, int64_t Tk, int w, int lane) {
+                                        const bf16_t* vh, int64_t Tk, int w, int l) {
   using TG = BTile<D>;
   constexpr int NT = NW * 64;
-  int l = lane;
-  asm volatile("" : "+v"(l));  // LDS addresses are formed per step (not kept per stage)
   const int half = l / 32, lr = l % 32;
   if (wr) {
     load_tile<D, NT>(kh, key2, Tk - 1, wr, w, l);
     load_tile<D, NT>(vh, key2, Tk - 1, wr + TG::TILE, w, l);
   }
   __builtin_amdgcn_sched_barrier(0);
-  const unsigned char* Kt = rd;
-  const unsigned char* Vt = rd + TG::TILE;
+  // opaque copies of the lane offsets: the addresses are formed per step
+  // instead of being kept live for all three stages
+  int ro = s_.r, to = s_.t, to8 = s_.t8;
+  asm volatile("" : "+v"(ro), "+v"(to), "+v"(to8));
+  const lds_u8* Kt = (const lds_u8*)rd;
+  const lds_u8* Vt = Kt + TG::TILE;
+  // the block reaches past the wave's first row: the diagonal block (or a later one)
   const bool need_mask = key0 + PYR_BLOCK - 1 > s_.row0;
   const int rel = (int)(s_.row0 - key0) + lr;  // row position in the block's key coordinates
 #pragma unroll
@@ -335,8 +362,9 @@ __device__ __forceinline__ void dq_step(DqWave<D>& s_, const unsigned char* rd, 
       bf16x8 fk[KS], fv[KS];
 #pragma unroll
       for (int x = 0; x < KS; ++x) {
-        fk[x] = row_frag_l<D>(Kt, kt * 32, ph * KS + x, l);
-        fv[x] = row_frag_l<D>(Vt, kt * 32, ph * KS + x, l);
+        const int o = (ro ^ ((ph * KS + x) << 5)) + kt * 32 * TG::ROW;
+        fk[x] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Kt + o));
+        fv[x] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Vt + o));
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -346,29 +374,45 @@ __device__ __forceinline__ void dq_step(DqWave<D>& s_, const unsigned char* rd, 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // K^T fragments for dQ^T (independent of dS: in flight during the VALU work)
-    bf16x8 tk[2][D / 32];
+    // K^T fragments for dQ^T (independent of dS: in flight during the VALU
+    // work); the second half is read after the first half's products
+    auto tread = [&](int k2, int dt) {
+      const int o = (kt * 32 + k2 * 16) * TG::ROW;
+      const s16x4 t1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Kt + ((to ^ (dt << 6)) + o)));
+      const s16x4 t2 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Kt + ((to8 ^ (dt << 6)) + o)));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 tk[D / 32];
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) tk[k2][dt] = trans_frag<D>(Kt, kt * 32 + 16 * k2, dt, l);
+    for (int dt = 0; dt < D / 32; ++dt) tk[dt] = tread(0, dt);
     __builtin_amdgcn_sched_barrier(0);
     // S^T element e of the lane: key kt*32 + (e/4)*8 + half*4 + e%4, row lr
     f32x16 ds;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int key = kt * 32 + (e / 4) * 8 + half * 4 + (e % 4);
       const float p = __builtin_amdgcn_exp2f(fmaf(s[e], s_.sl2, -s_.lse2));
-      ds[e] = (need_mask && key > rel) ? 0.f : p * (dp[e] - s_.dsr);
+      ds[e] = p * (dp[e] - s_.dsr);
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kt * 32 + (e / 4) * 8 + half * 4 + (e % 4);
+        if (key > rel) ds[e] = 0.f;
+      }
     }
     bf16x8 dsb[2];
     pack_b(ds, dsb);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
+    for (int dt = 0; dt < D / 32; ++dt)
+      s_.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tk[dt], dsb[0], s_.acc[dt], 0, 0, 0);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        s_.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tk[k2][dt], dsb[k2], s_.acc[dt], 0, 0, 0);
+    for (int dt = 0; dt < D / 32; ++dt) tk[dt] = tread(1, dt);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      s_.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tk[dt], dsb[1], s_.acc[dt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -405,6 +449,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq(
   DqWave<D> s_;
   s_.row0 = (int64_t)i * PYR_BLOCK + (w % 2) * 32;  // first query token of the wave
   s_.sl2 = g.scale * PYR_LOG2E;
+  {
+    const TileLanes<D> tl(l);
+    s_.r = tl.r;
+    s_.t = tl.t;
+    s_.t8 = tl.t8;
+  }
 
   // compact route row (entries outside [0, nb) are skipped); count in s_sel[kMaxSelB]
   if (tid == 0) {
@@ -559,9 +609,7 @@ template <int D>
 struct DkdvWave {
   uint4 kb[D / 16], vb[D / 16];  // K, V B fragments of the wave's 32 keys
   f32x16 dka[D / 32], dva[D / 32];  // dK^T, dV^T accumulators
-  int roff[D / 16];  // lane's row-fragment offsets in a tile (rows rh*32 + l%32)
-  int toff[D / 32];  // lane's transposed-read offsets (rows rh*32 + 4*half + (l%16)/4)
-  int toff8[D / 32];  // the same 8 rows further down
+  int r, t, t8;  // TileLanes of the lane (rows relative to rh*32)
   int kl, rh, half, l;  // kl: the lane's key within the block
   float sl2;
 };
@@ -583,18 +631,8 @@ __device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* 
   if (i < j) return;  // a later key block: no pair is visible
   // opaque copies of the lane offsets: the addresses are formed per step
   // instead of being kept live for all three stages
-  int ro[D / 16], to[D / 32], to8[D / 32];
-#pragma unroll
-  for (int x = 0; x < D / 16; ++x) {
-    ro[x] = s_.roff[x];
-    asm volatile("" : "+v"(ro[x]));
-  }
-#pragma unroll
-  for (int x = 0; x < D / 32; ++x) {
-    to[x] = s_.toff[x];
-    to8[x] = s_.toff8[x];
-    asm volatile("" : "+v"(to[x]), "+v"(to8[x]));
-  }
+  int ro = s_.r, to = s_.t, to8 = s_.t8;
+  asm volatile("" : "+v"(ro), "+v"(to), "+v"(to8));
   const lds_u8* Qt = (const lds_u8*)rd;
   const lds_u8* Ot = Qt + TG::TILE;
   const lds_u8* aux = Qt + 2 * TG::TILE;
@@ -603,8 +641,9 @@ __device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* 
   bf16x8 fq[D / 16], fo[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    fq[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Qt + ro[ks]));
-    fo[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Ot + ro[ks]));
+    const int o = (ro ^ (ks << 5)) + rh * 32 * TG::ROW;
+    fq[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Qt + o));
+    fo[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Ot + o));
   }
   __builtin_amdgcn_sched_barrier(0);
   f32x16 s, dp;
@@ -622,10 +661,9 @@ __device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* 
   // phase 2: P, then dV^T += dO^T P.  Element e of the lane: row
   // rr(e) = rh*32 + (e/4)*8 + half*4 + e%4 of the query block, key kl.
   auto tread = [&](const lds_u8* t, int k2, int dt) {
-    const s16x4 t1 =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + to[dt] + k2 * 16 * TG::ROW));
-    const s16x4 t2 =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + to8[dt] + k2 * 16 * TG::ROW));
+    const int o = (rh * 32 + k2 * 16) * TG::ROW;
+    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + ((to ^ (dt << 6)) + o)));
+    const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + ((to8 ^ (dt << 6)) + o)));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   bf16x8 tf[2][D / 32];
@@ -729,20 +767,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
   s_.kl = kt * 32 + s_.l % 32;  // the lane's key in the block (B fragment column)
   const int l = s_.l, half = s_.half;
   {
-    using TG = BTile<D>;
-    const int s16 = l % 16, g16 = l / 16;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) s_.roff[ks] = TG::off(s_.rh * 32 + l % 32, 2 * ks + half);
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      // transposed reads (see trans_frag): rows rh*32 + 4*half + s16/4 and 8
-      // rows further (+16 for k2 = 1: the swizzle repeats every 16 rows), the
-      // lane's 4 d from c
-      const int c = dt * 32 + (g16 % 2) * 16 + 4 * (s16 % 4);
-      const int r1 = s_.rh * 32 + 4 * half + s16 / 4;
-      s_.toff[dt] = TG::off(r1, c >> 3) + (c & 7) * 2;
-      s_.toff8[dt] = TG::off(r1 + 8, c >> 3) + (c & 7) * 2;
-    }
+    const TileLanes<D> tl(l);
+    s_.r = tl.r;
+    s_.t = tl.t;
+    s_.t8 = tl.t8;
   }
   const int kposl = j * PYR_BLOCK + s_.kl;  // the lane's key position
 
