@@ -614,39 +614,36 @@ struct DkdvWave {
   float sl2;
 };
 
-// One visitor: the tiles in `rd`, query block i, against key block j.  First
-// issues (if `wr`) the loads of visitor n+2 into `wr`; rd and wr are distinct
-// __shared__ arrays, so the compiler knows those loads do not touch what this
-// step reads and does not wait for them.  The work runs in three phases (S and
-// dP; P and dV; dS and dK), each reading its LDS operands just before use.
+// Row fragments of a visitor's Q and dO rows rh*32 .. +31 in the tiles at Qt.
 template <int D>
-__device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* rd, int i, int j,
-                                          unsigned char* wr, int i2, int h2, const bf16_t* q,
-                                          const bf16_t* dout, const float* rec, const PyrGeom& g,
-                                          int bi, int w) {
+__device__ __forceinline__ void dkdv_row_frags(const lds_u8* Qt, int ro, int rh,
+                                               bf16x8 (&fq)[D / 16], bf16x8 (&fo)[D / 16]) {
   using TG = BTile<D>;
-  const int l = s_.l, half = s_.half, rh = s_.rh;
-  if (wr) load_visitor<D>(q, dout, rec, g, bi, h2, i2, wr, w, l);
-  __builtin_amdgcn_sched_barrier(0);
-  if (i < j) return;  // a later key block: no pair is visible
-  // opaque copies of the lane offsets: the addresses are formed per step
-  // instead of being kept live for all three stages
-  int ro = s_.r, to = s_.t, to8 = s_.t8;
-  asm volatile("" : "+v"(ro), "+v"(to), "+v"(to8));
-  const lds_u8* Qt = (const lds_u8*)rd;
-  const lds_u8* Ot = Qt + TG::TILE;
-  const lds_u8* aux = Qt + 2 * TG::TILE;
-  // phase 1: S = Q K^T and dP = dO V^T for rows rh*32 .. +31 (M) and the
-  // wave's keys (N)
-  bf16x8 fq[D / 16], fo[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const int o = (ro ^ (ks << 5)) + rh * 32 * TG::ROW;
     fq[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Qt + o));
-    fo[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Ot + o));
+    fo[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(Qt + TG::TILE + o));
   }
-  __builtin_amdgcn_sched_barrier(0);
-  f32x16 s, dp;
+}
+
+// Transposed fragments (see trans_frag) of the tile at t: rows rh*32 + 16 k2.
+template <int D>
+__device__ __forceinline__ bf16x8 dkdv_tread(const lds_u8* t, int to, int to8, int rh, int k2,
+                                             int dt) {
+  using TG = BTile<D>;
+  const int o = (rh * 32 + k2 * 16) * TG::ROW;
+  const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + ((to ^ (dt << 6)) + o)));
+  const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + ((to8 ^ (dt << 6)) + o)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// S = Q K^T and dP = dO V^T of the first visitor (tiles in rd).
+template <int D>
+__device__ __forceinline__ void dkdv_first(const DkdvWave<D>& s_, const unsigned char* rd,
+                                          f32x16& s, f32x16& dp) {
+  bf16x8 fq[D / 16], fo[D / 16];
+  dkdv_row_frags<D>((const lds_u8*)rd, s_.r, s_.rh, fq, fo);
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     s[e] = 0.f;
@@ -657,36 +654,75 @@ __device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* 
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[ks], as_bf16x8(s_.kb[ks]), s, 0, 0, 0);
     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo[ks], as_bf16x8(s_.vb[ks]), dp, 0, 0, 0);
   }
+}
+
+// One pipelined step.  On entry s, dp hold S and dP of visitor n (tiles in
+// rd, query block i); the tiles of visitor n+1 are in rdn.  Issues (if wr) the
+// loads of visitor n+3, then computes S and dP of visitor n+1 on the matrix
+// cores while the vector units form P of visitor n, then dV (with dS formed
+// meanwhile) and dK of visitor n; leaves S, dP of visitor n+1 in s, dp.  rd,
+// rdn and wr are distinct __shared__ arrays, so the compiler does not wait for
+// the loads in flight before the step's LDS reads.  When visitor n+1 does not
+// exist rdn holds stale tiles and its results are not used.
+template <int D>
+__device__ __forceinline__ void dkdv_pipe(DkdvWave<D>& s_, f32x16& s, f32x16& dp,
+                                          const unsigned char* rd, const unsigned char* rdn,
+                                          int i, int j, unsigned char* wr, int i3, int h3,
+                                          const bf16_t* q, const bf16_t* dout, const float* rec,
+                                          const PyrGeom& g, int bi, int w) {
+  using TG = BTile<D>;
+  const int l = s_.l, half = s_.half, rh = s_.rh;
+  if (wr) load_visitor<D>(q, dout, rec, g, bi, h3, i3, wr, w, l);
   __builtin_amdgcn_sched_barrier(0);
-  // phase 2: P, then dV^T += dO^T P.  Element e of the lane: row
-  // rr(e) = rh*32 + (e/4)*8 + half*4 + e%4 of the query block, key kl.
-  auto tread = [&](const lds_u8* t, int k2, int dt) {
-    const int o = (rh * 32 + k2 * 16) * TG::ROW;
-    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + ((to ^ (dt << 6)) + o)));
-    const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + ((to8 ^ (dt << 6)) + o)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
+  // opaque copies of the lane offsets: the addresses are formed per step
+  // instead of being kept live for all four stages
+  int ro = s_.r, to = s_.t, to8 = s_.t8;
+  asm volatile("" : "+v"(ro), "+v"(to), "+v"(to8));
+  const lds_u8* Qt = (const lds_u8*)rd;
+  const lds_u8* Ot = Qt + TG::TILE;
+  const lds_u8* aux = Qt + 2 * TG::TILE;
+  const bool live = i >= j;  // a later key block has no visible pair
+  // reads: the next visitor's row fragments, this visitor's dO^T fragments and record
+  bf16x8 fq[D / 16], fo[D / 16];
+  dkdv_row_frags<D>((const lds_u8*)rdn, ro, rh, fq, fo);
   bf16x8 tf[2][D / 32];
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) tf[k2][dt] = tread(Ot, k2, dt);
-  f32x4 ls4[4];
+    for (int dt = 0; dt < D / 32; ++dt) tf[k2][dt] = dkdv_tread<D>(Ot, to, to8, rh, k2, dt);
+  f32x4 ls4[4], dd4[4];
 #pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4)
+  for (int g4 = 0; g4 < 4; ++g4) {
     ls4[g4] = *(const lds_f32x4*)(aux + (rh * 32 + g4 * 8 + half * 4) * 4);
+    dd4[g4] = *(const lds_f32x4*)(aux + (64 + rh * 32 + g4 * 8 + half * 4) * 4);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  // every pair is visible unless this is the diagonal block or the ragged last
-  // query block
-  const int qoff = (i - j) * PYR_BLOCK;  // row position minus key position base
+  // S, dP of the next visitor on the matrix cores; P of this one meanwhile.
+  // Element e of the lane: row rr(e) = rh*32 + (e/4)*8 + half*4 + e%4 of the
+  // query block, key kl.
+  constexpr int EPK = 16 / (D / 16);  // P elements per k step
+  f32x16 s2, dp2, pf;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    s2[e] = 0.f;
+    dp2[e] = 0.f;
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[ks], as_bf16x8(s_.kb[ks]), s2, 0, 0, 0);
+    dp2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo[ks], as_bf16x8(s_.vb[ks]), dp2, 0, 0, 0);
+#pragma unroll
+    for (int e = ks * EPK; e < (ks + 1) * EPK; ++e)
+      pf[e] = __builtin_amdgcn_exp2f(fmaf(s[e], s_.sl2, -ls4[e / 4][e % 4]));
+  }
+  // every pair is visible unless this is the diagonal block or the ragged
+  // last query block; a later key block sees none
   const int64_t qpos0 = (int64_t)i * PYR_BLOCK;
   const bool full = i > j && qpos0 + PYR_BLOCK <= g.Tq;
-  const int lim = (int)min<int64_t>(g.Tq - qpos0, PYR_BLOCK);  // valid rows of the block
-  f32x16 pf;
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    pf[e] = __builtin_amdgcn_exp2f(fmaf(s[e], s_.sl2, -ls4[e / 4][e % 4]));
   if (!full) {
+    const int qoff = (i - j) * PYR_BLOCK;  // row position minus key position base
+    const int64_t rows_left = g.Tq - qpos0;
+    const int lim = !live ? 0 : (rows_left < PYR_BLOCK ? (int)rows_left : PYR_BLOCK);  // valid rows
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int rr = rh * 32 + (e / 4) * 8 + half * 4 + e % 4;
@@ -696,34 +732,32 @@ __device__ __forceinline__ void dkdv_step(DkdvWave<D>& s_, const unsigned char* 
   bf16x8 pb[2];
   pack_b(pf, pb);
   __builtin_amdgcn_sched_barrier(0);
+  // dV^T += dO^T P; the Q^T fragments are read and dS formed meanwhile
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
       s_.dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[k2][dt], pb[k2], s_.dva[dt], 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // phase 3: dS = P (dP - D) (zero where P is), then dK^T += Q^T dS
+  bf16x8 tq[2][D / 32];
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) tf[k2][dt] = tread(Qt, k2, dt);
-  f32x4 dd4[4];
-#pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4)
-    dd4[g4] = *(const lds_f32x4*)(aux + (64 + rh * 32 + g4 * 8 + half * 4) * 4);
-  __builtin_amdgcn_sched_barrier(0);
+    for (int dt = 0; dt < D / 32; ++dt) tq[k2][dt] = dkdv_tread<D>(Qt, to, to8, rh, k2, dt);
   f32x16 dsf;
 #pragma unroll
   for (int e = 0; e < 16; ++e) dsf[e] = pf[e] * (dp[e] - dd4[e / 4][e % 4]);
   bf16x8 dsb[2];
   pack_b(dsf, dsb);
   __builtin_amdgcn_sched_barrier(0);
+  // dK^T += Q^T dS
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
-      s_.dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[k2][dt], dsb[k2], s_.dka[dt], 0, 0, 0);
+      s_.dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[k2][dt], dsb[k2], s_.dka[dt], 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
+  s = s2;
+  dp = dp2;
 }
 
 template <int D>
@@ -732,14 +766,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
     const bf16_t* __restrict__ dout, const float* __restrict__ rec, BwdList wl,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, PyrGeom g) {
   using SG = DkdvStage<D>;
-  // Three visitor stages, each its own __shared__ array, used in a fixed
-  // rotation (the loop is unrolled by three): a step reads one stage while the
-  // loads of the visitor two steps ahead fill another, and the compiler can
-  // tell the arrays apart, so it does not wait for those loads before the
-  // step's LDS reads.
+  // Four visitor stages, each its own __shared__ array, used in a fixed
+  // rotation (the loop is unrolled by four): step n reads the stages of
+  // visitors n and n+1 while the loads of visitors n+2 and n+3 fill the
+  // others, and the compiler can tell the arrays apart, so it does not wait for
+  // those loads before the step's LDS reads.
   __shared__ __align__(16) unsigned char st0[SG::BYTES];
   __shared__ __align__(16) unsigned char st1[SG::BYTES];
   __shared__ __align__(16) unsigned char st2[SG::BYTES];
+  __shared__ __align__(16) unsigned char st3[SG::BYTES];
   __shared__ int s_ids[kMaxItemQ];  // the item's query blocks, ascending
 
   const int nsplit = wl.hdr[0], nlight = wl.hdr[1];
@@ -816,19 +851,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
   };
   if (nvis > 0) issue_next(st0);
   if (nvis > 1) issue_next(st1);
+  if (nvis > 2) issue_next(st2);
   int vi = 0, vh = 0;  // the visitor of the current step
-  constexpr int WAIT_ONE = 0x0F70 | (SG::PER & 15) | ((SG::PER >> 4) << 14);  // vmcnt(PER)
-  // step n reads stage `rd` and issues visitor n+2 into `wr`
-#define PYR_DKDV_STEP(n, rd, wr)                                                            \
+  constexpr int PER = SG::PER;
+  f32x16 s, dp;  // S and dP of the current visitor
+  if (nvis > 0) {
+    // this wave's loads of visitor 0 are done when at most those of visitors
+    // 1 and 2 are in flight
+    if (nvis > 2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * PER) & 15) | (((2 * PER) >> 4) << 14));
+    else if (nvis > 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (PER & 15) | ((PER >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+    dkdv_first<D>(s_, st0, s, dp);
+  }
+  // step n: visitor n's tiles in rd, visitor n+1's in rdn; issues visitor n+3 into wr
+#define PYR_DKDV_STEP(n, rd, rdn, wr)                                                       \
   {                                                                                         \
-    if ((n) + 1 < nvis)                                                                     \
-      __builtin_amdgcn_s_waitcnt(WAIT_ONE); /* this wave's loads of visitor n are done */   \
+    if ((n) + 2 < nvis) /* visitor n+1 done; n+2 may be in flight */                        \
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (PER & 15) | ((PER >> 4) << 14));                 \
     else                                                                                    \
       __builtin_amdgcn_s_waitcnt(0x0F70);                                                   \
     lds_barrier(); /* everyone's; the stage of visitor n-1 is free */                       \
-    const bool more = (n) + 2 < nvis;                                                       \
-    const int i2 = more ? s_ids[ci] : 0, h2 = hk0 + ch;                                     \
-    dkdv_step<D>(s_, rd, s_ids[vi], j, more ? (wr) : nullptr, i2, h2, q, dout, rec, g, bi, w); \
+    const bool more = (n) + 3 < nvis;                                                       \
+    const int i3 = more ? s_ids[ci] : 0, h3 = hk0 + ch;                                     \
+    dkdv_pipe<D>(s_, s, dp, rd, rdn, s_ids[vi], j, more ? (wr) : nullptr, i3, h3, q, dout,  \
+                 rec, g, bi, w);                                                            \
     if (more && ++ch == G) {                                                                \
       ch = 0;                                                                               \
       ++ci;                                                                                 \
@@ -840,10 +890,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(
   }
   // (guarded steps, not breaks: an exit in mid-body makes the register
   // allocator copy the accumulators around the loop)
-  for (int n = 0; n < nvis; n += 3) {
-    PYR_DKDV_STEP(n, st0, st2);
-    if (n + 1 < nvis) PYR_DKDV_STEP(n + 1, st1, st0);
-    if (n + 2 < nvis) PYR_DKDV_STEP(n + 2, st2, st1);
+  for (int n = 0; n < nvis; n += 4) {
+    PYR_DKDV_STEP(n, st0, st1, st3);
+    if (n + 1 < nvis) PYR_DKDV_STEP(n + 1, st1, st2, st0);
+    if (n + 2 < nvis) PYR_DKDV_STEP(n + 2, st2, st3, st1);
+    if (n + 3 < nvis) PYR_DKDV_STEP(n + 3, st3, st0, st2);
   }
 #undef PYR_DKDV_STEP
 
