@@ -40,7 +40,7 @@ Readings of the pages this oracle rests on (the pages leave these open):
       in the cache; its diagonal block is (Tk-1) // block.
   R11 Attention is token-causal: a query at position t sees key positions
       s <= t of its selected blocks only (this masks the diagonal block alone).
-  R12 The backward treats the route table as fixed (a discrete choice with no
+  R14 The backward treats the route table as fixed (a discrete choice with no
       gradient): q, k and v receive the gradient of the attention over the
       selected blocks only, and the pyramid and the scores receive none.  It
       recomputes the probabilities from the forward's log-sum-exp (PHBA §A.1.4).
@@ -314,7 +314,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, bloc
 
 # ---------------------------------------------------------------------------
 # Backward of the block-sparse attention for a fixed route table (PHBA §A.1.4:
-# probabilities recomputed from the forward's log-sum-exp; reading R12)
+# probabilities recomputed from the forward's log-sum-exp; reading R14)
 # ---------------------------------------------------------------------------
 
 def attend_rows_backward(rows: np.ndarray, row_pos: np.ndarray, k_bh: np.ndarray,

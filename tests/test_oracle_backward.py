@@ -1,5 +1,5 @@
 """Pins of the oracle's attention backward (oracle/reference.py,
-attention_backward; PHBA §A.1.4, reading R12), all on the CPU:
+attention_backward; PHBA §A.1.4, reading R14), all on the CPU:
 
   * central finite differences of L = sum(d_out * o) in float64;
   * torch autograd (float64, CPU) of the dense formulation with the route and
