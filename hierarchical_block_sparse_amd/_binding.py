@@ -37,7 +37,7 @@ class PyrProblem(ctypes.Structure):
         ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
         ("block", ctypes.c_int32), ("branching", ctypes.c_int32), ("top_k", ctypes.c_int32),
-        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("kv_capacity", ctypes.c_int64),
     ]
 
 
@@ -63,6 +63,7 @@ def lib():
             ("pyr_num_query_blocks", ctypes.c_int64, [P]),
             ("pyr_attn_workspace_bytes", ctypes.c_size_t, [P]),
             ("pyr_build_pyramid", st, [P, vp, vp, vp]),
+            ("pyr_append_pyramid", st, [P, vp, ctypes.c_int64, vp, vp]),
             ("pyr_select_topk", st, [P, vp, vp, vp, vp, vp, vp]),
             ("pyr_block_sparse_attn", st, [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
             ("pyr_attn_bwd_workspace_bytes", ctypes.c_size_t, [P]),
@@ -104,11 +105,18 @@ class Problem:
     dtype: torch.dtype
     scale: float = 0.0
     block: int = 64
+    kv_capacity: int = 0  # 0: kv_len
 
     def c(self) -> PyrProblem:
         code = {torch.float32: PYR_F32, torch.bfloat16: PYR_BF16}.get(self.dtype, 99)
         return PyrProblem(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.q_len,
-                          self.kv_len, self.block, self.branching, self.top_k, code, self.scale)
+                          self.kv_len, self.block, self.branching, self.top_k, code, self.scale,
+                          self.kv_capacity)
+
+    @property
+    def kv_rows(self) -> int:
+        """Rows per head of k and v: the capacity, or kv_len."""
+        return self.kv_capacity or self.kv_len
 
     @property
     def decode(self) -> bool:
@@ -176,9 +184,16 @@ def pyr_abi_version() -> int:
 # ---- the hot path (same names as the C ABI) ----
 
 def pyr_build_pyramid(p: Problem, k, pyramid, stream=None):
-    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_len, p.head_dim), p.dtype)
+    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_rows, p.head_dim), p.dtype)
     _expect(pyramid, "pyramid", pyramid_shape(p), torch.float32)
     _check(lib().pyr_build_pyramid(ctypes.byref(p.c()), _ptr(k), _ptr(pyramid), _stream(stream)))
+
+
+def pyr_append_pyramid(p: Problem, k, old_len: int, pyramid, stream=None):
+    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_rows, p.head_dim), p.dtype)
+    _expect(pyramid, "pyramid", pyramid_shape(p), torch.float32)
+    _check(lib().pyr_append_pyramid(ctypes.byref(p.c()), _ptr(k), int(old_len), _ptr(pyramid),
+                                    _stream(stream)))
 
 
 def pyr_select_topk(p: Problem, q, pyramid, sel, trace_ids=None, trace_scores=None, stream=None):
@@ -196,8 +211,8 @@ def pyr_select_topk(p: Problem, q, pyramid, sel, trace_ids=None, trace_scores=No
 def pyr_block_sparse_attn(p: Problem, q, k, v, sel, o, lse=None, workspace=None, stream=None):
     nqb = pyr_num_query_blocks(p)
     _expect(q, "q", (p.batch, p.n_q_heads, p.q_len, p.head_dim), p.dtype)
-    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_len, p.head_dim), p.dtype)
-    _expect(v, "v", (p.batch, p.n_kv_heads, p.kv_len, p.head_dim), p.dtype)
+    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_rows, p.head_dim), p.dtype)
+    _expect(v, "v", (p.batch, p.n_kv_heads, p.kv_rows, p.head_dim), p.dtype)
     _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
     _expect(o, "o", (p.batch, p.n_q_heads, p.q_len, p.head_dim), p.dtype)
     _expect(lse, "lse", (p.batch, p.n_q_heads, p.q_len), torch.float32)

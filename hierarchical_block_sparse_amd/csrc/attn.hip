@@ -128,8 +128,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
   const int rsub = (w % WPH) * 32;
   const float sl2 = g.scale * PYR_LOG2E;
   const int64_t row0 = (int64_t)i * PYR_BLOCK + rsub;  // first query token of this wave
-  const bf16_t* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
-  const bf16_t* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
+  const bf16_t* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
+  const bf16_t* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
 
   for (int jj = tid; jj <= g.K; jj += NT) s_sel[jj] = sel[unit * (g.K + 1) + jj];
 
@@ -663,8 +663,8 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
   __syncthreads();
   const int nsel = s_n, nun = s_nun;
   IlvRun run;
-  run.kh = k + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
-  run.vh = v + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
+  run.kh = k + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
+  run.vh = v + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
   run.ord = s_ord;
   run.ktiles = &ktiles[0][0];
   run.vtiles = &vtiles[0][0];
@@ -793,8 +793,8 @@ __global__ __launch_bounds__(64) void attn_prefill_valu(const T* __restrict__ q,
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
   float m = -INFINITY, lsum = 0.f;
-  const T* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
-  const T* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
+  const T* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
+  const T* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
   __syncthreads();
   for (int jj = 0; jj <= g.K; ++jj) {
     const int j = s_sel[jj];
@@ -903,8 +903,8 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_split(
   const int32_t* srow = sel + bhk * (g.K + 1);
   const int jb0 = split * kDecBlocksPerSplit;
   const int jb1 = min(g.K + 1, jb0 + kDecBlocksPerSplit);
-  const T* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
-  const T* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tk * D;
+  const T* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
+  const T* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
 
   float m_r[4], l_r[4], acc[4][DPL];
 #pragma unroll

@@ -68,6 +68,10 @@ pyr_status resolve(const pyr_problem* p, PyrGeom* g) {
     return fail(PYR_ERR_INVALID, "dtype %d", p->dtype);
   if (p->kv_len < 0 || p->q_len < 0) return fail(PYR_ERR_INVALID, "negative length");
   if (p->kv_len > ((int64_t)1 << 36)) return fail(PYR_ERR_UNSUPPORTED, "kv_len > 2^36");
+  if (p->kv_capacity != 0 && p->kv_capacity < p->kv_len)
+    return fail(PYR_ERR_INVALID, "kv_capacity %lld < kv_len %lld", (long long)p->kv_capacity,
+                (long long)p->kv_len);
+  if (p->kv_capacity > ((int64_t)1 << 36)) return fail(PYR_ERR_UNSUPPORTED, "kv_capacity > 2^36");
   const bool prefill = p->q_len == p->kv_len;
   const bool decode = p->q_len == 1 && p->kv_len > 1;
   if (!prefill && !decode)
@@ -90,9 +94,17 @@ pyr_status resolve(const pyr_problem* p, PyrGeom* g) {
   g->K = p->top_k;
   g->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
   g->planes = p->dtype == PYR_BF16 ? 2 : 1;
-  const int L = level_sizes(g->nb, p->branching, g->lsize, g->loff, &g->n_tot);
+  // layout (level count, offsets, node count) from the capacity; valid nodes
+  // per level from kv_len (one node, the mean of everything, above its root)
+  g->Tks = p->kv_capacity ? p->kv_capacity : p->kv_len;
+  const int64_t nb_cap = (g->Tks + PYR_BLOCK - 1) / PYR_BLOCK;
+  const int L = level_sizes(nb_cap, p->branching, nullptr, g->loff, &g->n_tot);
   if (L < 0) return fail(PYR_ERR_UNSUPPORTED, "more than %d pyramid levels", PYR_MAX_LEVELS);
   g->L = L;
+  for (int64_t l = 0, n = g->nb; l < L; ++l) {
+    g->lsize[l] = (int32_t)n;
+    n = n > 1 ? (n + p->branching - 1) / p->branching : n;
+  }
   if (g->G > 128)
     return fail(PYR_ERR_UNSUPPORTED, "at most 128 query heads per KV head (G=%d)", g->G);
   if (decode && g->G > 16)
@@ -197,6 +209,23 @@ pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void
                     "pyr_block_sparse_attn launch");
 }
 
+pyr_status pyr_append_pyramid(const pyr_problem* p, const void* k, int64_t old_len,
+                              float* pyramid, hipStream_t stream) {
+  g_err[0] = 0;
+  PyrGeom g;
+  pyr_status s = resolve(p, &g);
+  if (s != PYR_OK) return s;
+  if (old_len <= 0 || old_len > g.Tk)
+    return fail(PYR_ERR_INVALID, "old_len %lld outside (0, kv_len = %lld]", (long long)old_len,
+                (long long)g.Tk);
+  if ((int64_t)g.B * g.Hk == 0 || old_len == g.Tk) return PYR_OK;
+  if (!k || !pyramid) return fail(PYR_ERR_NULL, "k or pyramid is NULL");
+  if (!aligned16(k) || !aligned16(pyramid))
+    return fail(PYR_ERR_MISALIGNED, "tensors must be 16-byte aligned");
+  return hip_status(pyr_launch_append(g, p->dtype, k, old_len, pyramid, stream),
+                    "pyr_append_pyramid launch");
+}
+
 size_t pyr_attn_bwd_workspace_bytes(const pyr_problem* p) {
   PyrGeom g;
   return resolve(p, &g) == PYR_OK ? pyr_attn_bwd_ws_bytes(g) : 0;
@@ -214,6 +243,8 @@ pyr_status pyr_block_sparse_attn_bwd(const pyr_problem* p, const void* q, const 
   if (g.decode) return fail(PYR_ERR_UNSUPPORTED, "the backward is implemented for prefill only");
   if (p->dtype != PYR_BF16)
     return fail(PYR_ERR_UNSUPPORTED, "the backward is implemented for bfloat16 only");
+  if (g.Tks != g.Tk)
+    return fail(PYR_ERR_UNSUPPORTED, "the backward takes k and v without spare capacity");
   if (g.K + 1 > PYR_BWD_MAX_SLOTS)
     return fail(PYR_ERR_UNSUPPORTED, "route rows of %d slots (at most %d)", g.K + 1,
                 PYR_BWD_MAX_SLOTS);

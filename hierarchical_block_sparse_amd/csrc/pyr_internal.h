@@ -11,6 +11,7 @@
 // Problem geometry resolved once on the host and passed by value to kernels.
 struct PyrGeom {
   int64_t Tq, Tk;          // query / key lengths
+  int64_t Tks;             // rows per head in k and v: the capacity (or Tk)
   int64_t n_tot;           // pyramid nodes per (batch, KV head) slab
   int32_t planes;          // pyramid planes: 1 (fp32 problems) or 2 (bf16: + hi/lo split)
   int32_t B, Hq, Hk, G, D; // batch, heads, group size Hq/Hk, head dim
@@ -20,8 +21,8 @@ struct PyrGeom {
   int32_t branching, K;    // children per node, nodes kept per level
   int32_t decode;          // 1: one query token at position Tk-1
   float scale;             // scoring / softmax scale
-  int32_t lsize[PYR_MAX_LEVELS];  // nodes per level, finest first
-  int64_t loff[PYR_MAX_LEVELS];   // node offset of each level inside a slab
+  int32_t lsize[PYR_MAX_LEVELS];  // valid nodes per level (from Tk), finest first
+  int64_t loff[PYR_MAX_LEVELS];   // node offset of each level inside a slab (from the capacity)
 };
 
 // Token count covered by node m of level `level` (blocks [m b^l, (m+1) b^l)).
@@ -36,6 +37,8 @@ __host__ __device__ inline int64_t pyr_node_tokens(const PyrGeom& g, int level, 
 // Launchers (each returns the hipError_t of its launches).
 hipError_t pyr_launch_build(const PyrGeom& g, int dtype, const void* k, float* pyr,
                             hipStream_t st);
+hipError_t pyr_launch_append(const PyrGeom& g, int dtype, const void* k, int64_t old_len,
+                             float* pyr, hipStream_t st);
 hipError_t pyr_launch_select(const PyrGeom& g, int dtype, const void* q, const float* pyr,
                              int32_t* sel, int32_t* trace_ids, float* trace_scores,
                              hipStream_t st);

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
   const int c = blockIdx.x % chunks_per_bh;
   const int64_t blk0 = (int64_t)c * chunk;
   const int nblk = (int)min<int64_t>(chunk, g.nb - blk0);
-  const T* kb = k + bh * g.Tk * D;
+  const T* kb = k + bh * g.Tks * D;
   float* slab = pyr + bh * g.planes * g.n_tot * D;
 
   const int col = (tid % TPR) * VEC;
@@ -173,6 +173,77 @@ __global__ __launch_bounds__(kThreads) void build_top(float* __restrict__ pyr, P
   }
 }
 
+__device__ __forceinline__ float key_f32(float x) { return x; }
+__device__ __forceinline__ float key_f32(bf16_t x) { return bf16_to_f32(x); }
+
+// Decode-time maintenance: one workgroup per (batch, KV head) recomputes every
+// node over the tokens [old_len, Tk): the level-0 nodes of the affected blocks
+// as the mean of their valid key rows, then, level by level, the affected
+// ancestors as token-weighted means of their children (the children are up to
+// date by then).  Nodes outside those ranges are not touched.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void append_nodes(const T* __restrict__ k,
+                                                         float* __restrict__ pyr, PyrGeom g,
+                                                         int64_t old_len) {
+  constexpr int NG = kThreads / D;  // row groups of the level-0 reduction
+  __shared__ float part[NG][D];
+  const int64_t bh = blockIdx.x;
+  const T* kb = k + bh * g.Tks * D;
+  float* slab = pyr + bh * g.planes * g.n_tot * D;
+  const int tid = threadIdx.x, dcol = tid % D, rg = tid / D;
+  int64_t a0 = old_len / PYR_BLOCK, a1 = (g.Tk - 1) / PYR_BLOCK;  // affected blocks
+  for (int64_t j = a0; j <= a1; ++j) {
+    const int64_t t0 = j * PYR_BLOCK;
+    const int64_t t1 = t0 + PYR_BLOCK < g.Tk ? t0 + PYR_BLOCK : g.Tk;
+    float s = 0.f;
+    for (int64_t t = t0 + rg; t < t1; t += NG) s += key_f32(kb[t * D + dcol]);
+    part[rg][dcol] = s;
+    __syncthreads();
+    if (rg == 0) {
+      float tot = 0.f;
+#pragma unroll
+      for (int r = 0; r < NG; ++r) tot += part[r][dcol];
+      put_node<D>(g, slab, g.loff[0] + j, dcol, tot / (float)(t1 - t0));
+    }
+    __syncthreads();
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int b = g.branching;
+  for (int lvl = 1; lvl < g.L; ++lvl) {
+    a0 /= b;
+    a1 /= b;
+    const int64_t n_below = g.lsize[lvl - 1];
+    const float* below = slab + g.loff[lvl - 1] * D;
+    for (int64_t idx = tid; idx < (a1 - a0 + 1) * D; idx += kThreads) {
+      const int64_t m = a0 + idx / D;
+      const int c = (int)(idx % D);
+      float num = 0.f, den = 0.f;
+      for (int jj = 0; jj < b; ++jj) {
+        const int64_t cidx = m * b + jj;
+        if (cidx < n_below) {
+          const float w = (float)pyr_node_tokens(g, lvl - 1, cidx);
+          num += below[cidx * D + c] * w;
+          den += w;
+        }
+      }
+      put_node<D>(g, slab, g.loff[lvl] + m, c, num / den);
+    }
+    __threadfence_block();
+    __syncthreads();
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_append_t(const PyrGeom& g, const void* k, int64_t old_len, float* pyr,
+                           hipStream_t st) {
+  const int64_t n_bh = (int64_t)g.B * g.Hk;
+  if (n_bh == 0 || old_len >= g.Tk) return hipSuccess;
+  hipLaunchKernelGGL((append_nodes<T, D>), dim3((unsigned)n_bh), dim3(kThreads), 0, st,
+                     static_cast<const T*>(k), pyr, g, old_len);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_build_t(const PyrGeom& g, const void* k, float* pyr, hipStream_t st) {
   const int64_t n_bh = (int64_t)g.B * g.Hk;
@@ -208,4 +279,14 @@ hipError_t pyr_launch_build(const PyrGeom& g, int dtype, const void* k, float* p
   }
   return g.D == 64 ? launch_build_t<float, 64>(g, k, pyr, st)
                    : launch_build_t<float, 128>(g, k, pyr, st);
+}
+
+hipError_t pyr_launch_append(const PyrGeom& g, int dtype, const void* k, int64_t old_len,
+                             float* pyr, hipStream_t st) {
+  if (dtype == 1) {
+    return g.D == 64 ? launch_append_t<bf16_t, 64>(g, k, old_len, pyr, st)
+                     : launch_append_t<bf16_t, 128>(g, k, old_len, pyr, st);
+  }
+  return g.D == 64 ? launch_append_t<float, 64>(g, k, old_len, pyr, st)
+                   : launch_append_t<float, 128>(g, k, old_len, pyr, st);
 }

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define PYR_ABI_VERSION 1
+#define PYR_ABI_VERSION 2
 
 typedef enum pyr_status {
   PYR_OK = 0,
@@ -82,17 +82,24 @@ typedef struct pyr_problem {
                           added on top, so a route row has K+1 slots          */
   int32_t dtype;       /* pyr_dtype of q, k, v and o                          */
   float scale;         /* softmax and scoring scale; 0 => 1/sqrt(head_dim)    */
+  int64_t kv_capacity; /* tokens the pyramid layout is sized for: 0 => kv_len,
+                          else >= kv_len.  Level count, level offsets and node
+                          count follow the capacity, the valid nodes of each
+                          level follow kv_len, so a pyramid can grow by
+                          pyr_append_pyramid without moving (decode)          */
 } pyr_problem;
 
 /* ---- geometry helpers (host-only, no device work; -1 on invalid input) ---- */
 
 /* Number of pyramid levels L, finest (64-token blocks) to the single root:
- * n_0 = ceil(kv_len/64), n_{l+1} = ceil(n_l / b) until n = 1. */
+ * n_0 = ceil(C/64), n_{l+1} = ceil(n_l / b) until n = 1, with C the capacity
+ * (kv_capacity, or kv_len when that is 0).  Levels above the root of the valid
+ * keys hold one node: the mean of all of them. */
 int32_t pyr_num_levels(const pyr_problem* p);
 /* Node offset of a level inside one (batch, KV head) pyramid slab (finest
  * level first; levels are concatenated). */
 int64_t pyr_level_offset(const pyr_problem* p, int32_t level);
-/* Nodes per (batch, KV head) slab: sum of all level sizes. */
+/* Nodes per (batch, KV head) slab: sum of all level sizes at the capacity. */
 int64_t pyr_pyramid_nodes(const pyr_problem* p);
 /* Planes of a pyramid slab: 1 for float32 problems, 2 for bfloat16 problems
  * (plane 1 repeats plane 0 split into bfloat16 pairs, see pyr_build_pyramid). */
@@ -158,6 +165,27 @@ pyr_status pyr_select_topk(const pyr_problem* p, const void* q, const float* pyr
 pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void* k,
                                  const void* v, const int32_t* sel, void* o, float* lse,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- decode: pyramid maintenance ---- */
+
+/* Bring a pyramid up to date after keys were appended (PISA abstract: a node's
+ * pooled key is the mean of the keys under it, so appending keys changes only
+ * the nodes over the new tokens).  p describes the state after the append
+ * (kv_len = new length); the pyramid was built or last appended for old_len
+ * tokens with the same capacity, and k now holds tokens [0, kv_len) of every
+ * (batch, KV head).  Every node whose token range meets [old_len, kv_len) is
+ * recomputed — level-0 nodes as the mean of their valid keys, higher nodes as
+ * the token-weighted mean of their children — and every other node is left as
+ * it is, so the result equals pyr_build_pyramid for kv_len tokens (up to fp32
+ * rounding order).  Requires 0 < old_len <= kv_len <= capacity (else
+ * PYR_ERR_INVALID); old_len == kv_len is a no-op.  Work grows with the number
+ * of new blocks: meant for decode steps and short chunks (a long prefill is
+ * cheaper through pyr_build_pyramid).
+ *   k        [B, Hk, kv_len, d] in p->dtype (rows of the capacity beyond kv_len
+ *            may follow; only [0, kv_len) is read)                    (input)
+ *   pyramid  the layout of pyr_build_pyramid for p             (input/output) */
+pyr_status pyr_append_pyramid(const pyr_problem* p, const void* k, int64_t old_len,
+                              float* pyramid, hipStream_t stream);
 
 /* ---- training: backward of the attention for a fixed route table ---- */
 

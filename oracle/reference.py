@@ -44,6 +44,12 @@ Readings of the pages this oracle rests on (the pages leave these open):
       gradient): q, k and v receive the gradient of the attention over the
       selected blocks only, and the pyramid and the scores receive none.  It
       recomputes the probabilities from the forward's log-sum-exp (PHBA §A.1.4).
+  R15 Decode-time maintenance: after keys are appended, every node whose
+      token range gains tokens holds the mean of all its tokens again (the
+      pyramid equals a fresh build of the longer sequence); nodes that gain
+      none are unchanged.  A pyramid laid out for a capacity C has the levels
+      of ceil(C / block) blocks; levels above the root of the valid keys hold
+      one node, the mean of all of them.
 """
 
 from __future__ import annotations
@@ -110,6 +116,42 @@ def build_pyramid(k: np.ndarray, block: int, branching: int) -> list[np.ndarray]
             out[:, :, m, :] = k[:, :, t0:t1, :].mean(axis=2)
         levels.append(out)
     return levels
+
+
+def append_pyramid(levels: list[np.ndarray], k: np.ndarray, old_len: int, block: int,
+                   branching: int) -> list[np.ndarray]:
+    """Pyramid of k[:, :, :new_len] from the pyramid `levels` of its first
+    old_len tokens (new_len = k.shape[2]), by running sums (decode-time
+    maintenance; reading R15): a node over tokens [t0, t1) had
+    c_old = |[t0, t1) cut [0, old_len)| tokens; its new mean is
+    (mean_old * c_old + sum of k over [max(t0, old_len), min(t1, new_len)))
+    / c_new.  Nodes that gain no token keep their old value; new nodes (and
+    new levels) start from c_old = 0.  Only the new tokens are read.
+    """
+    k = np.asarray(k, dtype=np.float64)
+    B, Hk, new_len, d = k.shape
+    if not 0 < old_len <= new_len:
+        raise ValueError("need 0 < old_len <= new_len")
+    nb_old, nb = num_blocks(old_len, block), num_blocks(new_len, block)
+    sizes_old, sizes = level_sizes(nb_old, branching), level_sizes(nb, branching)
+    out = []
+    for lvl, n in enumerate(sizes):
+        lv = np.zeros((B, Hk, n, d), dtype=np.float64)
+        if lvl < len(sizes_old):
+            lv[:, :, :sizes_old[lvl], :] = levels[lvl]
+        elif sizes_old:
+            lv[:, :, 0, :] = levels[-1][:, :, 0, :]  # the old root covers every old token
+        for m in range(n):
+            lo, hi = node_block_range(lvl, m, nb, branching)
+            t0, t1 = lo * block, min(hi * block, new_len)
+            c_old = max(0, min(t1, old_len) - t0)
+            a = max(t0, old_len)
+            if a >= t1:
+                continue  # no new token under this node
+            add_sum = k[:, :, a:t1, :].sum(axis=2)
+            lv[:, :, m, :] = (lv[:, :, m, :] * c_old + add_sum) / (t1 - t0)
+        out.append(lv)
+    return out
 
 
 def concat_levels(levels: list[np.ndarray]) -> np.ndarray:

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     assert {"pyr_build_pyramid", "pyr_select_topk", "pyr_block_sparse_attn"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert H.pyr_abi_version() == 1
+    assert H.pyr_abi_version() == 2
 
 
 def test_single_hip_runtime_in_process():
@@ -212,3 +212,37 @@ def test_backward_binding_rejects_wrong_shapes_on_host(monkeypatch):
         H.pyr_block_sparse_attn_bwd(p, q, k, k, sel, q, lse.double(), q, q, k, k, None)
     with pytest.raises(ValueError, match="sel: shape"):
         H.pyr_block_sparse_attn_bwd(p, q, k, k, sel[..., :4], q, lse, q, q, k, k, None)
+
+
+def test_capacity_geometry():
+    """With kv_capacity the layout (levels, offsets, nodes) follows the capacity."""
+    p = _p(q_len=1, kv_len=64 * 5 + 3, kv_capacity=64 * 40)
+    cap = reference.level_sizes(40, 4)                     # 40/10/3/1
+    assert H.pyr_num_levels(p) == len(cap)
+    assert H.pyr_pyramid_nodes(p) == sum(cap)
+    assert [H.pyr_level_offset(p, l) for l in range(len(cap))] == [sum(cap[:l]) for l in range(len(cap))]
+    assert H.pyramid_shape(p)[3] == sum(cap)
+    s, msg = _status("pyr_build_pyramid", ctypes.byref(_p(kv_capacity=100).c()), ctypes.c_void_p(16),
+                     ctypes.c_void_p(16), None)
+    assert s == 2 and "kv_capacity" in msg
+
+
+def test_append_validation():
+    ptr = ctypes.c_void_p(16)
+    p = _p(q_len=1, kv_len=1000, kv_capacity=4096)
+    c = ctypes.byref(p.c())
+    for old in (0, -1, 1001):
+        s, msg = _status("pyr_append_pyramid", c, ptr, old, ptr, None)
+        assert s == 2 and "old_len" in msg
+    assert _status("pyr_append_pyramid", c, None, 1000, None, None)[0] == 0   # nothing to do
+    s, _ = _status("pyr_append_pyramid", c, None, 999, ptr, None)
+    assert s == 1
+    s, _ = _status("pyr_append_pyramid", c, ptr, 999, ctypes.c_void_p(20), None)
+    assert s == 4
+
+
+def test_backward_rejects_capacity():
+    ptr = ctypes.c_void_p(16)
+    p = _p(kv_capacity=8192)
+    s, msg = _bwd(p, [ptr] * 10, ptr, 1 << 40)
+    assert s == 3 and "capacity" in msg
