@@ -12,6 +12,11 @@ Prints one JSON line.  `value` is tokens/s of the whole path; `roofline`
 describes the dominant kernel (the attention); `cpu_baseline` is the float64
 CPU oracle timed on this host over a bounded sample of the same workload.
 
+With --packed (prefill workloads) the workload's tokens are cut into a packed
+batch of mixed-length sequences (log-uniform lengths in [1K, 32K] tokens), each
+attending within itself through the packed-sequence form of the same entry
+points; `value` is tokens/s over all of them.
+
 With --backward (prefill workloads) a step is the training pass of the path:
 build -> select -> attention -> pyr_block_sparse_attn_bwd for a seeded dL/do,
 `value` is tokens/s of that pass and `roofline` describes the backward call
@@ -35,6 +40,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "select+sparse-attn tokens/s at T=128K; TFLOP/s & HBM GB/s as % of peak"
 METRIC_BWD = "training pass (select+sparse-attn forward + attention backward) tokens/s"
+METRIC_PACKED = "select+sparse-attn tokens/s over a packed batch of mixed-length sequences"
+PACKED_SHORTEST, PACKED_LONGEST = 1024, 32768
 
 
 def parse():
@@ -46,6 +53,8 @@ def parse():
                     choices=["gqa_128k", "mha_32k", "prefill_1m", "decode_256k", "tiny_fp32"])
     ap.add_argument("--cpu-baseline-units", type=int, default=2048,
                     help="units of the workload the oracle runs for the CPU baseline (0: skip)")
+    ap.add_argument("--packed", action="store_true",
+                    help="cut the workload's tokens into a packed batch of mixed-length sequences")
     ap.add_argument("--backward", action="store_true",
                     help="time the training pass (forward + backward of the attention)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -248,16 +257,28 @@ def main():
     if args.backward and (cfg.decode or cfg.dtype != torch.bfloat16):
         print(json.dumps({"error": "the backward runs on bfloat16 prefill workloads"}), flush=True)
         sys.exit(2)
+    if args.packed and (cfg.decode or args.backward or cfg.batch != 1):
+        print(json.dumps({"error": "--packed takes a batch-1 prefill workload, forward only"}),
+              flush=True)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"# generating {cfg.name} inputs", file=sys.stderr, flush=True)
-    q, k, v = W.make_inputs(cfg, dev)
-    p = H.Problem(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.q_len, cfg.kv_len,
-                  cfg.branching, cfg.top_k, cfg.dtype)
+    lengths = None
+    if args.packed:
+        lengths = W.packed_lengths(cfg.q_len, PACKED_SHORTEST, PACKED_LONGEST, cfg.seed)
+        q, k, v, cu = W.make_packed_inputs(cfg, lengths, dev)
+        p = H.problem_for_packed(q, k, cu, max(lengths), cfg.branching, cfg.top_k)
+    else:
+        q, k, v = W.make_inputs(cfg, dev)
+        p = H.Problem(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.q_len,
+                      cfg.kv_len, cfg.branching, cfg.top_k, cfg.dtype)
+    # per-sequence views of the workload for the work accounting
+    parts = [cfg.with_(q_len=n, kv_len=n) for n in lengths] if lengths else [cfg]
     pyr = H.alloc_pyramid(p, dev)
     sel = H.alloc_sel(p, dev)
     o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    lse = torch.empty(p.lse_shape, dtype=torch.float32, device=dev)
     ws = H.alloc_workspace(p, dev)
     stream = torch.cuda.current_stream()
     if cfg.decode:
@@ -313,13 +334,19 @@ def main():
     tokens = cfg.batch * (1 if cfg.decode else cfg.q_len)
     value = tokens / (ms_per_step / 1e3)
 
-    a_flops, a_bytes = attn_work(cfg)
-    n_tot = H.pyr_pyramid_nodes(p)
-    b_bytes = build_bytes(cfg, n_tot, H.pyr_pyramid_planes(p))
-    s_flops, s_bytes = select_work(cfg, scored_candidates(cfg))
+    a_flops = sum(attn_work(c)[0] for c in parts)
+    a_bytes = sum(attn_work(c)[1] for c in parts)
+    if lengths:
+        from oracle.reference import level_sizes  # geometry only
+        b_bytes = sum(build_bytes(c, sum(level_sizes(-(-c.kv_len // 64), c.branching)),
+                                  H.pyr_pyramid_planes(p)) for c in parts)
+    else:
+        b_bytes = build_bytes(cfg, H.pyr_pyramid_nodes(p), H.pyr_pyramid_planes(p))
+    s_flops = sum(select_work(c, scored_candidates(c))[0] for c in parts)
+    s_bytes = sum(select_work(c, scored_candidates(c))[1] for c in parts)
     t_build, t_sel, t_attn = (x / 1e3 for x in stage_ms[:3])
     achieved = a_flops / t_attn / 1e12
-    traffic = kernel_traffic(cfg.name)
+    traffic = kernel_traffic(cfg.name + ("_packed" if lengths else ""))
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -365,6 +392,13 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if lengths:
+        line["metric"] = METRIC_PACKED
+        line["config"].update({
+            "workload": cfg.name + "_packed", "sequences": len(lengths),
+            "q_len": max(lengths), "kv_len": max(lengths), "total_tokens": sum(lengths),
+            "lengths": f"log-uniform in [{PACKED_SHORTEST}, {PACKED_LONGEST}], last cut to fit",
+        })
     if args.backward:
         t_bwd = stage_ms[3] / 1e3
         b_flops = 5 * a_flops // 2
@@ -387,7 +421,15 @@ def main():
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         # the backward costs the oracle about 2.5x the forward: a third of the units
         n_units = max(4, args.cpu_baseline_units // 3) if args.backward else args.cpu_baseline_units
-        line["cpu_baseline"] = cpu_baseline(cfg, q, k, v, n_units, backward=args.backward)
+        if lengths:
+            # the oracle on the longest sequence alone, at that sequence's tokens/s
+            i = max(range(len(lengths)), key=lambda j: lengths[j])
+            a0 = sum(lengths[:i])
+            views = [x[:, a0:a0 + lengths[i]].unsqueeze(0) for x in (q, k, v)]
+            line["cpu_baseline"] = cpu_baseline(parts[i], *views, n_units)
+            line["cpu_baseline"]["sample"] += f" (longest sequence, {lengths[i]} tokens)"
+        else:
+            line["cpu_baseline"] = cpu_baseline(cfg, q, k, v, n_units, backward=args.backward)
     print(json.dumps(line), flush=True)
 
 

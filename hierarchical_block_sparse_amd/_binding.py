@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import torch
 
@@ -38,6 +38,7 @@ class PyrProblem(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
         ("block", ctypes.c_int32), ("branching", ctypes.c_int32), ("top_k", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("kv_capacity", ctypes.c_int64),
+        ("cu", ctypes.c_void_p), ("total_len", ctypes.c_int64),
     ]
 
 
@@ -106,17 +107,43 @@ class Problem:
     scale: float = 0.0
     block: int = 64
     kv_capacity: int = 0  # 0: kv_len
+    # packed sequences: int32 device tensor of batch+1 row offsets (None: dense)
+    cu: torch.Tensor | None = field(default=None, compare=False, repr=False)
+    total_len: int = 0    # packed: rows per head of q, k, v, o and lse
 
     def c(self) -> PyrProblem:
         code = {torch.float32: PYR_F32, torch.bfloat16: PYR_BF16}.get(self.dtype, 99)
         return PyrProblem(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.q_len,
                           self.kv_len, self.block, self.branching, self.top_k, code, self.scale,
-                          self.kv_capacity)
+                          self.kv_capacity, None if self.cu is None else self.cu.data_ptr(),
+                          self.total_len)
+
+    @property
+    def packed(self) -> bool:
+        return self.cu is not None
 
     @property
     def kv_rows(self) -> int:
-        """Rows per head of k and v: the capacity, or kv_len."""
+        """Rows per head of k and v: the capacity, or kv_len (dense problems)."""
         return self.kv_capacity or self.kv_len
+
+    @property
+    def q_shape(self):
+        """Shape of q and o: [B, Hq, q_len, d], packed [Hq, total_len, d]."""
+        if self.packed:
+            return (self.n_q_heads, self.total_len, self.head_dim)
+        return (self.batch, self.n_q_heads, self.q_len, self.head_dim)
+
+    @property
+    def kv_shape(self):
+        """Shape of k and v: [B, Hk, kv_rows, d], packed [Hk, total_len, d]."""
+        if self.packed:
+            return (self.n_kv_heads, self.total_len, self.head_dim)
+        return (self.batch, self.n_kv_heads, self.kv_rows, self.head_dim)
+
+    @property
+    def lse_shape(self):
+        return self.q_shape[:-1]
 
     @property
     def decode(self) -> bool:
@@ -144,6 +171,13 @@ def _expect(t, name, shape, dtype, device_type="cuda"):
         raise ValueError(f"{name}: must be a {device_type} tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
+
+
+def _cp(p: Problem):
+    """The C problem of p, after checking its packed-sequence offsets tensor."""
+    if p.cu is not None:
+        _expect(p.cu, "cu", (p.batch + 1,), torch.int32)
+    return ctypes.byref(p.c())
 
 
 # ---- geometry helpers (same names as the C ABI) ----
@@ -184,50 +218,50 @@ def pyr_abi_version() -> int:
 # ---- the hot path (same names as the C ABI) ----
 
 def pyr_build_pyramid(p: Problem, k, pyramid, stream=None):
-    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_rows, p.head_dim), p.dtype)
+    _expect(k, "k", p.kv_shape, p.dtype)
     _expect(pyramid, "pyramid", pyramid_shape(p), torch.float32)
-    _check(lib().pyr_build_pyramid(ctypes.byref(p.c()), _ptr(k), _ptr(pyramid), _stream(stream)))
+    _check(lib().pyr_build_pyramid(_cp(p), _ptr(k), _ptr(pyramid), _stream(stream)))
 
 
 def pyr_append_pyramid(p: Problem, k, old_len: int, pyramid, stream=None):
-    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_rows, p.head_dim), p.dtype)
+    _expect(k, "k", p.kv_shape, p.dtype)
     _expect(pyramid, "pyramid", pyramid_shape(p), torch.float32)
-    _check(lib().pyr_append_pyramid(ctypes.byref(p.c()), _ptr(k), int(old_len), _ptr(pyramid),
+    _check(lib().pyr_append_pyramid(_cp(p), _ptr(k), int(old_len), _ptr(pyramid),
                                     _stream(stream)))
 
 
 def pyr_select_topk(p: Problem, q, pyramid, sel, trace_ids=None, trace_scores=None, stream=None):
     nqb, L = pyr_num_query_blocks(p), pyr_num_levels(p)
-    _expect(q, "q", (p.batch, p.n_q_heads, p.q_len, p.head_dim), p.dtype)
+    _expect(q, "q", p.q_shape, p.dtype)
     _expect(pyramid, "pyramid", pyramid_shape(p), torch.float32)
     _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
     _expect(trace_ids, "trace_ids", (p.batch, p.n_kv_heads, nqb, L, p.top_k), torch.int32)
     _expect(trace_scores, "trace_scores", (p.batch, p.n_kv_heads, nqb, L, p.top_k + 1),
             torch.float32)
-    _check(lib().pyr_select_topk(ctypes.byref(p.c()), _ptr(q), _ptr(pyramid), _ptr(sel),
+    _check(lib().pyr_select_topk(_cp(p), _ptr(q), _ptr(pyramid), _ptr(sel),
                                  _ptr(trace_ids), _ptr(trace_scores), _stream(stream)))
 
 
 def pyr_block_sparse_attn(p: Problem, q, k, v, sel, o, lse=None, workspace=None, stream=None):
     nqb = pyr_num_query_blocks(p)
-    _expect(q, "q", (p.batch, p.n_q_heads, p.q_len, p.head_dim), p.dtype)
-    _expect(k, "k", (p.batch, p.n_kv_heads, p.kv_rows, p.head_dim), p.dtype)
-    _expect(v, "v", (p.batch, p.n_kv_heads, p.kv_rows, p.head_dim), p.dtype)
+    _expect(q, "q", p.q_shape, p.dtype)
+    _expect(k, "k", p.kv_shape, p.dtype)
+    _expect(v, "v", p.kv_shape, p.dtype)
     _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
-    _expect(o, "o", (p.batch, p.n_q_heads, p.q_len, p.head_dim), p.dtype)
-    _expect(lse, "lse", (p.batch, p.n_q_heads, p.q_len), torch.float32)
+    _expect(o, "o", p.q_shape, p.dtype)
+    _expect(lse, "lse", p.lse_shape, torch.float32)
     nbytes = 0
     if workspace is not None:
         if workspace.device.type != "cuda" or not workspace.is_contiguous():
             raise ValueError("workspace: must be a contiguous cuda tensor")
         nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().pyr_block_sparse_attn(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
+    _check(lib().pyr_block_sparse_attn(_cp(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
                                        _ptr(o), _ptr(lse), _ptr(workspace), nbytes,
                                        _stream(stream)))
 
 
 def pyr_attn_bwd_workspace_bytes(p: Problem) -> int:
-    return lib().pyr_attn_bwd_workspace_bytes(ctypes.byref(p.c()))
+    return lib().pyr_attn_bwd_workspace_bytes(_cp(p))
 
 
 def _workspace_bytes(workspace) -> int:
@@ -241,15 +275,15 @@ def _workspace_bytes(workspace) -> int:
 def pyr_block_sparse_attn_bwd(p: Problem, q, k, v, sel, o, lse, dout, dq, dk, dv, workspace,
                               stream=None):
     nqb = pyr_num_query_blocks(p)
-    qs = (p.batch, p.n_q_heads, p.q_len, p.head_dim)
-    ks = (p.batch, p.n_kv_heads, p.kv_len, p.head_dim)
+    qs = p.q_shape
+    ks = p.kv_shape
     for t, name, shape in ((q, "q", qs), (k, "k", ks), (v, "v", ks), (o, "o", qs),
                            (dout, "dout", qs), (dq, "dq", qs), (dk, "dk", ks), (dv, "dv", ks)):
         _expect(t, name, shape, p.dtype)
     _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
-    _expect(lse, "lse", (p.batch, p.n_q_heads, p.q_len), torch.float32)
+    _expect(lse, "lse", p.lse_shape, torch.float32)
     _check(lib().pyr_block_sparse_attn_bwd(
-        ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(o), _ptr(lse), _ptr(dout),
+        _cp(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(o), _ptr(lse), _ptr(dout),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), _workspace_bytes(workspace),
         _stream(stream)))
 
@@ -314,4 +348,29 @@ def forward(q, k, v, branching: int, top_k: int, scale: float = 0.0, pyramid=Non
     pyr_block_sparse_attn(p, q, k, v, sel, o, lse, alloc_workspace(p, q.device))
     if with_trace:
         return o, lse, sel, pyramid, trace
+    return o, lse, sel, pyramid
+
+
+def problem_for_packed(q, k, cu, max_len: int, branching: int, top_k: int,
+                       scale: float = 0.0) -> Problem:
+    """The packed problem of q [Hq, total, d], k [Hk, total, d] and row offsets
+    cu (int32, batch+1 entries) whose sequences are at most max_len long."""
+    Hq, total, d = q.shape
+    Hk = k.shape[0]
+    return Problem(cu.numel() - 1, Hq, Hk, d, max_len, max_len, branching, top_k, q.dtype, scale,
+                   cu=cu, total_len=total)
+
+
+def forward_packed(q, k, v, cu, max_len: int, branching: int, top_k: int, scale: float = 0.0):
+    """The whole path on a packed batch: every sequence attends within itself.
+    Returns (o, lse, sel, pyramid) with o like q and lse [Hq, total]; rows of
+    no sequence are left as torch.empty leaves them."""
+    p = problem_for_packed(q, k, cu, max_len, branching, top_k, scale)
+    pyramid = alloc_pyramid(p, q.device)
+    pyr_build_pyramid(p, k, pyramid)
+    sel = alloc_sel(p, q.device)
+    pyr_select_topk(p, q, pyramid, sel)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    pyr_block_sparse_attn(p, q, k, v, sel, o, lse, alloc_workspace(p, q.device))
     return o, lse, sel, pyramid

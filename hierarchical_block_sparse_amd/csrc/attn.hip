@@ -124,12 +124,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
   int bi, hk, i;
   int64_t unit;
   unit_of(g, blockIdx.x / wg_per_unit, bi, hk, i, unit);
+  const PyrSeq sq = pyr_seq(g, bi);
+  if (i >= sq.nqb) return;  // past the end of a shorter packed sequence
   const int h = hk * g.G + sub * (NW / WPH) + w / WPH;
   const int rsub = (w % WPH) * 32;
   const float sl2 = g.scale * PYR_LOG2E;
   const int64_t row0 = (int64_t)i * PYR_BLOCK + rsub;  // first query token of this wave
-  const bf16_t* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
-  const bf16_t* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
+  const bf16_t* kh = k + (sq.k0 + hk * sq.khs) * D;
+  const bf16_t* vh = v + (sq.k0 + hk * sq.khs) * D;
 
   for (int jj = tid; jj <= g.K; jj += NT) s_sel[jj] = sel[unit * (g.K + 1) + jj];
 
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
     int n = 0;
     for (int jj = 0; jj <= g.K; ++jj) {
       const int j = s_sel[jj];
-      if (j >= 0 && j < g.nb) s_sel[n++] = j;
+      if (j >= 0 && j < sq.nb) s_sel[n++] = j;
     }
     s_n = n;
   }
@@ -146,15 +148,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
   const int nsel = s_n;
 #pragma unroll
   for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
-    if (s0 < nsel) issue_tiles<D, NW>(kh, vh, g.Tk, s_sel[s0], tiles[s0][0], tiles[s0][1], w, l);
+    if (s0 < nsel) issue_tiles<D, NW>(kh, vh, sq.Tk, s_sel[s0], tiles[s0][0], tiles[s0][1], w, l);
 
   // Q^T fragments (B operand): lane holds query row rt*32 + lr and d = ks*16 + 8*half .. +7.
   // Rows past the end of a ragged last block load the last row instead; they are never stored.
-  const bf16_t* qh = q + ((int64_t)bi * g.Hq + h) * g.Tq * D;
+  const bf16_t* qh = q + (sq.q0 + h * sq.qhs) * D;
   uint4 qb[RT][D / 16];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int64_t tok = min<int64_t>(row0 + rt * 32 + lr, g.Tq - 1);
+    const int64_t tok = min<int64_t>(row0 + rt * 32 + lr, sq.Tq - 1);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qb[rt][ks] = ld16(qh + tok * D + ks * 16 + 8 * half);
   }
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
     __syncthreads();  // every wave's loads of block jj landed; the oldest stage is free
     const int nx = jj + NSTAGE - 1;
     const int nst = st + NSTAGE - 1 >= NSTAGE ? st - 1 : st + NSTAGE - 1;
-    if (nx < nsel) issue_tiles<D, NW>(kh, vh, g.Tk, s_sel[nx], tiles[nst][0], tiles[nst][1], w, l);
+    if (nx < nsel) issue_tiles<D, NW>(kh, vh, sq.Tk, s_sel[nx], tiles[nst][0], tiles[nst][1], w, l);
     const unsigned char* Kt = tiles[st][0];
     const unsigned char* Vt = tiles[st][1];
     const int64_t key0 = (int64_t)j * PYR_BLOCK;
@@ -292,12 +294,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
 
   // finalize: rows of this lane = rt*32 + lr; dims of oacc[dt][rt][e] =
   // dt*32 + (e/4)*8 + half*4 + e%4
-  bf16_t* oh = o + ((int64_t)bi * g.Hq + h) * g.Tq * D;
+  bf16_t* oh = o + (sq.q0 + h * sq.qhs) * D;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float lt = l_run[rt] + __shfl_xor(l_run[rt], 32, 64);
     const int64_t tok = row0 + rt * 32 + lr;
-    if (tok >= g.Tq) continue;
+    if (tok >= sq.Tq) continue;
     const float inv = 1.f / lt;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
         for (int e = 0; e < 4; ++e) pk[e] = (__bf16)(oacc[dt][rt][g4 * 4 + e] * inv);
         *reinterpret_cast<bf16x4*>(oh + tok * D + d0) = pk;
       }
-    if (lse && half == 0) lse[((int64_t)bi * g.Hq + h) * g.Tq + tok] = (m_run[rt] + log2f(lt)) * PYR_LN2;
+    if (lse && half == 0) lse[sq.q0 + h * sq.qhs + tok] = (m_run[rt] + log2f(lt)) * PYR_LN2;
   }
 }
 // ---------------------------------------------------------------------------
@@ -627,6 +629,8 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
   int bi, hk, i;
   int64_t unit;
   unit_of(g, blockIdx.x / wg_per_unit, bi, hk, i, unit);
+  const PyrSeq sq = pyr_seq(g, bi);
+  if (i >= sq.nqb) return;  // past the end of a shorter packed sequence
   // waves 2h and 2h+1 take the two 32-row halves of head sub*4 + h
   const int h = hk * g.G + sub * 4 + w / 2;
   const int64_t row0 = (int64_t)i * PYR_BLOCK + (w % 2) * 32;
@@ -644,7 +648,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
       for (int base = 0; base <= g.K; base += 64) {
         const int jj = base + l;
         const int j = jj <= g.K ? s_sel[jj] : -1;
-        const bool ok = j >= 0 && j < g.nb && ((pass == 0) == (j < i));
+        const bool ok = j >= 0 && j < sq.nb && ((pass == 0) == (j < i));
         const unsigned long long m = __ballot(ok);
         if (ok) s_ord[n + __popcll(m & ((1ull << l) - 1ull))] = j;
         n += __popcll(m);
@@ -663,12 +667,12 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
   __syncthreads();
   const int nsel = s_n, nun = s_nun;
   IlvRun run;
-  run.kh = k + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
-  run.vh = v + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
+  run.kh = k + (sq.k0 + hk * sq.khs) * D;
+  run.vh = v + (sq.k0 + hk * sq.khs) * D;
   run.ord = s_ord;
   run.ktiles = &ktiles[0][0];
   run.vtiles = &vtiles[0][0];
-  run.Tk = g.Tk;
+  run.Tk = sq.Tk;
   run.row0 = row0;
   run.nsel = nsel;
   run.w = w;
@@ -679,16 +683,16 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
 
   // Q^T fragments (B operand): lane holds query row lr and d = ks*16 + 8*half .. +7.
   // Rows past the end of a ragged last block load the last row; they are never stored.
-  const bf16_t* qh = q + ((int64_t)bi * g.Hq + h) * g.Tq * D;
+  const bf16_t* qh = q + (sq.q0 + h * sq.qhs) * D;
   uint4 qb[D / 16];
   {
-    const int64_t tok = min<int64_t>(row0 + lr, g.Tq - 1);
+    const int64_t tok = min<int64_t>(row0 + lr, sq.Tq - 1);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qb[ks] = ld16(qh + tok * D + ks * 16 + 8 * half);
   }
 #pragma unroll
   for (int b = 0; b < 3; ++b)
-    if (b < nsel) ilv_issue<D>(run.kh, run.vh, g.Tk, s_ord[b], w, l, ktiles[b], vtiles[b]);
+    if (b < nsel) ilv_issue<D>(run.kh, run.vh, sq.Tk, s_ord[b], w, l, ktiles[b], vtiles[b]);
 
   const IlvOffsets<D> fo(l);
   f32x16 oacc[D / 32];
@@ -741,9 +745,9 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
                                                   false, false);
   const float lt = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   const int64_t tok = row0 + lr;
-  if (tok >= g.Tq) return;
+  if (tok >= sq.Tq) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  bf16_t* orow = o + (((int64_t)bi * g.Hq + h) * g.Tq + tok) * D;
+  bf16_t* orow = o + (sq.q0 + h * sq.qhs + tok) * D;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -755,7 +759,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
       *reinterpret_cast<bf16x4*>(orow + dt * 32 + g4 * 8 + half * 4) = pk;
     }
   if (lse && half == 0)
-    lse[((int64_t)bi * g.Hq + h) * g.Tq + tok] = lt > 0.f ? (m_run + log2f(lt)) * PYR_LN2 : -INFINITY;
+    lse[sq.q0 + h * sq.qhs + tok] = lt > 0.f ? (m_run + log2f(lt)) * PYR_LN2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -777,13 +781,15 @@ __global__ __launch_bounds__(64) void attn_prefill_valu(const T* __restrict__ q,
   int bi, hk, i;
   int64_t unit;
   unit_of(g, blockIdx.x / g.G, bi, hk, i, unit);
+  const PyrSeq sq = pyr_seq(g, bi);
+  if (i >= sq.nqb) return;  // past the end of a shorter packed sequence
   const int h = hk * g.G + hsub;
   const float sl2 = g.scale * PYR_LOG2E;
   const int64_t rp = (int64_t)i * PYR_BLOCK + t;
-  const bool valid = rp < g.Tq;
+  const bool valid = rp < sq.Tq;
   for (int jj = t; jj <= g.K; jj += 64) s_sel[jj] = sel[unit * (g.K + 1) + jj];
   float qr[D], acc[D];
-  const T* qrow = q + (((int64_t)bi * g.Hq + h) * g.Tq + (valid ? rp : 0)) * D;
+  const T* qrow = q + (sq.q0 + h * sq.qhs + (valid ? rp : 0)) * D;
   for (int d0 = 0; d0 < D; d0 += VEC) {
     float x[VEC];
     unpack16<T>(ld16(qrow + d0), x);
@@ -793,19 +799,19 @@ __global__ __launch_bounds__(64) void attn_prefill_valu(const T* __restrict__ q,
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
   float m = -INFINITY, lsum = 0.f;
-  const T* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
-  const T* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
+  const T* kh = k + (sq.k0 + hk * sq.khs) * D;
+  const T* vh = v + (sq.k0 + hk * sq.khs) * D;
   __syncthreads();
   for (int jj = 0; jj <= g.K; ++jj) {
     const int j = s_sel[jj];
-    if (j < 0 || j >= g.nb) continue;  // uniform across the workgroup
+    if (j < 0 || j >= sq.nb) continue;  // uniform across the workgroup
     const int64_t key0 = (int64_t)j * PYR_BLOCK;
     __syncthreads();
     for (int s = t; s < 64 * (D / VEC); s += 64) {
       const int key = s / (D / VEC), c = (s % (D / VEC)) * VEC;
       const int64_t kp = key0 + key;
       float xk[VEC], xv[VEC];
-      if (kp < g.Tk) {
+      if (kp < sq.Tk) {
         unpack16<T>(ld16(kh + kp * D + c), xk);
         unpack16<T>(ld16(vh + kp * D + c), xv);
       } else {
@@ -846,7 +852,7 @@ __global__ __launch_bounds__(64) void attn_prefill_valu(const T* __restrict__ q,
     m = m_new;
   }
   if (!valid) return;
-  T* orow = o + (((int64_t)bi * g.Hq + h) * g.Tq + rp) * D;
+  T* orow = o + (sq.q0 + h * sq.qhs + rp) * D;
   const float inv = 1.f / lsum;
   for (int d = 0; d < D; ++d) {
     const float y = acc[d] * inv;
@@ -855,7 +861,7 @@ __global__ __launch_bounds__(64) void attn_prefill_valu(const T* __restrict__ q,
     else
       orow[d] = (T)f32_to_bf16_bits(y);
   }
-  if (lse) lse[((int64_t)bi * g.Hq + h) * g.Tq + rp] = (m + log2f(lsum)) * PYR_LN2;
+  if (lse) lse[sq.q0 + h * sq.qhs + rp] = (m + log2f(lsum)) * PYR_LN2;
 }
 
 // ---------------------------------------------------------------------------

@@ -78,6 +78,20 @@ pyr_status resolve(const pyr_problem* p, PyrGeom* g) {
     return fail(PYR_ERR_UNSUPPORTED, "q_len %lld with kv_len %lld (need q_len == kv_len or q_len == 1)",
                 (long long)p->q_len, (long long)p->kv_len);
   if (!(p->scale >= 0.f) || isinf(p->scale)) return fail(PYR_ERR_INVALID, "scale must be finite and >= 0");
+  if (p->cu) {
+    if (!prefill)
+      return fail(PYR_ERR_UNSUPPORTED,
+                  "packed sequences need q_len == kv_len (the bound on every sequence's length)");
+    if (p->kv_capacity != 0)
+      return fail(PYR_ERR_UNSUPPORTED, "packed sequences take no kv_capacity");
+    if (p->total_len < 0) return fail(PYR_ERR_INVALID, "total_len %lld < 0", (long long)p->total_len);
+    if (p->total_len > ((int64_t)1 << 36)) return fail(PYR_ERR_UNSUPPORTED, "total_len > 2^36");
+    if (reinterpret_cast<uintptr_t>(p->cu) & 3u)
+      return fail(PYR_ERR_MISALIGNED, "cu must be 4-byte aligned");
+  } else if (p->total_len != 0) {
+    return fail(PYR_ERR_INVALID, "total_len %lld without cu (dense problems take 0)",
+                (long long)p->total_len);
+  }
 
   memset(g, 0, sizeof *g);
   g->Tq = p->q_len;
@@ -95,9 +109,13 @@ pyr_status resolve(const pyr_problem* p, PyrGeom* g) {
   g->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
   g->planes = p->dtype == PYR_BF16 ? 2 : 1;
   // layout (level count, offsets, node count) from the capacity; valid nodes
-  // per level from kv_len (one node, the mean of everything, above its root)
-  g->Tks = p->kv_capacity ? p->kv_capacity : p->kv_len;
-  const int64_t nb_cap = (g->Tks + PYR_BLOCK - 1) / PYR_BLOCK;
+  // per level from kv_len (one node, the mean of everything, above its root).
+  // Packed sequences: every slab is laid out for the length bound kv_len, and
+  // every head of q, k, v, o and lse holds total_len rows.
+  g->cu = p->cu;
+  g->Tks = p->cu ? p->total_len : (p->kv_capacity ? p->kv_capacity : p->kv_len);
+  g->Tqs = p->cu ? p->total_len : p->q_len;
+  const int64_t nb_cap = ((p->cu ? p->kv_len : g->Tks) + PYR_BLOCK - 1) / PYR_BLOCK;
   const int L = level_sizes(nb_cap, p->branching, nullptr, g->loff, &g->n_tot);
   if (L < 0) return fail(PYR_ERR_UNSUPPORTED, "more than %d pyramid levels", PYR_MAX_LEVELS);
   g->L = L;
@@ -158,7 +176,7 @@ pyr_status pyr_build_pyramid(const pyr_problem* p, const void* k, float* pyramid
   PyrGeom g;
   pyr_status s = resolve(p, &g);
   if (s != PYR_OK) return s;
-  const bool empty = (int64_t)g.B * g.Hk == 0 || g.nb == 0;
+  const bool empty = (int64_t)g.B * g.Hk == 0 || g.nb == 0 || (g.cu && g.Tks == 0);
   if (!empty && (!k || !pyramid)) return fail(PYR_ERR_NULL, "k or pyramid is NULL");
   if (!empty && (!aligned16(k) || !aligned16(pyramid)))
     return fail(PYR_ERR_MISALIGNED, "k and pyramid must be 16-byte aligned");
@@ -173,7 +191,7 @@ pyr_status pyr_select_topk(const pyr_problem* p, const void* q, const float* pyr
   PyrGeom g;
   pyr_status s = resolve(p, &g);
   if (s != PYR_OK) return s;
-  const bool empty = (int64_t)g.B * g.Hk * g.nqb == 0 || g.Tq == 0;
+  const bool empty = (int64_t)g.B * g.Hk * g.nqb == 0 || g.Tq == 0 || (g.cu && g.Tqs == 0);
   if (!empty && (!q || !pyramid || !sel)) return fail(PYR_ERR_NULL, "q, pyramid or sel is NULL");
   if (!empty && (!aligned16(q) || !aligned16(pyramid) || !aligned16(sel) ||
                  (trace_ids && !aligned16(trace_ids)) || (trace_scores && !aligned16(trace_scores))))
@@ -193,7 +211,7 @@ pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void
   PyrGeom g;
   pyr_status s = resolve(p, &g);
   if (s != PYR_OK) return s;
-  const bool empty = (int64_t)g.B * g.Hk * g.nqb == 0 || g.Tq == 0;
+  const bool empty = (int64_t)g.B * g.Hk * g.nqb == 0 || g.Tq == 0 || (g.cu && g.Tqs == 0);
   if (!empty && (!q || !k || !v || !sel || !o)) return fail(PYR_ERR_NULL, "q, k, v, sel or o is NULL");
   if (!empty && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) ||
                  !aligned16(o) || (lse && !aligned16(lse))))
@@ -215,6 +233,7 @@ pyr_status pyr_append_pyramid(const pyr_problem* p, const void* k, int64_t old_l
   PyrGeom g;
   pyr_status s = resolve(p, &g);
   if (s != PYR_OK) return s;
+  if (g.cu) return fail(PYR_ERR_UNSUPPORTED, "pyr_append_pyramid takes no packed sequences");
   if (old_len <= 0 || old_len > g.Tk)
     return fail(PYR_ERR_INVALID, "old_len %lld outside (0, kv_len = %lld]", (long long)old_len,
                 (long long)g.Tk);
@@ -228,7 +247,7 @@ pyr_status pyr_append_pyramid(const pyr_problem* p, const void* k, int64_t old_l
 
 size_t pyr_attn_bwd_workspace_bytes(const pyr_problem* p) {
   PyrGeom g;
-  return resolve(p, &g) == PYR_OK ? pyr_attn_bwd_ws_bytes(g) : 0;
+  return resolve(p, &g) == PYR_OK && !g.cu ? pyr_attn_bwd_ws_bytes(g) : 0;
 }
 
 pyr_status pyr_block_sparse_attn_bwd(const pyr_problem* p, const void* q, const void* k,
@@ -241,6 +260,7 @@ pyr_status pyr_block_sparse_attn_bwd(const pyr_problem* p, const void* q, const 
   pyr_status s = resolve(p, &g);
   if (s != PYR_OK) return s;
   if (g.decode) return fail(PYR_ERR_UNSUPPORTED, "the backward is implemented for prefill only");
+  if (g.cu) return fail(PYR_ERR_UNSUPPORTED, "the backward takes no packed sequences");
   if (p->dtype != PYR_BF16)
     return fail(PYR_ERR_UNSUPPORTED, "the backward is implemented for bfloat16 only");
   if (g.Tks != g.Tk)

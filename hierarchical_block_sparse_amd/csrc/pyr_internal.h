@@ -11,7 +11,9 @@
 // Problem geometry resolved once on the host and passed by value to kernels.
 struct PyrGeom {
   int64_t Tq, Tk;          // query / key lengths
-  int64_t Tks;             // rows per head in k and v: the capacity (or Tk)
+  int64_t Tks;             // rows per head in k and v: the capacity (or Tk); packed: all rows
+  int64_t Tqs;             // rows per head in q, o and lse: Tq; packed: all rows
+  const int32_t* cu;       // packed sequences: device row offsets [B + 1]; dense: null
   int64_t n_tot;           // pyramid nodes per (batch, KV head) slab
   int32_t planes;          // pyramid planes: 1 (fp32 problems) or 2 (bf16: + hi/lo split)
   int32_t B, Hq, Hk, G, D; // batch, heads, group size Hq/Hk, head dim
@@ -25,13 +27,54 @@ struct PyrGeom {
   int64_t loff[PYR_MAX_LEVELS];   // node offset of each level inside a slab (from the capacity)
 };
 
-// Token count covered by node m of level `level` (blocks [m b^l, (m+1) b^l)).
-__host__ __device__ inline int64_t pyr_node_tokens(const PyrGeom& g, int level, int64_t m) {
+// Token count covered by node m of level `level` (blocks [m b^l, (m+1) b^l))
+// of a sequence of Tk keys.
+__host__ __device__ inline int64_t pyr_node_tokens(int64_t Tk, int branching, int level,
+                                                   int64_t m) {
   int64_t span = PYR_BLOCK;
-  for (int i = 0; i < level; ++i) span *= g.branching;
+  for (int i = 0; i < level; ++i) span *= branching;
   int64_t t0 = m * span, t1 = t0 + span;
-  if (t1 > g.Tk) t1 = g.Tk;
+  if (t1 > Tk) t1 = Tk;
   return t1 > t0 ? t1 - t0 : 0;
+}
+
+// One sequence of a problem.  Row t of query head h is row q0 + h * qhs + t of
+// q (and of o and lse); row t of KV head hk is row k0 + hk * khs + t of k and
+// v.  Dense batches use the strides of [B, H, T, d].  In a packed batch every
+// head holds all sequences back to back, sequence bi owning rows
+// [cu[bi], cu[bi+1]); the offsets are clipped to the packed row count and the
+// length to the problem's bound, so malformed offsets cannot reach outside the
+// tensors.
+struct PyrSeq {
+  int64_t Tq, Tk;    // query and key lengths of the sequence
+  int64_t q0, k0;    // row of token 0 of head 0
+  int64_t qhs, khs;  // rows between heads
+  int32_t nb, nqb;   // key blocks, query blocks
+};
+
+__device__ __forceinline__ PyrSeq pyr_seq(const PyrGeom& g, int bi) {
+  PyrSeq s;
+  if (g.cu) {
+    const int64_t tot = g.Tks;
+    int64_t a = g.cu[bi], e = g.cu[bi + 1];
+    a = a < 0 ? 0 : (a > tot ? tot : a);
+    e = e < a ? a : (e > tot ? tot : e);
+    const int64_t n = e - a < g.Tk ? e - a : g.Tk;
+    s.Tq = s.Tk = n;
+    s.q0 = s.k0 = a;
+    s.qhs = s.khs = tot;
+    s.nb = s.nqb = (int32_t)((n + PYR_BLOCK - 1) / PYR_BLOCK);
+  } else {
+    s.Tq = g.Tq;
+    s.Tk = g.Tk;
+    s.qhs = g.Tqs;
+    s.khs = g.Tks;
+    s.q0 = (int64_t)bi * g.Hq * g.Tqs;
+    s.k0 = (int64_t)bi * g.Hk * g.Tks;
+    s.nb = g.nb;
+    s.nqb = g.nqb;
+  }
+  return s;
 }
 
 // Launchers (each returns the hipError_t of its launches).

@@ -63,9 +63,11 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x / chunks_per_bh;
   const int c = blockIdx.x % chunks_per_bh;
+  const PyrSeq sq = pyr_seq(g, (int)(bh / g.Hk));
   const int64_t blk0 = (int64_t)c * chunk;
-  const int nblk = (int)min<int64_t>(chunk, g.nb - blk0);
-  const T* kb = k + bh * g.Tks * D;
+  const int nblk = (int)min<int64_t>(chunk, sq.nb - blk0);
+  if (nblk <= 0) return;  // past the end of a shorter packed sequence
+  const T* kb = k + (sq.k0 + (bh % g.Hk) * sq.khs) * D;
   float* slab = pyr + bh * g.planes * g.n_tot * D;
 
   const int col = (tid % TPR) * VEC;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         const int64_t tok = (blk0 + jb + u) * PYR_BLOCK + r0 + p * RPP;
-        if (jb + u < nblk && tok < g.Tk)
+        if (jb + u < nblk && tok < sq.Tk)
           raw[u][p] = ld16_nt(kb + tok * D + col);
         else
           raw[u][p] = make_uint4(0, 0, 0, 0);
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
 #pragma unroll
         for (int r = 0; r < RPP; ++r) s += part[u][r][dcol];
         const int64_t m = blk0 + jb + u;
-        const float mean = s / (float)pyr_node_tokens(g, 0, m);
+        const float mean = s / (float)pyr_node_tokens(sq.Tk, g.branching, 0, m);
         nodes[0][jb + u][dcol] = mean;
         put_node<D>(g, slab, g.loff[0] + m, dcol, mean);
       }
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
       for (int j = 0; j < b; ++j) {
         const int cidx = m * b + j;
         if (cidx < n_below) {
-          const float w = (float)pyr_node_tokens(g, lvl - 1, first_below + cidx);
+          const float w = (float)pyr_node_tokens(sq.Tk, b, lvl - 1, first_below + cidx);
           num += nodes[cur][cidx][dcol] * w;
           den += w;
         }
@@ -150,9 +152,13 @@ __global__ __launch_bounds__(kThreads) void build_top(float* __restrict__ pyr, P
                                                       int first_level) {
   float* slab = pyr + (int64_t)blockIdx.x * g.planes * g.n_tot * D;
   const int b = g.branching;
+  const PyrSeq sq = pyr_seq(g, (int)(blockIdx.x / g.Hk));
+  if (sq.nb == 0) return;
+  // valid nodes one level below first_level (one node above the root)
+  int n_below = sq.nb;
+  for (int lvl = 1; lvl < first_level; ++lvl) n_below = n_below > 1 ? (n_below + b - 1) / b : 1;
   for (int lvl = first_level; lvl < g.L; ++lvl) {
-    const int n_here = g.lsize[lvl];
-    const int n_below = g.lsize[lvl - 1];
+    const int n_here = n_below > 1 ? (n_below + b - 1) / b : 1;
     const float* below = slab + g.loff[lvl - 1] * D;
 
     for (int idx = threadIdx.x; idx < n_here * D; idx += kThreads) {
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void build_top(float* __restrict__ pyr, P
       for (int j = 0; j < b; ++j) {
         const int64_t cidx = (int64_t)m * b + j;
         if (cidx < n_below) {
-          const float w = (float)pyr_node_tokens(g, lvl - 1, cidx);
+          const float w = (float)pyr_node_tokens(sq.Tk, b, lvl - 1, cidx);
           num += below[cidx * D + dcol] * w;
           den += w;
         }
@@ -170,6 +176,7 @@ __global__ __launch_bounds__(kThreads) void build_top(float* __restrict__ pyr, P
     }
     __threadfence_block();
     __syncthreads();
+    n_below = n_here;
   }
 }
 
@@ -222,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void append_nodes(const T* __restrict__ k
       for (int jj = 0; jj < b; ++jj) {
         const int64_t cidx = m * b + jj;
         if (cidx < n_below) {
-          const float w = (float)pyr_node_tokens(g, lvl - 1, cidx);
+          const float w = (float)pyr_node_tokens(g.Tk, b, lvl - 1, cidx);
           num += below[cidx * D + c] * w;
           den += w;
         }

@@ -250,6 +250,18 @@ __device__ __forceinline__ void write_route(const PyrGeom& g, int64_t unit, cons
   for (int j = threadIdx.x; j <= g.K; j += kThreads) out[j] = j < nk ? kept[j] : (j == nk ? diag : -1);
 }
 
+// A unit past the end of a shorter packed sequence: its route row (and trace)
+// hold nothing.
+__device__ void blank_unit(const PyrGeom& g, int64_t unit, int32_t* sel, int32_t* trace_ids,
+                           float* trace_scores) {
+  for (int j = threadIdx.x; j <= g.K; j += kThreads) sel[unit * (g.K + 1) + j] = -1;
+  if (trace_ids)
+    for (int j = threadIdx.x; j < g.L * g.K; j += kThreads) trace_ids[unit * g.L * g.K + j] = -1;
+  if (trace_scores)
+    for (int j = threadIdx.x; j < g.L * (g.K + 1); j += kThreads)
+      trace_scores[unit * g.L * (g.K + 1) + j] = NAN;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 prefill path: MFMA scoring.  MT = 16-row M tiles per wave.
 // ---------------------------------------------------------------------------
@@ -366,6 +378,11 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
   const int i = (int)(unit % g.nqb);
   const int64_t bhk = unit / g.nqb;  // b * Hk + hk
   const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
+  const PyrSeq sq = pyr_seq(g, bi);
+  if (i >= sq.nqb) {
+    blank_unit(g, unit, sel, trace_ids, trace_scores);
+    return;
+  }
   const int diag = i;
   const int RW = MT * 16;  // rows per wave
   const float sl2 = g.scale * PYR_LOG2E;
@@ -382,18 +399,18 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
   for (int mt = 0; mt < MT; ++mt) {
     const int ra = w * RW + mt * 16 + (l % 16);
     const int h = ra / PYR_BLOCK, t = ra % PYR_BLOCK;
-    const int64_t tok = min<int64_t>((int64_t)i * PYR_BLOCK + t, g.Tq - 1);
-    const bf16_t* qrow = q + (((int64_t)bi * g.Hq + (int64_t)hk * g.G + h) * g.Tq + tok) * D;
+    const int64_t tok = min<int64_t>((int64_t)i * PYR_BLOCK + t, sq.Tq - 1);
+    const bf16_t* qrow = q + (sq.q0 + ((int64_t)hk * g.G + h) * sq.qhs + tok) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) qa[mt][ks] = ld16(qrow + ks * 32 + 8 * (l / 16));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rc = w * RW + mt * 16 + 4 * (l / 16) + j;
-      if ((int64_t)i * PYR_BLOCK + rc % PYR_BLOCK < g.Tq) rowvalid |= 1u << (mt * 4 + j);
+      if ((int64_t)i * PYR_BLOCK + rc % PYR_BLOCK < sq.Tq) rowvalid |= 1u << (mt * 4 + j);
     }
   }
 
-  const bool full = (int64_t)(i + 1) * PYR_BLOCK <= g.Tq;  // every row of the unit is real
+  const bool full = (int64_t)(i + 1) * PYR_BLOCK <= sq.Tq;  // every row of the unit is real
   // plane 1 of the slab: the split rows
   const unsigned char* split =
       reinterpret_cast<const unsigned char*>(pyr + (bhk * g.planes + 1) * g.n_tot * D);
@@ -513,6 +530,11 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
   const int i = (int)(unit % g.nqb);
   const int64_t bhk = unit / g.nqb;
   const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
+  const PyrSeq sq = pyr_seq(g, bi);
+  if (i >= sq.nqb) {
+    blank_unit(g, unit, sel, trace_ids, trace_scores);
+    return;
+  }
   int64_t tok0, ntok;
   int diag;
   if (g.decode) {
@@ -521,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
     diag = (int)((g.Tk - 1) / PYR_BLOCK);
   } else {
     tok0 = (int64_t)i * PYR_BLOCK;
-    ntok = min<int64_t>(PYR_BLOCK, g.Tq - tok0);
+    ntok = min<int64_t>(PYR_BLOCK, sq.Tq - tok0);
     diag = i;
   }
   const int R = (int)(g.G * ntok);
@@ -547,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
         const int cc = p / R, r = p % R;
         const int h = (int)(r / ntok);
         const int64_t tok = tok0 + r % ntok;
-        const T* qrow = q + (((int64_t)bi * g.Hq + (int64_t)hk * g.G + h) * g.Tq + tok) * D;
+        const T* qrow = q + (sq.q0 + ((int64_t)hk * g.G + h) * sq.qhs + tok) * D;
         const float* krow = lvl + (int64_t)cand[c0 + cc] * D;
         float acc = 0.f;
         for (int d0 = 0; d0 < D; d0 += 16 / (int)sizeof(T)) {

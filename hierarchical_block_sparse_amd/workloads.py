@@ -19,6 +19,7 @@ add 3u to that sequence's single query token in every head of the group.
 
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, replace
 
 import numpy as np
@@ -209,3 +210,43 @@ def make_route(cfg: Config, with_invalid: bool = True):
                 out[bi, hk, i, :len(row)] = row
     return torch.from_numpy(out)
 
+
+
+# ---- packed batches (sequences back to back along the token axis) ----
+
+def packed_lengths(total: int, shortest: int, longest: int, seed: int = 0) -> list[int]:
+    """Sequence lengths of a packed batch of `total` rows: log-uniform in
+    [shortest, longest] (numpy.random.default_rng(5000 + seed)), drawn until
+    they fill `total`; the last one is cut to fit."""
+    rng = np.random.default_rng(5000 + seed)
+    out: list[int] = []
+    while sum(out) < total:
+        n = int(round(math.exp(rng.uniform(math.log(shortest), math.log(longest)))))
+        out.append(min(n, total - sum(out)))
+    return out
+
+
+def make_packed_inputs(cfg: Config, lengths, device="cpu", spare_rows: int = 0):
+    """(q, k, v, cu) of a packed batch: q [Hq, total, d], k and v [Hk, total, d]
+    and cu int32 [S+1] with cu[s] = lengths[0] + ... + lengths[s-1].  Sequence
+    s holds the inputs make_inputs draws for cfg at batch 1 and length
+    lengths[s] with seed cfg.seed * 1000 + s (planted retrieval stays inside
+    the sequence).  spare_rows rows of NaN follow the last sequence: no
+    sequence owns them, so nothing may read them."""
+    device = torch.device(device)
+    qs, ks, vs = [], [], []
+    for s, n in enumerate(lengths):
+        c = replace(cfg, batch=1, q_len=n, kv_len=n, seed=cfg.seed * 1000 + s)
+        q, k, v = make_inputs(c, device)
+        qs.append(q[0])
+        ks.append(k[0])
+        vs.append(v[0])
+    if spare_rows:
+        nan = float("nan")
+        qs.append(torch.full((cfg.n_q_heads, spare_rows, cfg.head_dim), nan, dtype=cfg.dtype,
+                             device=device))
+        ks.append(torch.full((cfg.n_kv_heads, spare_rows, cfg.head_dim), nan, dtype=cfg.dtype,
+                             device=device))
+        vs.append(ks[-1].clone())
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device=device)
+    return torch.cat(qs, 1), torch.cat(ks, 1), torch.cat(vs, 1), cu

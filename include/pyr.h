@@ -39,6 +39,28 @@
  *    diagonal block is (kv_len-1)/64.  Other q_len are PYR_ERR_UNSUPPORTED.
  *    kv_len need not be a multiple of 64: a ragged last block is pooled over
  *    its valid tokens and masked beyond kv_len.
+ *
+ * Packed sequences (pyr_problem.cu != NULL; prefill only)
+ * --------------------------------------------------------
+ *  - q, o are [Hq, total_len, d], k, v are [Hk, total_len, d] and lse is
+ *    [Hq, total_len]: every head holds the sequences back to back, sequence s
+ *    in rows [cu[s], cu[s+1]).  Rows outside every sequence are neither read
+ *    nor written.
+ *  - Each sequence is its own problem of length n_s = cu[s+1] - cu[s]: its
+ *    64-token blocks start at its first row, its pyramid pools only its own
+ *    keys, selection and attention never leave it, and a ragged last block
+ *    is pooled over its valid rows.  The results are those of a dense problem
+ *    of batch 1 and length n_s for every s.
+ *  - The pyramid is [batch, Hk, P, nodes, d] and sel is [batch, Hk, nqb, K+1]
+ *    with the layout a dense problem of length kv_len (the bound) has; route
+ *    rows of query blocks past a sequence's end hold -1 only (trace rows -1
+ *    and NaN), and pyramid nodes past its valid levels are left unwritten.
+ *  - The offsets are read on the device, so the host cannot check them:
+ *    offsets that break the rules above give unspecified results, but every
+ *    access stays inside the tensors (offsets are clipped to [0, total_len]
+ *    and lengths to kv_len).
+ *  - pyr_append_pyramid and pyr_block_sparse_attn_bwd take no packed
+ *    sequences (PYR_ERR_UNSUPPORTED).
  */
 #ifndef PYR_H_
 #define PYR_H_
@@ -52,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PYR_ABI_VERSION 2
+#define PYR_ABI_VERSION 3
 
 typedef enum pyr_status {
   PYR_OK = 0,
@@ -87,6 +109,16 @@ typedef struct pyr_problem {
                           count follow the capacity, the valid nodes of each
                           level follow kv_len, so a pyramid can grow by
                           pyr_append_pyramid without moving (decode)          */
+  const int32_t* cu;   /* NULL: a dense batch.  Else a packed batch of `batch`
+                          sequences (PHBA §A.1.1-§A.1.2: packed inputs, block
+                          boundaries from cu and the block size): a DEVICE
+                          array of batch+1 int32 row offsets, cu[0] = 0,
+                          nondecreasing, cu[batch] <= total_len; sequence s
+                          owns rows [cu[s], cu[s+1]) of every head.  Needs
+                          q_len == kv_len = a bound on every sequence's length
+                          and kv_capacity == 0.  See "Packed sequences".      */
+  int64_t total_len;   /* packed: rows per head of q, k, v, o and lse; 0 when
+                          cu is NULL                                          */
 } pyr_problem;
 
 /* ---- geometry helpers (host-only, no device work; -1 on invalid input) ---- */

@@ -50,6 +50,13 @@ Readings of the pages this oracle rests on (the pages leave these open):
       none are unchanged.  A pyramid laid out for a capacity C has the levels
       of ceil(C / block) blocks; levels above the root of the valid keys hold
       one node, the mean of all of them.
+  R16 Packed sequences (PHBA §A.1.1-§A.1.2): a packed batch is a set of
+      independent sequences, sequence s owning rows [cu[s], cu[s+1]) of every
+      head.  Its blocks start at its own first row (boundaries from cu and the
+      block size), its pooled keys average its own valid rows only, and its
+      candidates, routes and attended keys never leave it; route slots of
+      query blocks past its end hold -1.  So each sequence gets exactly the
+      result of a batch-1 problem of its own length.
 """
 
 from __future__ import annotations
@@ -425,3 +432,55 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndar
                     np.add.at(dk[bi, hk], kp, dkk)
                     np.add.at(dv[bi, hk], kp, dvv)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences (PHBA §A.1.1: packed inputs reset state at every sequence
+# boundary; §A.1.2: block boundaries from cu and the block size, means over
+# valid rows, routes inside the same sequence, -1 where nothing is
+# available; reading R16)
+# ---------------------------------------------------------------------------
+
+def packed_spans(cu) -> list[tuple[int, int]]:
+    """(first row, length) of every sequence: sequence s owns rows [cu[s], cu[s+1])."""
+    cu = [int(x) for x in cu]
+    return [(cu[s], cu[s + 1] - cu[s]) for s in range(len(cu) - 1)]
+
+
+def packed_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu, max_len: int, block: int,
+                   branching: int, top_k: int, scale: float | None = None):
+    """The whole path on a packed batch, one sequence at a time.
+
+    q [Hq, total, d]; k, v [Hk, total, d]; cu the batch+1 row offsets;
+    max_len bounds every length and fixes the route table's query-block axis.
+    Every sequence runs alone as a batch-1 problem of its own length
+    (build_pyramid, select, attention).  Returns a dict with
+      o [Hq, total, d], lse [Hq, total]   float64, NaN on rows of no sequence
+      sel [S, Hk, ceil(max_len/block), K+1]   int64, -1 past each sequence
+      levels   per sequence, the oracle pyramid levels ([1, Hk, n_l, d] each)
+    """
+    Hq, total, d = q.shape
+    Hk = k.shape[0]
+    spans = packed_spans(cu)
+    nqb_max = -(-max_len // block)
+    o = np.full((Hq, total, d), np.nan)
+    lse = np.full((Hq, total), np.nan)
+    sel = np.full((len(spans), Hk, nqb_max, top_k + 1), -1, dtype=np.int64)
+    levels = []
+    for s, (a, n) in enumerate(spans):
+        if n > max_len:
+            raise ValueError(f"sequence {s} has {n} rows, more than max_len {max_len}")
+        if n == 0:
+            levels.append([])
+            continue
+        qs = np.asarray(q[None, :, a:a + n, :], dtype=np.float64)
+        ks = np.asarray(k[None, :, a:a + n, :], dtype=np.float64)
+        vs = np.asarray(v[None, :, a:a + n, :], dtype=np.float64)
+        lv = build_pyramid(ks, block, branching)
+        ss, _ = select(qs, lv, n, block, branching, top_k, scale)
+        oo, ll = attention(qs, ks, vs, ss, block, scale)
+        o[:, a:a + n, :] = oo[0]
+        lse[:, a:a + n] = ll[0]
+        sel[s, :, :ss.shape[2], :] = ss[0]
+        levels.append(lv)
+    return dict(o=o, lse=lse, sel=sel, levels=levels)

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     assert {"pyr_build_pyramid", "pyr_select_topk", "pyr_block_sparse_attn"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert H.pyr_abi_version() == 2
+    assert H.pyr_abi_version() == 3
 
 
 def test_single_hip_runtime_in_process():
@@ -246,3 +246,81 @@ def test_backward_rejects_capacity():
     p = _p(kv_capacity=8192)
     s, msg = _bwd(p, [ptr] * 10, ptr, 1 << 40)
     assert s == 3 and "capacity" in msg
+
+
+def _packed_c(total=1000, **kw):
+    """The C problem of a packed batch of 3 sequences; cu is a stand-in device
+    address (validation never dereferences it)."""
+    kw = dict(dict(batch=3, q_len=512, kv_len=512), **kw)
+    c = _p(**kw).c()
+    c.cu = 64
+    c.total_len = total
+    return c
+
+
+def test_packed_geometry():
+    """A packed problem has the layout of a dense one of length kv_len (the
+    bound on every sequence's length)."""
+    c = _packed_c()
+    dense = _p(batch=3, q_len=512, kv_len=512)
+    lib = H.lib()
+    assert lib.pyr_num_levels(ctypes.byref(c)) == H.pyr_num_levels(dense)
+    assert lib.pyr_pyramid_nodes(ctypes.byref(c)) == H.pyr_pyramid_nodes(dense)
+    assert lib.pyr_num_query_blocks(ctypes.byref(c)) == 8
+    assert lib.pyr_attn_workspace_bytes(ctypes.byref(c)) == 0
+    assert lib.pyr_attn_bwd_workspace_bytes(ctypes.byref(c)) == 0
+
+
+def test_packed_validation():
+    ptr = ctypes.c_void_p(16)
+    cases = [
+        (_packed_c(q_len=1, kv_len=512), 3, "q_len == kv_len"),
+        (_packed_c(kv_capacity=1024), 3, "kv_capacity"),
+        (_packed_c(total=-1), 2, "total_len"),
+    ]
+    c = _packed_c()
+    c.cu = 66
+    cases.append((c, 4, "cu"))
+    c = _p().c()
+    c.total_len = 10
+    cases.append((c, 2, "total_len"))
+    for c, status, word in cases:
+        s, msg = _status("pyr_build_pyramid", ctypes.byref(c), ptr, ptr, None)
+        assert s == status and word in msg, (s, msg)
+    c = _packed_c()
+    s, msg = _status("pyr_append_pyramid", ctypes.byref(c), ptr, 10, ptr, None)
+    assert s == 3 and "packed" in msg
+    s, msg = _status("pyr_block_sparse_attn_bwd", ctypes.byref(c), *([ptr] * 10), ptr, 1 << 40, None)
+    assert s == 3 and "packed" in msg
+
+
+def test_packed_empty_is_noop():
+    c = ctypes.byref(_packed_c(total=0))
+    assert _status("pyr_build_pyramid", c, None, None, None)[0] == 0
+    assert _status("pyr_select_topk", c, None, None, None, None, None, None)[0] == 0
+    assert _status("pyr_block_sparse_attn", c, None, None, None, None, None, None, None, 0,
+                   None)[0] == 0
+
+
+def test_packed_binding_shapes(monkeypatch):
+    """The binding expects [H, total, d] tensors, [H, total] lse and batch+1
+    offsets for a packed problem, and checks them before calling the library."""
+    orig = B._expect
+    monkeypatch.setattr(B, "_expect", lambda t, n, s, d, device_type="cuda": orig(t, n, s, d, "cpu"))
+    cu = torch.tensor([0, 100, 300], dtype=torch.int32)
+    q = torch.zeros((4, 300, 128), dtype=torch.bfloat16)
+    k = torch.zeros((2, 300, 128), dtype=torch.bfloat16)
+    p = H.problem_for_packed(q, k, cu, 256, 4, 8)
+    assert (p.batch, p.total_len, p.q_len, p.kv_len) == (2, 300, 256, 256)
+    assert p.q_shape == (4, 300, 128) and p.kv_shape == (2, 300, 128) and p.lse_shape == (4, 300)
+    with pytest.raises(ValueError, match="k: shape"):
+        H.pyr_build_pyramid(p, k[:, :200], torch.zeros(H.pyramid_shape(p)))
+    with pytest.raises(ValueError, match="cu: shape"):
+        H.pyr_build_pyramid(H.Problem(**{**p.__dict__, "cu": cu[:2]}), k,
+                            torch.zeros(H.pyramid_shape(p)))
+    with pytest.raises(ValueError, match="cu: dtype"):
+        H.pyr_build_pyramid(H.Problem(**{**p.__dict__, "cu": cu.long()}), k,
+                            torch.zeros(H.pyramid_shape(p)))
+    sel = torch.zeros((2, 2, 4, 9), dtype=torch.int32)
+    with pytest.raises(ValueError, match="lse: shape"):
+        H.pyr_block_sparse_attn(p, q, k, k, sel, q, torch.zeros((4, 2, 150)))
