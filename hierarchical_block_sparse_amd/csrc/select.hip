@@ -39,7 +39,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 32;   // candidates per LDS chunk (MFMA path): two 16-wide N tiles
 constexpr int kZbuf = 8192;  // fp32 scratch for the generic path
-constexpr int kSelStages = 3;  // candidate chunks in LDS (MFMA path): one computing, two loading
+constexpr int kSelStages = 2;  // candidate chunks in LDS (MFMA path): one scored while one loads
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -60,9 +60,7 @@ struct SelLayout {
     if (mfma) {
       off_part = o;  o += 8 * kWaves * cmax;                // float2 [wave][candidate]
       off_misc = o;  o += 4 * (PYR_MAX_LEVELS + 4);         // int ancestors, kept count
-      o = (o + 15) & ~15;
-      off_hl = o;    o += kSelStages * kChunk * 4 * D;      // bf16 [stage][cand][hi, lo][D]
-      off_zbuf = o;
+      off_hl = off_zbuf = o;
     } else {
       off_part = off_hl = off_misc = o;
       off_zbuf = o;  o += 4 * kZbuf;
@@ -267,6 +265,8 @@ __device__ void blank_unit(const PyrGeom& g, int64_t unit, int32_t* sel, int32_t
 // ---------------------------------------------------------------------------
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
 
 // Split rows of chunk c's candidates (plane 1 of the pyramid: per node a bf16
 // hi row and a bf16 lo row, 4D bytes) into one LDS stage with direct 16-byte
@@ -345,8 +345,9 @@ __device__ __forceinline__ void tile_lse(const f32x4 (&acc)[MT], uint32_t rowval
   s = sum32(sum16(s));
 }
 
+// Four M tiles (G = 4) fit 168 VGPRs, so three workgroups share a CU.
 template <int D, int MT>
-__global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict__ q,
+__global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const bf16_t* __restrict__ q,
                                                         const float* __restrict__ pyr,
                                                         int32_t* __restrict__ sel,
                                                         int32_t* __restrict__ trace_ids,
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
   constexpr int CPR = D / 8;                               // 16-byte chunks per bf16 row
   constexpr int STAGE = kChunk * 4 * D;                    // bytes per LDS stage
   constexpr int PER = kChunk * 2 * CPR / kThreads;         // chunk loads per thread
-  constexpr int WAIT_ONE = 0x0F70 | (PER & 15) | ((PER >> 4) << 14);  // vmcnt(PER)
+
   // All LDS is the one dynamic array: with a second __shared__ variable the
   // compiler would give each its own alias scope and wait for every chunk load
   // in flight before any LDS read, undoing the prefetch.
@@ -366,10 +367,12 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
   int* cand = reinterpret_cast<int*>(smem + lay.off_cand);
   float* score = reinterpret_cast<float*>(smem + lay.off_score);
   int* rank = reinterpret_cast<int*>(smem + lay.off_rank);
-  float2* part = reinterpret_cast<float2*>(smem + lay.off_part);
+  lds_f32x2* part = (lds_f32x2*)(smem + lay.off_part);
   int* s_anc = reinterpret_cast<int*>(smem + lay.off_misc);
   int& s_nkept = s_anc[PYR_MAX_LEVELS];
-  unsigned char* stages = smem + lay.off_hl;
+  // the candidate stages are an array of their own: LDS writes to the dynamic
+  // area then do not wait for the stage loads in flight
+  __shared__ __attribute__((aligned(16))) unsigned char stages[kSelStages * kChunk * 4 * D];
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -426,63 +429,45 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
     }
     const unsigned char* lvl = split + g.loff[level] * 4 * D;
     const int nchunks = (C + kChunk - 1) / kChunk;
-    // chunks c and c+1 load while chunk c-1 is scored; stage of chunk c is c % 3
+    // chunk c+1 loads while chunk c is scored; stage of chunk c is c % 2
     issue_chunk<D>(lvl, cand, C, 0, stages, w, l);
-    if (nchunks > 1) issue_chunk<D>(lvl, cand, C, 1, stages + STAGE, w, l);
-    // Chunks go in groups of four whose per-tile partials stay in registers
-    // until the group ends: an LDS write while chunk loads are in flight
-    // would make the compiler wait for all of them.
-    for (int c0 = 0; c0 < nchunks; c0 += 4) {
-      float2 pbuf[8];
+    for (int c = 0; c < nchunks; ++c) {
+      // this wave's loads of chunk c have landed; after the barrier every
+      // wave's have, and the stage of chunk c-1 is free
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      lds_barrier();
+      if (c + 1 < nchunks)
+        issue_chunk<D>(lvl, cand, C, c + 1, stages + ((c + 1) % kSelStages) * STAGE, w, l);
+      const unsigned char* st = stages + (c % kSelStages) * STAGE;
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg) {
-        const int c = c0 + cg;
-        if (c >= nchunks) break;  // uniform
-        // this wave's loads of chunk c have landed once at most those of
-        // chunk c+1 are outstanding; after the barrier every wave's have, and
-        // the stage of chunk c-1 is free
-        if (c + 1 < nchunks)
-          __builtin_amdgcn_s_waitcnt(WAIT_ONE);
-        else
-          __builtin_amdgcn_s_waitcnt(0x0F70);
-        lds_barrier();
-        if (c + 2 < nchunks)
-          issue_chunk<D>(lvl, cand, C, c + 2, stages + ((c + 2) % kSelStages) * STAGE, w, l);
-        const unsigned char* st = stages + (c % kSelStages) * STAGE;
+      for (int nt = 0; nt < kChunk / 16; ++nt) {
+        if (c * kChunk + nt * 16 >= C) break;  // uniform
+        f32x4 acc[MT];
 #pragma unroll
-        for (int nt = 0; nt < kChunk / 16; ++nt) {
-          if (c * kChunk + nt * 16 >= C) break;  // uniform
-          f32x4 acc[MT];
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // B fragment: candidate r = nt*16 + l%16, logical chunk 4*ks + l/16
+        // of its hi and lo rows, stored at that chunk ^ (r % CPR)
+        const int r = nt * 16 + (l % 16);
+        const unsigned char* row = st + r * 4 * D;
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          // B fragment: candidate r = nt*16 + l%16, logical chunk 4*ks + l/16
-          // of its hi and lo rows, stored at that chunk ^ (r % CPR)
-          const int r = nt * 16 + (l % 16);
-          const unsigned char* row = st + r * 4 * D;
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const int off = ((4 * ks + l / 16) ^ (r % CPR)) << 4;
+          const bf16x8 bhv = as_bf16x8(*reinterpret_cast<const uint4*>(row + off));
+          const bf16x8 blv = as_bf16x8(*reinterpret_cast<const uint4*>(row + 2 * D + off));
 #pragma unroll
-          for (int ks = 0; ks < D / 32; ++ks) {
-            const int off = ((4 * ks + l / 16) ^ (r % CPR)) << 4;
-            const bf16x8 bhv = as_bf16x8(*reinterpret_cast<const uint4*>(row + off));
-            const bf16x8 blv = as_bf16x8(*reinterpret_cast<const uint4*>(row + 2 * D + off));
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), bhv, acc[mt], 0, 0, 0);
-              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), blv, acc[mt], 0, 0, 0);
-            }
+          for (int mt = 0; mt < MT; ++mt) {
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), bhv, acc[mt], 0, 0, 0);
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), blv, acc[mt], 0, 0, 0);
           }
-          // this wave's LogSumExp over its rows, per candidate (lane column l % 16)
-          float m, s;
-          if (full)
-            tile_lse<MT, true>(acc, rowvalid, sl2, m, s);
-          else
-            tile_lse<MT, false>(acc, rowvalid, sl2, m, s);
-          pbuf[cg * 2 + nt] = make_float2(m, s);
         }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int cn = c0 * kChunk + e * 16;
-        if (cn < C && l < 16) part[w * cmax + cn + l] = pbuf[e];
+        // this wave's LogSumExp over its rows, per candidate (lane column l % 16)
+        float m, s;
+        if (full)
+          tile_lse<MT, true>(acc, rowvalid, sl2, m, s);
+        else
+          tile_lse<MT, false>(acc, rowvalid, sl2, m, s);
+        const int cn = c * kChunk + nt * 16 + l;
+        if (l < 16 && cn < C) part[w * cmax + cn] = f32x2{m, s};
       }
     }
     __syncthreads();
@@ -490,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void select_mfma(const bf16_t* __restrict
       float m = -INFINITY, s = 0.f;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
-        const float2 p = part[ww * cmax + j];
+        const f32x2 p = part[ww * cmax + j];
         lse2_merge(m, s, p.x, p.y);
       }
       const float sc = (m + log2f(s)) * PYR_LN2;
@@ -636,7 +621,10 @@ hipError_t launch_select_d(const PyrGeom& g, int dtype, const void* q, const flo
 }  // namespace
 
 size_t pyr_select_lds_bytes(const PyrGeom& g, int dtype) {
-  return SelLayout(g.K, g.branching, g.D, mfma_tiles(g, dtype) != 0).total;
+  const bool mfma = mfma_tiles(g, dtype) != 0;
+  // dynamic layout, plus the candidate stages of the MFMA path (a static array)
+  return SelLayout(g.K, g.branching, g.D, mfma).total +
+         (mfma ? (size_t)kSelStages * kChunk * 4 * g.D : 0);
 }
 
 hipError_t pyr_launch_select(const PyrGeom& g, int dtype, const void* q, const float* pyr,
