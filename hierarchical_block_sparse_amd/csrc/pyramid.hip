@@ -16,9 +16,9 @@
 //    (16-byte loads, several blocks in flight per thread), reduces each block
 //    to its mean, then folds the chunk's nodes up s levels inside LDS.  This is
 //    the HBM-bound pass: every key byte is read exactly once.
-//  * build_top: one workgroup per (batch, KV head) folds the remaining levels
-//    (above level s) from the nodes in the output slab; these are a few
-//    hundred KiB at most and stay in L2.
+//  * build_level: one launch per remaining level (above level s), one thread
+//    per (node, column) of every slab, reading the children from the output
+//    slab (a few hundred KiB at most, in L2).
 // A parent is the token-weighted mean of its children, so a ragged last block
 // or a ragged last node gives the exact token mean.
 #include "pyr_device.h"
@@ -147,37 +147,39 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void build_top(float* __restrict__ pyr, PyrGeom g,
-                                                      int first_level) {
-  float* slab = pyr + (int64_t)blockIdx.x * g.planes * g.n_tot * D;
-  const int b = g.branching;
-  const PyrSeq sq = pyr_seq(g, (int)(blockIdx.x / g.Hk));
-  if (sq.nb == 0) return;
-  // valid nodes one level below first_level (one node above the root)
-  int n_below = sq.nb;
-  for (int lvl = 1; lvl < first_level; ++lvl) n_below = n_below > 1 ? (n_below + b - 1) / b : 1;
-  for (int lvl = first_level; lvl < g.L; ++lvl) {
-    const int n_here = n_below > 1 ? (n_below + b - 1) / b : 1;
-    const float* below = slab + g.loff[lvl - 1] * D;
+// Valid nodes of level `lvl` for a sequence of nb blocks (one above its root).
+__device__ __forceinline__ int64_t level_valid(int64_t nb, int b, int lvl) {
+  for (int l = 0; l < lvl; ++l) nb = nb > 1 ? (nb + b - 1) / b : 1;
+  return nb;
+}
 
-    for (int idx = threadIdx.x; idx < n_here * D; idx += kThreads) {
-      const int m = idx / D, dcol = idx % D;
-      float num = 0.f, den = 0.f;
-      for (int j = 0; j < b; ++j) {
-        const int64_t cidx = (int64_t)m * b + j;
-        if (cidx < n_below) {
-          const float w = (float)pyr_node_tokens(sq.Tk, b, lvl - 1, cidx);
-          num += below[cidx * D + dcol] * w;
-          den += w;
-        }
-      }
-      put_node<D>(g, slab, g.loff[lvl] + m, dcol, num / den);
+// One level above the chunks: one thread per (node, column), nodes of every
+// slab spread over the whole grid (a level is one launch, the launches of
+// consecutive levels are ordered by the stream).
+template <int D>
+__global__ __launch_bounds__(kThreads) void build_level(float* __restrict__ pyr, PyrGeom g,
+                                                        int lvl, int wg_per_bh) {
+  const int64_t bh = blockIdx.x / wg_per_bh;
+  const int64_t idx = (int64_t)(blockIdx.x % wg_per_bh) * kThreads + threadIdx.x;
+  const PyrSeq sq = pyr_seq(g, (int)(bh / g.Hk));
+  const int b = g.branching;
+  const int64_t n_below = level_valid(sq.nb, b, lvl - 1);
+  const int64_t n_here = sq.nb ? level_valid(sq.nb, b, lvl) : 0;
+  const int64_t m = idx / D;
+  if (m >= n_here) return;
+  const int dcol = (int)(idx % D);
+  float* slab = pyr + bh * g.planes * g.n_tot * D;
+  const float* below = slab + g.loff[lvl - 1] * D;
+  float num = 0.f, den = 0.f;
+  for (int j = 0; j < b; ++j) {
+    const int64_t cidx = m * b + j;
+    if (cidx < n_below) {
+      const float w = (float)pyr_node_tokens(sq.Tk, b, lvl - 1, cidx);
+      num += below[cidx * D + dcol] * w;
+      den += w;
     }
-    __threadfence_block();
-    __syncthreads();
-    n_below = n_here;
   }
+  put_node<D>(g, slab, g.loff[lvl] + m, dcol, num / den);
 }
 
 __device__ __forceinline__ float key_f32(float x) { return x; }
@@ -268,9 +270,10 @@ hipError_t launch_build_t(const PyrGeom& g, const void* k, float* pyr, hipStream
                      chunks_per_bh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (s + 1 < g.L) {
-    hipLaunchKernelGGL((build_top<D>), dim3((unsigned)n_bh), dim3(kThreads), 0, st, pyr, g,
-                       s + 1);
+  for (int lvl = s + 1; lvl < g.L && e == hipSuccess; ++lvl) {
+    const int64_t wg = ((int64_t)g.lsize[lvl] * D + kThreads - 1) / kThreads;  // longest sequence
+    hipLaunchKernelGGL((build_level<D>), dim3((unsigned)(n_bh * wg)), dim3(kThreads), 0, st, pyr,
+                       g, lvl, (int)wg);
     e = hipGetLastError();
   }
   return e;
