@@ -66,6 +66,10 @@ def lib():
             ("pyr_build_pyramid", st, [P, vp, vp, vp]),
             ("pyr_append_pyramid", st, [P, vp, ctypes.c_int64, vp, vp]),
             ("pyr_select_topk", st, [P, vp, vp, vp, vp, vp, vp]),
+            ("pyr_select_topk_budgets", st,
+             [P, vp, vp, vp, ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp]),
+            ("pyr_budgets_from_entropy", st,
+             [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]),
             ("pyr_block_sparse_attn", st, [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
             ("pyr_attn_bwd_workspace_bytes", ctypes.c_size_t, [P]),
             ("pyr_block_sparse_attn_bwd", st,
@@ -240,6 +244,33 @@ def pyr_select_topk(p: Problem, q, pyramid, sel, trace_ids=None, trace_scores=No
             torch.float32)
     _check(lib().pyr_select_topk(_cp(p), _ptr(q), _ptr(pyramid), _ptr(sel),
                                  _ptr(trace_ids), _ptr(trace_scores), _stream(stream)))
+
+
+def pyr_select_topk_budgets(p: Problem, q, pyramid, sel, k_head=None, fallback_k: int = 0,
+                            fallback_margin: float = 0.0, trace_ids=None, trace_scores=None,
+                            stream=None):
+    """Selection with per-KV-head budgets k_head (int32 [Hk] on the device, or
+    None) and a finest-level confidence fallback to fallback_k blocks."""
+    nqb, L = pyr_num_query_blocks(p), pyr_num_levels(p)
+    _expect(q, "q", p.q_shape, p.dtype)
+    _expect(pyramid, "pyramid", pyramid_shape(p), torch.float32)
+    _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
+    _expect(k_head, "k_head", (p.n_kv_heads,), torch.int32)
+    _expect(trace_ids, "trace_ids", (p.batch, p.n_kv_heads, nqb, L, p.top_k), torch.int32)
+    _expect(trace_scores, "trace_scores", (p.batch, p.n_kv_heads, nqb, L, p.top_k + 1),
+            torch.float32)
+    _check(lib().pyr_select_topk_budgets(_cp(p), _ptr(q), _ptr(pyramid), _ptr(k_head),
+                                         int(fallback_k), float(fallback_margin), _ptr(sel),
+                                         _ptr(trace_ids), _ptr(trace_scores), _stream(stream)))
+
+
+def pyr_budgets_from_entropy(entropy, total: int, k_min: int, k_max: int) -> list[int]:
+    """Per-head budgets in proportion to head entropy (host-only)."""
+    n = len(entropy)
+    ent = (ctypes.c_float * max(n, 1))(*[float(x) for x in entropy])
+    out = (ctypes.c_int32 * max(n, 1))()
+    _check(lib().pyr_budgets_from_entropy(ent, n, int(total), int(k_min), int(k_max), out))
+    return [int(out[i]) for i in range(n)]
 
 
 def pyr_block_sparse_attn(p: Problem, q, k, v, sel, o, lse=None, workspace=None, stream=None):

@@ -135,6 +135,22 @@ pyr_status hip_status(hipError_t e, const char* what) {
   return fail(PYR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+pyr_status select_checked(const PyrGeom& g, int dtype, const void* q, const float* pyramid,
+                          int32_t* sel, int32_t* trace_ids, float* trace_scores,
+                          hipStream_t stream) {
+  const bool empty = (int64_t)g.B * g.Hk * g.nqb == 0 || g.Tq == 0 || (g.cu && g.Tqs == 0);
+  if (!empty && (!q || !pyramid || !sel)) return fail(PYR_ERR_NULL, "q, pyramid or sel is NULL");
+  if (!empty && (!aligned16(q) || !aligned16(pyramid) || !aligned16(sel) ||
+                 (trace_ids && !aligned16(trace_ids)) || (trace_scores && !aligned16(trace_scores))))
+    return fail(PYR_ERR_MISALIGNED, "tensors must be 16-byte aligned");
+  if (empty) return PYR_OK;
+  if (pyr_select_lds_bytes(g, dtype) > 160 * 1024)
+    return fail(PYR_ERR_UNSUPPORTED, "selection needs %zu bytes of LDS (> 160 KiB)",
+                pyr_select_lds_bytes(g, dtype));
+  return hip_status(pyr_launch_select(g, dtype, q, pyramid, sel, trace_ids, trace_scores, stream),
+                    "pyr_select_topk launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,17 +207,27 @@ pyr_status pyr_select_topk(const pyr_problem* p, const void* q, const float* pyr
   PyrGeom g;
   pyr_status s = resolve(p, &g);
   if (s != PYR_OK) return s;
-  const bool empty = (int64_t)g.B * g.Hk * g.nqb == 0 || g.Tq == 0 || (g.cu && g.Tqs == 0);
-  if (!empty && (!q || !pyramid || !sel)) return fail(PYR_ERR_NULL, "q, pyramid or sel is NULL");
-  if (!empty && (!aligned16(q) || !aligned16(pyramid) || !aligned16(sel) ||
-                 (trace_ids && !aligned16(trace_ids)) || (trace_scores && !aligned16(trace_scores))))
-    return fail(PYR_ERR_MISALIGNED, "tensors must be 16-byte aligned");
-  if (empty) return PYR_OK;
-  if (pyr_select_lds_bytes(g, p->dtype) > 160 * 1024)
-    return fail(PYR_ERR_UNSUPPORTED, "selection needs %zu bytes of LDS (> 160 KiB)",
-                pyr_select_lds_bytes(g, p->dtype));
-  return hip_status(pyr_launch_select(g, p->dtype, q, pyramid, sel, trace_ids, trace_scores, stream),
-                    "pyr_select_topk launch");
+  return select_checked(g, p->dtype, q, pyramid, sel, trace_ids, trace_scores, stream);
+}
+
+pyr_status pyr_select_topk_budgets(const pyr_problem* p, const void* q, const float* pyramid,
+                                   const int32_t* k_head, int32_t fallback_k,
+                                   float fallback_margin, int32_t* sel, int32_t* trace_ids,
+                                   float* trace_scores, hipStream_t stream) {
+  g_err[0] = 0;
+  PyrGeom g;
+  pyr_status s = resolve(p, &g);
+  if (s != PYR_OK) return s;
+  if (fallback_k < 0 || fallback_k > g.K)
+    return fail(PYR_ERR_INVALID, "fallback_k %d outside [0, top_k = %d]", fallback_k, g.K);
+  if (isnan(fallback_margin) || isinf(fallback_margin))
+    return fail(PYR_ERR_INVALID, "fallback_margin must be finite");
+  if (k_head && (reinterpret_cast<uintptr_t>(k_head) & 3u))
+    return fail(PYR_ERR_MISALIGNED, "k_head must be 4-byte aligned");
+  g.k_head = k_head;
+  g.fb_k = fallback_k;
+  g.fb_margin = fallback_margin;
+  return select_checked(g, p->dtype, q, pyramid, sel, trace_ids, trace_scores, stream);
 }
 
 pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void* k,
@@ -286,6 +312,30 @@ pyr_status pyr_block_sparse_attn_bwd(const pyr_problem* p, const void* q, const 
   if (empty) return PYR_OK;
   return hip_status(pyr_launch_attn_bwd(g, q, k, v, sel, o, lse, dout, dq, dk, dv, workspace, stream),
                     "pyr_block_sparse_attn_bwd launch");
+}
+
+pyr_status pyr_budgets_from_entropy(const float* entropy, int32_t n_heads, int32_t total,
+                                    int32_t k_min, int32_t k_max, int32_t* k_out) {
+  g_err[0] = 0;
+  if (n_heads < 0) return fail(PYR_ERR_INVALID, "n_heads %d < 0", n_heads);
+  if (n_heads == 0) return PYR_OK;
+  if (!entropy || !k_out) return fail(PYR_ERR_NULL, "entropy or k_out is NULL");
+  if (k_min < 1 || k_max < k_min)
+    return fail(PYR_ERR_INVALID, "need 1 <= k_min <= k_max (k_min %d, k_max %d)", k_min, k_max);
+  if (total < 0) return fail(PYR_ERR_INVALID, "total %d < 0", total);
+  double sum = 0.0;
+  for (int32_t h = 0; h < n_heads; ++h) {
+    if (!(entropy[h] >= 0.f) || isinf(entropy[h]))
+      return fail(PYR_ERR_INVALID, "entropy[%d] must be finite and >= 0", h);
+    sum += entropy[h];
+  }
+  for (int32_t h = 0; h < n_heads; ++h) {
+    const double share = sum > 0.0 ? (double)total * entropy[h] / sum : (double)total / n_heads;
+    double k = floor(share + 0.5);
+    k = k < k_min ? k_min : (k > k_max ? k_max : k);
+    k_out[h] = (int32_t)k;
+  }
+  return PYR_OK;
 }
 
 const char* pyr_status_string(pyr_status s) {

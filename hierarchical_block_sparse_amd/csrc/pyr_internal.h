@@ -14,6 +14,9 @@ struct PyrGeom {
   int64_t Tks;             // rows per head in k and v: the capacity (or Tk); packed: all rows
   int64_t Tqs;             // rows per head in q, o and lse: Tq; packed: all rows
   const int32_t* cu;       // packed sequences: device row offsets [B + 1]; dense: null
+  const int32_t* k_head;   // selection budgets per KV head (device, [Hk]); null: K everywhere
+  float fb_margin;         // finest-level confidence margin below which fb_k blocks are kept
+  int32_t fb_k;            // fallback budget (0: no fallback)
   int64_t n_tot;           // pyramid nodes per (batch, KV head) slab
   int32_t planes;          // pyramid planes: 1 (fp32 problems) or 2 (bf16: + hi/lo split)
   int32_t B, Hq, Hk, G, D; // batch, heads, group size Hq/Hk, head dim

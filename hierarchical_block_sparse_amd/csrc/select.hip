@@ -126,19 +126,21 @@ __device__ __forceinline__ void keep_chunk(int j, uint32_t kj, int C, uint32_t T
   ties += __popcll(em);
 }
 
-// Keep the top K of C > K candidates in ascending index order and write the
+// Keep the top K of C >= K candidates in ascending index order and write the
 // trace.  Candidates are ascending by node index, so "lower index wins a tie"
 // is "lower position wins": the kept set is every candidate with a score above
 // the K-th largest, T, plus the first (by position) of those equal to T until
 // there are K.  Wave 0 finds T two bits at a time (the largest key with at
 // least K keys >= it) with ballots over the candidates, four per lane in
 // registers (more are re-read from LDS), then compacts the kept set in index
-// order.
+// order.  *margin gets the K-th best score minus the best rejected one (NaN
+// when nothing is rejected).  The trace row is g.K wide: slots past K hold -1
+// (ids) and NaN (scores), slot g.K of the scores the best rejected score.
 __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* cand,
                                 const float* score, int* rank, int* kept, float* kscore,
-                                int* nkept, int32_t* tr_ids, float* tr_scores) {
+                                int* nkept, int K, float* margin, int32_t* tr_ids,
+                                float* tr_scores) {
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
-  const int K = g.K;
   const int nch = (C + 63) / 64;
   if (w == 0) {
     uint32_t kr[4];
@@ -192,17 +194,39 @@ __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* c
       rej = r2 > rej ? r2 : rej;
     }
     if (l == 0) {
-      if (tr_scores) tr_scores[level * (K + 1) + K] = key_score(rej);  // best rejected candidate
+      if (tr_scores) tr_scores[level * (g.K + 1) + g.K] = key_score(rej);  // best rejected
+      *margin = key_score(T) - key_score(rej);
       *nkept = K;
     }
   }
   __syncthreads();
   if (tr_ids) {
-    for (int j = tid; j < K; j += kThreads) tr_ids[level * K + j] = kept[j];
+    for (int j = tid; j < g.K; j += kThreads) tr_ids[level * g.K + j] = j < K ? kept[j] : -1;
   }
   if (tr_scores) {
-    for (int j = tid; j < K; j += kThreads) tr_scores[level * (K + 1) + j] = kscore[j];
+    for (int j = tid; j < g.K; j += kThreads)
+      tr_scores[level * (g.K + 1) + j] = j < K ? kscore[j] : NAN;
   }
+}
+
+// Nodes kept per level for the units of KV head hk: the head's budget when
+// budgets are given (clamped to [1, K]), else K.
+__device__ __forceinline__ int unit_budget(const PyrGeom& g, int hk) {
+  if (!g.k_head) return g.K;
+  const int k = g.k_head[hk];
+  return k < 1 ? 1 : (k > g.K ? g.K : k);
+}
+
+// Confidence fallback, decided after the finest level's top-Ku: when the
+// margin between the Ku-th best score and the best rejected one is below
+// g.fb_margin, the level is ranked again keeping the best g.fb_k candidates
+// (all of them if there are fewer).  Must be called by every thread; the
+// result is uniform.
+__device__ __forceinline__ bool fallback_due(const PyrGeom& g, int level, int kk, int Ku,
+                                             const float* margin) {
+  if (level != 0 || kk != Ku || g.fb_k <= Ku) return false;
+  __syncthreads();  // the trace of the first pass has read kept[]; *margin is visible
+  return *margin < g.fb_margin;
 }
 
 // Candidates of one level into cand[]; returns the count.  Must be called by
@@ -370,6 +394,7 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
   lds_f32x2* part = (lds_f32x2*)(smem + lay.off_part);
   int* s_anc = reinterpret_cast<int*>(smem + lay.off_misc);
   int& s_nkept = s_anc[PYR_MAX_LEVELS];
+  float* s_margin = reinterpret_cast<float*>(s_anc + PYR_MAX_LEVELS + 1);
   // the candidate stages are an array of their own: LDS writes to the dynamic
   // area then do not wait for the stage loads in flight
   __shared__ __attribute__((aligned(16))) unsigned char stages[kSelStages * kChunk * 4 * D];
@@ -387,6 +412,7 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
     return;
   }
   const int diag = i;
+  const int Ku = unit_budget(g, hk);
   const int RW = MT * 16;  // rows per wave
   const float sl2 = g.scale * PYR_LOG2E;
   const int cmax = lay.cmax;
@@ -423,7 +449,7 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
 
   for (int level = g.L - 1; level >= 0; --level) {
     const int C = build_candidates(g, level, s_anc, kept, s_nkept, cand);
-    if (C <= g.K) {
+    if (C <= Ku) {
       keep_all(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
       continue;
     }
@@ -482,7 +508,12 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
       score[j] = sc == sc ? sc : -INFINITY;  // a NaN score ranks last
     }
     __syncthreads();
-    top_k_and_trace(g, C, level, cand, score, rank, kept, kscore, &s_nkept, tr_ids, tr_sc);
+    for (int kk = Ku;;) {
+      top_k_and_trace(g, C, level, cand, score, rank, kept, kscore, &s_nkept, kk, s_margin,
+                      tr_ids, tr_sc);
+      if (!fallback_due(g, level, kk, Ku, s_margin)) break;
+      kk = C < g.fb_k ? C : g.fb_k;  // keep more of the same candidates
+    }
   }
   write_route(g, unit, kept, s_nkept, diag, sel);
 }
@@ -507,6 +538,7 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
   int* rank = reinterpret_cast<int*>(smem + lay.off_rank);
   float* zbuf = reinterpret_cast<float*>(smem + lay.off_zbuf);
   __shared__ int s_nkept;
+  __shared__ float s_margin[1];
   __shared__ int s_anc[PYR_MAX_LEVELS];
 
   const int tid = threadIdx.x;
@@ -532,6 +564,7 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
     diag = i;
   }
   const int R = (int)(g.G * ntok);
+  const int Ku = unit_budget(g, hk);
   const float sl2 = g.scale * PYR_LOG2E;
   const float* slab = pyr + bhk * g.planes * g.n_tot * D;  // plane 0: fp32 means
   int32_t* tr_ids = trace_ids ? trace_ids + unit * g.L * g.K : nullptr;
@@ -543,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
 
   for (int level = g.L - 1; level >= 0; --level) {
     const int C = build_candidates(g, level, s_anc, kept, s_nkept, cand);
-    if (C <= g.K) {
+    if (C <= Ku) {
       keep_all(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
       continue;
     }
@@ -576,7 +609,12 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
       }
       __syncthreads();
     }
-    top_k_and_trace(g, C, level, cand, score, rank, kept, kscore, &s_nkept, tr_ids, tr_sc);
+    for (int kk = Ku;;) {
+      top_k_and_trace(g, C, level, cand, score, rank, kept, kscore, &s_nkept, kk, s_margin,
+                      tr_ids, tr_sc);
+      if (!fallback_due(g, level, kk, Ku, s_margin)) break;
+      kk = C < g.fb_k ? C : g.fb_k;  // keep more of the same candidates
+    }
   }
   write_route(g, unit, kept, s_nkept, diag, sel);
 }

@@ -180,6 +180,42 @@ pyr_status pyr_select_topk(const pyr_problem* p, const void* q, const float* pyr
                            int32_t* sel, int32_t* trace_ids, float* trace_scores,
                            hipStream_t stream);
 
+/* Selection with per-head budgets and a confidence fallback (PHAROS, zensar.com
+ * summary: token budgets differ between attention heads (depth-sounding budget
+ * allocation) and the budget grows when the selection is not confident (fog
+ * gate confidence fallback); the page gives no formulas, so the two rules
+ * below are this library's).  Same as pyr_select_topk except:
+ *   k_head        NULL (every unit keeps K nodes per level) or a DEVICE array
+ *                 [Hk] int32: units of KV head hk keep K_h = k_head[hk] nodes
+ *                 per level, clamped to [1, K] on the device  (input)
+ *   fallback_k    0 (no fallback) or F in [1, K]: when the finest level was
+ *                 scored (more than K_h candidates) and its margin -- the K_h-th
+ *                 best score minus the best rejected score, natural-log
+ *                 LogSumExp units -- is below fallback_margin, the unit keeps
+ *                 the best min(F, candidates) of that level instead; F <= K_h
+ *                 has no effect
+ *   fallback_margin  finite; a margin below it triggers the fallback
+ * Route rows keep their K+1 slots (kept blocks, diagonal, -1 padding); trace
+ * rows list K_h ids per level (F at a finest level that fell back), -1 and
+ * NaN after them.  The margin is computed from the kernel's fp32 scores, so a
+ * unit whose margin lies within rounding of fallback_margin may go either way.
+ * PYR_ERR_INVALID for fallback_k outside [0, K] or a non-finite margin,
+ * PYR_ERR_MISALIGNED for a k_head that is not 4-byte aligned. */
+pyr_status pyr_select_topk_budgets(const pyr_problem* p, const void* q, const float* pyramid,
+                                   const int32_t* k_head, int32_t fallback_k,
+                                   float fallback_margin, int32_t* sel, int32_t* trace_ids,
+                                   float* trace_scores, hipStream_t stream);
+
+/* Host-only helper for per-head budgets (no device work): K_h =
+ * clamp(round(total * entropy[h] / sum(entropy)), k_min, k_max) -- budgets in
+ * proportion to each head's attention entropy (a head whose attention is
+ * spread out gets more blocks), an equal split when every entropy is 0.
+ * entropy and k_out are HOST arrays of n_heads entries.  PYR_ERR_INVALID for
+ * n_heads < 0, k_min < 1, k_max < k_min, total < 0 or an entropy that is
+ * negative or not finite. */
+pyr_status pyr_budgets_from_entropy(const float* entropy, int32_t n_heads, int32_t total,
+                                    int32_t k_min, int32_t k_max, int32_t* k_out);
+
 /* Exact attention over the selected blocks (PHBA §A.1.3: online-softmax
  * accumulation over routed blocks loaded straight from their original
  * layouts, writing output and log-sum-exp).  Query token t at position

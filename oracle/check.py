@@ -32,7 +32,7 @@ def _padded(sel: list[int], width: int) -> list[int]:
 
 
 def check_unit(rows, levels_bh, diag, branching, top_k, scale, dev_row, dev_kept_levels,
-               tol=1e-4):
+               tol=1e-4, k_finest=None, ref_row=None, row_width=None):
     """Judge one unit.
 
     rows            [R, d] query rows of the unit (float64)
@@ -40,10 +40,18 @@ def check_unit(rows, levels_bh, diag, branching, top_k, scale, dev_row, dev_kept
     dev_row         device route row (length K+1, -1 padded)
     dev_kept_levels per level (finest first) the device's kept node ids, -1 padded,
                     or None when the device gave no trace
+    top_k           nodes kept per level; k_finest (default top_k) at the finest
+                    level, where a budget fallback may keep more
+    ref_row         the oracle's route row when the caller computed it (budget
+                    and fallback selections); default select_unit's
+    row_width       slots of a route row (default top_k + 1)
     Returns (status, info) with status in {"exact", "near_tie", "fail"}.
     """
-    width = top_k + 1
-    ref = reference.select_unit(rows, levels_bh, diag, branching, top_k, scale)
+    width = top_k + 1 if row_width is None else row_width
+    k0 = top_k if k_finest is None else k_finest
+    if ref_row is None:
+        ref_row = reference.select_unit(rows, levels_bh, diag, branching, top_k, scale).sel
+    ref = reference.UnitSelection(sel=list(ref_row))
     dev_row = [int(x) for x in dev_row]
     if dev_row == _padded(ref.sel, width):
         return "exact", {}
@@ -56,11 +64,12 @@ def check_unit(rows, levels_bh, diag, branching, top_k, scale, dev_row, dev_kept
     for level in range(len(sizes) - 1, -1, -1):
         cand = reference.candidates(level, kept_above, diag, sizes, branching)
         dev = sorted(int(x) for x in dev_kept_levels[level] if x >= 0)
-        want = min(top_k, len(cand))
+        kl = k0 if level == 0 else top_k
+        want = min(kl, len(cand))
         if len(dev) != want or not set(dev) <= set(cand) or len(set(dev)) != len(dev):
             return "fail", {"reason": "kept set is not a K-subset of the candidates", "level": level,
                             "cand": cand, "device": dev}
-        if len(cand) > top_k:
+        if len(cand) > kl:
             s = reference.lse_scores(rows, levels_bh[level][cand], scale)
             by_id = dict(zip(cand, s))
             low_kept = min(by_id[c] for c in dev)

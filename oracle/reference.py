@@ -57,6 +57,14 @@ Readings of the pages this oracle rests on (the pages leave these open):
       candidates, routes and attended keys never leave it; route slots of
       query blocks past its end hold -1.  So each sequence gets exactly the
       result of a batch-1 problem of its own length.
+  R17 Budgets and fallback (PHAROS summary: per-head budgets from attention
+      entropy, a wider budget when selection confidence is low; no formulas
+      are given, these are ours): units of KV head h keep K_h nodes per level
+      (K_h in [1, K]); at the finest level, if it was scored and the margin
+      s(K_h-th best) - s(best rejected) is below a threshold tau, the unit
+      keeps the best min(F, C) of the same candidates instead (F > K_h).
+      Entropy budgets: K_h = clamp(round(total * H_h / sum H), k_min, k_max),
+      rounding half up, an equal split when sum H = 0.
 """
 
 from __future__ import annotations
@@ -273,6 +281,43 @@ def select_unit(rows: np.ndarray, levels: list[np.ndarray], diag: int, branching
         res.kept[level] = kept
     res.sel = sorted(kept) + [diag]                  # R9
     return res
+
+
+def finest_margin(s: np.ndarray, k: int) -> float:
+    """The k-th best score minus the (k+1)-th best (the best rejected one)."""
+    ordered = np.sort(np.asarray(s, dtype=np.float64))[::-1]
+    return float(ordered[k - 1] - ordered[k])
+
+
+def select_unit_budget(rows: np.ndarray, levels: list[np.ndarray], diag: int, branching: int,
+                       k_h: int, scale: float, fallback_k: int = 0,
+                       fallback_margin: float = 0.0) -> UnitSelection:
+    """select_unit with a budget of k_h nodes per level and the finest-level
+    confidence fallback of reading R17.  The result carries .fallback (bool)
+    and .margin (the finest level's margin, None when it was not scored)."""
+    res = select_unit(rows, levels, diag, branching, k_h, scale)
+    res.fallback, res.margin = False, None
+    s0 = res.scores[0]
+    if s0 is not None:                               # the finest level was scored
+        res.margin = finest_margin(s0, k_h)
+        if fallback_k > k_h and res.margin < fallback_margin:
+            cand = res.cands[0]
+            kept = sorted(top_k_nodes(cand, s0, min(fallback_k, len(cand))))
+            res.kept[0] = kept
+            res.sel = kept + [diag]
+            res.fallback = True
+    return res
+
+
+def budgets_from_entropy(entropy, total: int, k_min: int, k_max: int) -> list[int]:
+    """Per-head budgets in proportion to attention entropy (reading R17)."""
+    ent = [float(x) for x in entropy]
+    tot = sum(ent)
+    out = []
+    for x in ent:
+        share = total * x / tot if tot > 0 else total / len(ent)
+        out.append(int(min(max(math.floor(share + 0.5), k_min), k_max)))
+    return out
 
 
 def select(q: np.ndarray, levels: list[np.ndarray], Tk: int, block: int, branching: int,

@@ -324,3 +324,41 @@ def test_packed_binding_shapes(monkeypatch):
     sel = torch.zeros((2, 2, 4, 9), dtype=torch.int32)
     with pytest.raises(ValueError, match="lse: shape"):
         H.pyr_block_sparse_attn(p, q, k, k, sel, q, torch.zeros((4, 2, 150)))
+
+
+def test_select_budgets_validation():
+    p = _p()
+    c = ctypes.byref(p.c())
+    ptr = ctypes.c_void_p(16)
+    for fb_k, margin, kh, status, word in [(9, 0.0, None, 2, "fallback_k"), (-1, 0.0, None, 2, "fallback_k"),
+                                           (4, float("nan"), None, 2, "margin"),
+                                           (4, float("inf"), None, 2, "margin"),
+                                           (4, 0.5, ctypes.c_void_p(18), 4, "k_head")]:
+        s, msg = _status("pyr_select_topk_budgets", c, ptr, ptr, kh, fb_k, margin, ptr, None, None,
+                         None)
+        assert s == status and word in msg, (s, msg)
+    e = ctypes.byref(_p(batch=0).c())
+    assert _status("pyr_select_topk_budgets", e, None, None, None, 0, 0.0, None, None, None,
+                   None)[0] == 0
+
+
+def test_budgets_from_entropy_matches_the_oracle():
+    import numpy as np
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        n = int(rng.integers(1, 17))
+        ent = rng.random(n).astype(np.float32) * float(rng.choice([0.0, 1.0, 8.0]))
+        total = int(rng.integers(0, 300))
+        kmin = int(rng.integers(1, 8))
+        kmax = kmin + int(rng.integers(0, 64))
+        got = H.pyr_budgets_from_entropy([float(x) for x in ent], total, kmin, kmax)
+        assert got == reference.budgets_from_entropy([float(x) for x in ent], total, kmin, kmax)
+    lib = H.lib()
+    out = (ctypes.c_int32 * 2)()
+    ent = (ctypes.c_float * 2)(1.0, -1.0)
+    assert lib.pyr_budgets_from_entropy(ent, 2, 8, 1, 4, out) == 2
+    ent = (ctypes.c_float * 2)(1.0, 1.0)
+    assert lib.pyr_budgets_from_entropy(ent, 2, 8, 0, 4, out) == 2
+    assert lib.pyr_budgets_from_entropy(ent, 2, 8, 3, 2, out) == 2
+    assert lib.pyr_budgets_from_entropy(None, 2, 8, 1, 4, out) == 1
+    assert lib.pyr_budgets_from_entropy(None, 0, 8, 1, 4, None) == 0
