@@ -219,7 +219,7 @@ def attn_kernel_name(cfg):
         return "attn_decode_split+combine"
     if cfg.dtype.itemsize != 2:
         return "attn_prefill_valu"
-    return "attn_prefill_ilv" if cfg.group % 4 == 0 else "attn_prefill_mfma"
+    return "attn_prefill_pp" if cfg.group % 4 == 0 else "attn_prefill_mfma"
 
 
 def kernel_traffic(workload, kind="attn"):

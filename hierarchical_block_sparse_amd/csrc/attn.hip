@@ -15,10 +15,11 @@
 //    of S^T, each lane holds one query row: the row max and sum need a single
 //    cross-half shuffle, and P^T feeds the PV MFMA as its B operand straight from
 //    registers.  Online softmax in fp32, log2 domain.  Q stays in VGPRs.
-//  * attn_prefill_ilv (bf16, query heads per KV head a multiple of 4): the same
-//    data layout and MFMA shapes with 8 waves of 32 rows, software-pipelined
-//    inside each wave so that the exponentials of one 32-key half run between
-//    the MFMAs of the next half's scores and the previous half's PV product.
+//  * attn_prefill_pp (bf16, query heads per KV head a multiple of 4): the same
+//    data layout and MFMA shapes with 8 waves of 32 rows in two groups that
+//    take turns: while one wave of a SIMD runs the matrix work of a block (its
+//    LDS fragment reads and MFMAs), the other runs the vector work (row max,
+//    exponentials, bf16 packing), then they swap.
 //  * attn_prefill_valu: fp32 (or any dtype) reference-precision path, one
 //    thread per query row, fp32 dot products.
 //  * attn_decode_split + attn_decode_combine: decode (one query token per
@@ -316,27 +317,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
   }
 }
 // ---------------------------------------------------------------------------
-// bf16 prefill, MFMA, 8 waves, software-pipelined inside each wave
-//
-// Same data layout and MFMA shapes as attn_prefill_mfma (32 query rows per
-// wave, S^T = K Q^T, O^T += V^T P^T), but the work of a 32-key half block runs
-// skewed over three steps.  Step h of a wave applies the mask and the running
-// max to the scores S(h), then issues one fixed sequence in which the MFMAs of
-// S(h+1) and those of the PV product of half h-1 alternate, with the
-// exponentials of half h (each with its fma, sum and bf16 conversion) placed
-// between them, so the vector ALU works while the matrix core runs instead of
-// after it.  Scheduling barriers pin that order; the LDS fragment of an MFMA is
-// read kIlvPF MFMAs ahead.
-//
-// LDS holds three K tiles and four V tiles (block b in K slot b % 3 and V slot
-// b % 4).  One barrier per block, before the step that first reads K(x+1):
-// there the slots of K(x) and V(x-1) are free and block x+3 starts loading, so
-// a block's tiles have two blocks' time to arrive.  Blocks that need the
-// causal mask (the diagonal block) go last in the route, so the steady-state
-// steps carry no mask.
+// Helpers of the 8-wave bf16 prefill kernel: fragment offsets, tile loads,
+// the row maximum of a 32-key half and the exponentials of P^T.
 // ---------------------------------------------------------------------------
-constexpr int kIlvKS = 3, kIlvVS = 4;  // K and V tile slots
-constexpr int kIlvPF = 2;              // LDS fragment reads in flight ahead of the MFMA
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4v lds_u32x4;
@@ -345,12 +328,12 @@ typedef __attribute__((address_space(3))) u32x4v lds_u32x4;
 // repeats every 4 rows (V) and within 32 rows (K), so the two 32-key halves and
 // the 16-key groups of a half differ by constant offsets.
 template <int D>
-struct IlvOffsets {
+struct FragOffsets {
   // K fragment of step ks: row lr, 16-byte chunk 2*ks + half, stored at chunk
   // (2*ks + half) ^ swz = 2*ks ^ (swz ^ half): byte offset krow + (32*ks ^ kx)
   int krow, kx;
   int v[D / 32];  // V^T fragment of dim tile dt: keys 4*half + l%16/4 (and + 8)
-  __device__ IlvOffsets(int l) {
+  __device__ FragOffsets(int l) {
     using TG = TileGeom<D>;
     const int half = l / 32, lr = l % 32, g16 = l / 16, s16 = l % 16;
     krow = lr * TG::ROW;
@@ -364,52 +347,11 @@ struct IlvOffsets {
   }
 };
 
-// Sequence slot t of a step.  With both products, even slots are the S^T
-// MFMAs (ks = t/2) and odd slots the PV MFMAs (u = t/2: k2 = u / (D/32),
-// dt = u % (D/32)); with one product, every slot is that product's.
-template <int D, bool DO_S, bool DO_PV>
-struct IlvSlot {
-  static constexpr int NS = DO_S ? D / 16 : 0;
-  static constexpr int NP = DO_PV ? D / 16 : 0;
-  static constexpr int NM = NS + NP;
-  __device__ static constexpr bool is_s(int t) { return DO_S && (!DO_PV || t % 2 == 0); }
-  __device__ static constexpr int idx(int t) { return DO_S && DO_PV ? t / 2 : t; }
-};
-
-// Kh: K tile + the half's row offset; Vh: V tile + the half's row offset.
-template <int D, bool DO_S, bool DO_PV>
-__device__ __forceinline__ bf16x8 ilv_frag(int t, const lds_u8* Kh, const lds_u8* Vh,
-                                           const IlvOffsets<D>& fo) {
-  using TG = TileGeom<D>;
-  using SL = IlvSlot<D, DO_S, DO_PV>;
-  if (SL::is_s(t)) {
-    const u32x4v x = *reinterpret_cast<const lds_u32x4*>(Kh + ((32 * SL::idx(t)) ^ fo.kx));
-    return __builtin_bit_cast(bf16x8, x);
-  }
-  const int u = SL::idx(t), k2 = u / (D / 32), dt = u % (D / 32);
-  const lds_u8* p = Vh + fo.v[dt] + 16 * k2 * TG::ROW;
-  const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * TG::ROW));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Inputs of the 8-wave kernel's block loop.
-struct IlvRun {
-  const bf16_t* kh;
-  const bf16_t* vh;
-  const int* ord;
-  unsigned char* ktiles;
-  unsigned char* vtiles;
-  int64_t Tk, row0;
-  int nsel, w, l;
-  float sl2;
-};
-
 // Tile loads of block j for the 8-wave kernel (same layout as issue_tiles):
 // the block's first row is a uniform base and each lane adds a 32-bit
 // offset, clamped to the last row of the sequence.
 template <int D>
-__device__ __forceinline__ void ilv_issue(const bf16_t* kh, const bf16_t* vh, int64_t Tk, int j,
+__device__ __forceinline__ void tile_loads8(const bf16_t* kh, const bf16_t* vh, int64_t Tk, int j,
                                           int w, int l, unsigned char* ktile,
                                           unsigned char* vtile) {
   using TG = TileGeom<D>;
@@ -434,7 +376,7 @@ __device__ __forceinline__ void ilv_issue(const bf16_t* kh, const bf16_t* vh, in
 // with its share of the row sum and, for odd e, the packed bf16 pair of P^T.
 // Empty asm uses keep each result in the slot that computes it (IR passes
 // would otherwise sink the work past the sequence, to its first real use).
-__device__ __forceinline__ void ilv_exp(int e, f32x16& sc, float sl2, float mneg, float& ps0,
+__device__ __forceinline__ void exp_pair(int e, f32x16& sc, float sl2, float mneg, float& ps0,
                                         float& ps1, uint32_t (&pw)[8]) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const float p = __builtin_amdgcn_exp2f(fmaf(sc[e], sl2, mneg));
@@ -451,60 +393,16 @@ __device__ __forceinline__ void ilv_exp(int e, f32x16& sc, float sl2, float mneg
 }
 
 // P^T fragment k2 (keys 16*k2 .. of the half) from the packed pairs.
-__device__ __forceinline__ bf16x8 ilv_pfrag(const uint32_t (&pw)[8], int k2) {
+__device__ __forceinline__ bf16x8 p_frag(const uint32_t (&pw)[8], int k2) {
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const u32x4_t x = {pw[4 * k2], pw[4 * k2 + 1], pw[4 * k2 + 2], pw[4 * k2 + 3]};
   return __builtin_bit_cast(bf16x8, x);
 }
 
-// One step's fixed sequence: S(h+1) into sn (DO_S), O^T += V^T P(h-1)^T from
-// pp (DO_PV), and the probabilities of half h from sc into pc.
-template <int D, bool DO_S, bool DO_PV>
-__device__ __forceinline__ void ilv_region(const lds_u8* Kh, const lds_u8* Vh,
-                                           const IlvOffsets<D>& fo, const uint4 (&qb)[D / 16],
-                                           f32x16& sn, f32x16 (&oacc)[D / 32],
-                                           const uint32_t (&pp)[8], f32x16& sc, float sl2,
-                                           float mneg, uint32_t (&pc)[8], float& psum) {
-  using SL = IlvSlot<D, DO_S, DO_PV>;
-  constexpr int NM = SL::NM;
-  // the per-step K offsets are rebuilt from kx in every sequence; an opaque
-  // copy keeps the compiler from hoisting all of them into registers
-  IlvOffsets<D> fl = fo;
-  asm volatile("" : "+v"(fl.kx));
-  Kh += fo.krow;
-  float ps0 = 0.f, ps1 = 0.f;
-  if constexpr (DO_S) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sn[e] = 0.f;
-  }
-  if constexpr (NM == 0) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) ilv_exp(e, sc, sl2, mneg, ps0, ps1, pc);
-  } else {
-    bf16x8 fr[NM];
-#pragma unroll
-    for (int t = 0; t < kIlvPF && t < NM; ++t) fr[t] = ilv_frag<D, DO_S, DO_PV>(t, Kh, Vh, fl);
-#pragma unroll
-    for (int t = 0; t < NM; ++t) {
-      if (t + kIlvPF < NM) fr[t + kIlvPF] = ilv_frag<D, DO_S, DO_PV>(t + kIlvPF, Kh, Vh, fl);
-      if (SL::is_s(t)) {
-        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t], as_bf16x8(qb[SL::idx(t)]), sn, 0, 0, 0);
-      } else {
-        const int u = SL::idx(t), k2 = u / (D / 32), dt = u % (D / 32);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t], ilv_pfrag(pp, k2), oacc[dt], 0, 0, 0);
-      }
-#pragma unroll
-      for (int e = t * 16 / NM; e < (t + 1) * 16 / NM; ++e) ilv_exp(e, sc, sl2, mneg, ps0, ps1, pc);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  psum = ps0 + ps1;
-}
-
 // Maximum of a lane's row over the 32 keys of a half, both lane halves; the
 // mask drops keys past the row (key index within the block > rel).
 template <bool MASK>
-__device__ __forceinline__ float ilv_rowmax(f32x16& s, int kt, int half, int rel) {
+__device__ __forceinline__ float half_rowmax(f32x16& s, int kt, int half, int rel) {
   if (MASK) {
     // score e holds key kt*32 + (e/4)*8 + half*4 + e%4; compare its constant
     // part against the lane's bound so no per-score index stays live
@@ -520,22 +418,102 @@ __device__ __forceinline__ float ilv_rowmax(f32x16& s, int kt, int half, int rel
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Step for half KT of block x: scores in sc -> P^T in pc; S of the next half
-// (Kh) into sn when DO_S; PV of the previous half (Vh, pp) when DO_PV.
-template <int D, int KT, bool MASK>
-__device__ __forceinline__ void ilv_step(int rel, const lds_u8* Kh, const lds_u8* Vh,
-                                         const IlvOffsets<D>& fo, const uint4 (&qb)[D / 16],
-                                         f32x16& sc, f32x16& sn, const uint32_t (&pp)[8],
-                                         uint32_t (&pc)[8], f32x16 (&oacc)[D / 32], float sl2,
-                                         int half, float& m_run, float& l_run) {
-  const float mraw = ilv_rowmax<MASK>(sc, KT, half, rel);
+// ---------------------------------------------------------------------------
+// bf16 prefill, MFMA, 8 waves in two groups taking turns (ping-pong)
+//
+// Same tiles, fragments and MFMA shapes as attn_prefill_mfma (32 query rows
+// per wave, S^T = K Q^T, O^T += V^T P^T), eight waves (four heads x two row
+// halves), and each wave alternates two kinds of phase: a matrix phase (the
+// S^T MFMAs of the next block and the PV MFMAs of the current one, with their
+// LDS fragment reads) and a vector phase (row maximum, rescale,
+// exponentials, bf16 packing of P^T).  Waves 0-3 run one phase ahead of
+// waves 4-7, and wave w shares its SIMD with wave w+4, so in every phase each
+// SIMD has one wave on the matrix core and one on the vector ALU: the two
+// units overlap across waves, which they do better than inside one wave's
+// instruction stream.  A barrier ends every phase.  Block y sits in tile slot
+// y % 4 and is loaded four phases before its first use, when the slot's
+// previous block is done.
+// ---------------------------------------------------------------------------
+
+// Matrix phase: S^T of a whole block (two 32-key M tiles, DO_S) from Kn and
+// O^T += V^T P^T of a whole block (DO_PV) from Vx and p.  The MFMAs alternate
+// between the two products and their LDS fragments are read kPpPF ahead.
+constexpr int kPpPF = 6;
+
+template <int D, bool DO_S, bool DO_PV>
+struct PpSlot {
+  static constexpr int NS = DO_S ? 2 * (D / 16) : 0;  // (half kt, step ks)
+  static constexpr int NP = DO_PV ? 2 * (D / 16) : 0;  // (half kt, key group k2, dim tile dt)
+  static constexpr int NM = NS + NP;
+  __device__ static constexpr bool is_s(int t) { return DO_S && (!DO_PV || t % 2 == 0); }
+  __device__ static constexpr int idx(int t) { return DO_S && DO_PV ? t / 2 : t; }
+};
+
+template <int D, bool DO_S, bool DO_PV>
+__device__ __forceinline__ bf16x8 pp_frag(int t, const lds_u8* Kn, const lds_u8* Vx,
+                                          const FragOffsets<D>& fo) {
+  using TG = TileGeom<D>;
+  using SL = PpSlot<D, DO_S, DO_PV>;
+  constexpr int HALF = 32 * TG::ROW;
+  if (SL::is_s(t)) {
+    const int u = SL::idx(t), kt = u % 2, ks = u / 2;
+    const u32x4v x =
+        *reinterpret_cast<const lds_u32x4*>(Kn + kt * HALF + fo.krow + ((32 * ks) ^ fo.kx));
+    return __builtin_bit_cast(bf16x8, x);
+  }
+  const int u = SL::idx(t), kt = u / (D / 16), k2 = (u / (D / 32)) % 2, dt = u % (D / 32);
+  const lds_u8* p = Vx + kt * HALF + fo.v[dt] + 16 * k2 * TG::ROW;
+  const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * TG::ROW));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int D, bool DO_S, bool DO_PV>
+__device__ __forceinline__ void pp_matrix(const lds_u8* Kn, const lds_u8* Vx,
+                                          const FragOffsets<D>& fo, const uint4 (&qb)[D / 16],
+                                          f32x16 (&s)[2], const uint32_t (&p)[2][8],
+                                          f32x16 (&oacc)[D / 32]) {
+  using SL = PpSlot<D, DO_S, DO_PV>;
+  constexpr int NM = SL::NM;
+  FragOffsets<D> fl = fo;
+  asm volatile("" : "+v"(fl.kx));
+  if constexpr (DO_S) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
+  }
+  bf16x8 fr[NM];
+#pragma unroll
+  for (int t = 0; t < kPpPF && t < NM; ++t) fr[t] = pp_frag<D, DO_S, DO_PV>(t, Kn, Vx, fl);
+#pragma unroll
+  for (int t = 0; t < NM; ++t) {
+    if (t + kPpPF < NM) fr[t + kPpPF] = pp_frag<D, DO_S, DO_PV>(t + kPpPF, Kn, Vx, fl);
+    if (SL::is_s(t)) {
+      const int u = SL::idx(t), kt = u % 2, ks = u / 2;
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t], as_bf16x8(qb[ks]), s[kt], 0, 0, 0);
+    } else {
+      const int u = SL::idx(t), kt = u / (D / 16), k2 = (u / (D / 32)) % 2, dt = u % (D / 32);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t], p_frag(p[kt], k2), oacc[dt],
+                                                         0, 0, 0);
+    }
+    // keep the order: the reads of fragment t + kPpPF go out before MFMA t
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Vector phase: the block's scores in s -> P^T in p (packed bf16 pairs), with
+// the running max, the rescale of O and l, and the row sum.
+template <int D, bool MASK>
+__device__ __forceinline__ void pp_vector(f32x16 (&s)[2], uint32_t (&p)[2][8],
+                                          f32x16 (&oacc)[D / 32], float sl2, int half, int rel,
+                                          float& m_run, float& l_run) {
+  const float mraw =
+      fmaxf(half_rowmax<MASK>(s[0], 0, half, rel), half_rowmax<MASK>(s[1], 1, half, rel));
   const float mx = mraw * sl2;
   const float m_new = mx > m_run + kRescaleLog2 ? mx : m_run;
   // a row that has seen no visible key yet keeps m = -inf: all its p are 0
   const float mneg = m_new == -INFINITY ? 0.f : -m_new;
-  float psum;
-  ilv_region<D, true, true>(Kh, Vh, fo, qb, sn, oacc, pp, sc, sl2, mneg, pc, psum);
-  // O holds the PV products up to the previous half, all at the scale of m_run
   if (__any(m_new != m_run)) {
     const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
@@ -545,79 +523,121 @@ __device__ __forceinline__ void ilv_step(int rel, const lds_u8* Kh, const lds_u8
       for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
   }
   m_run = m_new;
-  l_run += psum;
+  // each exponential keeps its slot next to its fma, sum and conversion
+  // (measured faster than leaving the order to the compiler)
+  float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) exp_pair(e, s[kt], sl2, mneg, ps0, ps1, p[kt]);
+  l_run += ps0 + ps1;
 }
 
-// Both steps of block x (half 0, then half 1) with the barrier between them.
-// Scores of half 0 arrive in sA, P^T of the previous block's half 1 in pB;
-// the steps leave S of the next block's half 0 in sA and P^T of this block's
-// half 1 in pB.
-// The work of block x.  Its first step reads K(x) and V(x-1), its second
-// K(x+1) and V(x); the loads of block x+3 go into the slots of K(x) and V(x-1)
-// once the barrier between the steps shows that every wave is done with them,
-// and are waited for explicitly before their first use, two blocks later.
-template <int D, bool MASK>
-__device__ __forceinline__ void ilv_block_slots(
-    const IlvRun& r, int x, const lds_u8* Kx, const lds_u8* Vprev, const lds_u8* Kn,
-    const lds_u8* Vx, unsigned char* Kd, unsigned char* Vd, const bf16_t* kh, const bf16_t* vh,
-    const IlvOffsets<D>& fo, const uint4 (&qb)[D / 16],
-    f32x16& sA, f32x16& sB, uint32_t (&pA)[8], uint32_t (&pB)[8], f32x16 (&oacc)[D / 32],
-    float& m_run, float& l_run) {
+// Inputs of the ping-pong kernel's block loop.
+template <int D>
+struct PpRun {
+  const bf16_t* kh;
+  const bf16_t* vh;
+  const int* ord;
+  int64_t Tk, row0;
+  int nsel, w, l, grp;
+  float sl2;
+};
+
+// Tile slots of the ping-pong kernel: block y in K slot y % 4 and V slot
+// y % 4, each slot an LDS array of its own.  Inside the main loop every slot
+// is named at compile time, so the compiler can tell the slots being read
+// from the slots still loading and does not wait for those loads (with one
+// array, or a slot chosen at run time, every LDS read waits for every tile
+// load in flight, which undoes the prefetch).
+constexpr int kPpSlots = 4;
+constexpr int kPpTile = 64 * 2 * 128;  // bytes of a K or V tile at d = 128
+__shared__ __align__(16) unsigned char pp_k0[kPpTile], pp_k1[kPpTile], pp_k2[kPpTile],
+    pp_k3[kPpTile];
+__shared__ __align__(16) unsigned char pp_v0[kPpTile], pp_v1[kPpTile], pp_v2[kPpTile],
+    pp_v3[kPpTile];
+
+template <int S>
+__device__ __forceinline__ unsigned char* pp_kslot() {
+  if constexpr (S == 0) return pp_k0;
+  else if constexpr (S == 1) return pp_k1;
+  else if constexpr (S == 2) return pp_k2;
+  else return pp_k3;
+}
+template <int S>
+__device__ __forceinline__ unsigned char* pp_vslot() {
+  if constexpr (S == 0) return pp_v0;
+  else if constexpr (S == 1) return pp_v1;
+  else if constexpr (S == 2) return pp_v2;
+  else return pp_v3;
+}
+// Slot S, or (S < 0) slot y % 4 chosen at run time.
+template <int S>
+__device__ __forceinline__ unsigned char* pp_k(int y) {
+  if constexpr (S >= 0) return pp_kslot<S>();
+  const int m = y % kPpSlots;
+  return m == 0 ? pp_k0 : m == 1 ? pp_k1 : m == 2 ? pp_k2 : pp_k3;
+}
+template <int S>
+__device__ __forceinline__ unsigned char* pp_v(int y) {
+  if constexpr (S >= 0) return pp_vslot<S>();
+  const int m = y % kPpSlots;
+  return m == 0 ? pp_v0 : m == 1 ? pp_v1 : m == 2 ? pp_v2 : pp_v3;
+}
+
+// This wave's share of the loads of block y (if it exists) into slot S.
+template <int D, int S>
+__device__ __forceinline__ void pp_issue(const PpRun<D>& r, int y) {
+  if (y < r.nsel) tile_loads8<D>(r.kh, r.vh, r.Tk, r.ord[y], r.w, r.l, pp_k<S>(y), pp_v<S>(y));
+}
+
+// Wait for this wave's loads of block y: the loads of block y+1 (issued after
+// them) may stay in flight.
+template <int D>
+__device__ __forceinline__ void pp_wait(const PpRun<D>& r, int y) {
   using TG = TileGeom<D>;
   constexpr int NLOAD = 2 * (TG::CPR / 8);  // tile-load instructions per block per wave
-  constexpr int HALF = 32 * TG::ROW;        // bytes of a 32-key half tile
-  const int half = r.l / 32, lr = r.l % 32;
-  const int rel = MASK ? (int)(r.row0 - (int64_t)r.ord[x] * PYR_BLOCK) + lr : 0;
-  // half 0 of block x: S of half 1 of block x; PV of half 1 of block x-1
-  // (for x = 0 that product is zero: P^T starts at zero and the V slot of
-  // block -1 is zero-filled until block kIlvVS - 1 loads into it)
-  ilv_step<D, 0, MASK>(rel, Kx + HALF, Vprev + HALF, fo, qb, sA, sB, pB, pA, oacc, r.sl2, half,
-                       m_run, l_run);
-  // block x+1 has landed once at most the loads of block x+2 are outstanding;
-  // after the barrier every wave's have, and no wave reads the slots of block
-  // x+3 any more
-  if (x + 2 < r.nsel)
+  if (y + 1 < r.nsel)
     __builtin_amdgcn_s_waitcnt(0x0F70 | (NLOAD & 15) | ((NLOAD >> 4) << 14));
   else
     __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  if (x + 3 < r.nsel) ilv_issue<D>(kh, vh, r.Tk, r.ord[x + 3], r.w, r.l, Kd, Vd);
-  // half 1 of block x: S of half 0 of block x+1; PV of half 0 of block x
-  // (after the last block this computes S of a stale tile, which is dropped)
-  ilv_step<D, 1, MASK>(rel, Kn, Vx, fo, qb, sB, sA, pA, pB, oacc, r.sl2, half, m_run, l_run);
 }
 
-template <int D, bool MASK>
-__device__ __forceinline__ void ilv_block(const IlvRun& r, int x, const IlvOffsets<D>& fo,
-                                          const uint4 (&qb)[D / 16], f32x16& sA, f32x16& sB,
-                                          uint32_t (&pA)[8], uint32_t (&pB)[8],
-                                          f32x16 (&oacc)[D / 32], float& m_run, float& l_run) {
-  using TG = TileGeom<D>;
-  lds_u8* const kt0 = (lds_u8*)r.ktiles;
-  lds_u8* const vt0 = (lds_u8*)r.vtiles;
-  // slot offsets go through readfirstlane so that loop strength reduction
-  // does not turn every fragment address into an induction variable
-  const int kx = __builtin_amdgcn_readfirstlane((x % kIlvKS) * TG::TILE);
-  const int kn = __builtin_amdgcn_readfirstlane(((x + 1) % kIlvKS) * TG::TILE);
-  const int kd = __builtin_amdgcn_readfirstlane(((x + 3) % kIlvKS) * TG::TILE);
-  const int vp = __builtin_amdgcn_readfirstlane(((x + kIlvVS - 1) % kIlvVS) * TG::TILE);
-  const int vx = __builtin_amdgcn_readfirstlane((x % kIlvVS) * TG::TILE);
-  const int vd = __builtin_amdgcn_readfirstlane(((x + 3) % kIlvVS) * TG::TILE);
-  ilv_block_slots<D, MASK>(r, x, kt0 + kx, vt0 + vp, kt0 + kn, vt0 + vx, r.ktiles + kd,
-                           r.vtiles + vd, r.kh, r.vh, fo, qb, sA, sB, pA, pB, oacc, m_run, l_run);
+// Block x of a wave: the vector phase of block x, then the matrix phase with
+// PV(x) and (DO_S) S(x+1).  The barrier before each phase ends a global
+// phase; at the start of an even global phase 2x+2 the loads of block x+3 go
+// out, and at the end of the odd one before it block x+1 must have landed.
+// For group 0 the vector phase is the odd global phase 2x+1, for group 1 the
+// even one 2x+2.
+// J: the slot of block x (x % 4) when known at compile time, else -1.
+template <int D, bool MASK, bool DO_S, int J>
+__device__ __forceinline__ void pp_block(const PpRun<D>& r, int x, const FragOffsets<D>& fo,
+                                         const uint4 (&qb)[D / 16], f32x16 (&s)[2],
+                                         uint32_t (&p)[2][8], f32x16 (&oacc)[D / 32],
+                                         float& m_run, float& l_run) {
+  constexpr int JN = J < 0 ? -1 : (J + 1) % kPpSlots;  // slot of block x+1
+  constexpr int JL = J < 0 ? -1 : (J + 3) % kPpSlots;  // slot of block x+3
+  const int half = r.l / 32, lr = r.l % 32;
+  if (r.grp) pp_wait(r, x + 1);
+  lds_barrier();
+  if (r.grp) pp_issue<D, JL>(r, x + 3);
+  const int rel = MASK ? (int)(r.row0 - (int64_t)r.ord[x] * PYR_BLOCK) + lr : 0;
+  pp_vector<D, MASK>(s, p, oacc, r.sl2, half, rel, m_run, l_run);
+  if (!r.grp) pp_wait(r, x + 1);
+  lds_barrier();
+  if (!r.grp) pp_issue<D, JL>(r, x + 3);
+  pp_matrix<D, DO_S, true>((lds_u8*)pp_k<JN>(x + 1), (lds_u8*)pp_v<J>(x), fo, qb, s, p, oacc);
 }
 
 template <int D>
-__global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
+__global__ __launch_bounds__(512, 2) void attn_prefill_pp(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ sel, bf16_t* __restrict__ o, float* __restrict__ lse, PyrGeom g,
     int wg_per_unit) {
   using TG = TileGeom<D>;
   constexpr int NT = 512;
   constexpr int NLOAD = 2 * (TG::CPR / 8);  // tile-load instructions per block per wave
-  constexpr int HALF = 32 * TG::ROW;        // bytes of a 32-key half tile
-  __shared__ __align__(16) unsigned char ktiles[kIlvKS][TG::TILE];
-  __shared__ __align__(16) unsigned char vtiles[kIlvVS][TG::TILE];
+  static_assert(TG::TILE <= kPpTile, "tile slots are sized for d <= 128");
   __shared__ int s_sel[kMaxSel];
   __shared__ int s_ord[kMaxSel];
   __shared__ int s_n, s_nun;
@@ -631,15 +651,17 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
   unit_of(g, blockIdx.x / wg_per_unit, bi, hk, i, unit);
   const PyrSeq sq = pyr_seq(g, bi);
   if (i >= sq.nqb) return;  // past the end of a shorter packed sequence
-  // waves 2h and 2h+1 take the two 32-row halves of head sub*4 + h
+  // waves 2h and 2h+1 take the two 32-row halves of head sub*4 + h; waves
+  // 0-3 form group 0, waves 4-7 group 1
   const int h = hk * g.G + sub * 4 + w / 2;
+  const int grp = w >> 2;
   const int64_t row0 = (int64_t)i * PYR_BLOCK + (w % 2) * 32;
   const float sl2 = g.scale * PYR_LOG2E;
 
   for (int jj = tid; jj <= g.K; jj += NT) s_sel[jj] = sel[unit * (g.K + 1) + jj];
   __syncthreads();
-  // route order for the pipeline: valid blocks before the unit's own block
-  // first (no mask needed), then the rest (the diagonal block)
+  // route order: valid blocks before the unit's own block first (no mask
+  // needed), then the rest (the diagonal block)
   if (w == 0) {
     int n = 0, nun = 0;
 #pragma unroll 1
@@ -660,26 +682,10 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
       s_nun = nun;
     }
   }
-  {  // zero the V slot of block -1: the first step multiplies it by P^T = 0
-    uint4* z = reinterpret_cast<uint4*>(&vtiles[kIlvVS - 1][0]);
-    for (int e = tid; e < TG::TILE / 16; e += NT) z[e] = make_uint4(0u, 0u, 0u, 0u);
-  }
   __syncthreads();
   const int nsel = s_n, nun = s_nun;
-  IlvRun run;
-  run.kh = k + (sq.k0 + hk * sq.khs) * D;
-  run.vh = v + (sq.k0 + hk * sq.khs) * D;
-  run.ord = s_ord;
-  run.ktiles = &ktiles[0][0];
-  run.vtiles = &vtiles[0][0];
-  run.Tk = sq.Tk;
-  run.row0 = row0;
-  run.nsel = nsel;
-  run.w = w;
-  run.l = l;
-  run.sl2 = sl2;
-  lds_u8* const kt0 = (lds_u8*)&ktiles[0][0];
-  lds_u8* const vt0 = (lds_u8*)&vtiles[0][0];
+  const bf16_t* kh = k + (sq.k0 + hk * sq.khs) * D;
+  const bf16_t* vh = v + (sq.k0 + hk * sq.khs) * D;
 
   // Q^T fragments (B operand): lane holds query row lr and d = ks*16 + 8*half .. +7.
   // Rows past the end of a ragged last block load the last row; they are never stored.
@@ -690,54 +696,60 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_ilv(
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qb[ks] = ld16(qh + tok * D + ks * 16 + 8 * half);
   }
-#pragma unroll
-  for (int b = 0; b < 3; ++b)
-    if (b < nsel) ilv_issue<D>(run.kh, run.vh, sq.Tk, s_ord[b], w, l, ktiles[b], vtiles[b]);
 
-  const IlvOffsets<D> fo(l);
+  const FragOffsets<D> fo(l);
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x16 sA, sB;        // scores of even / odd halves
-  uint32_t pA[8], pB[8];  // P^T of even / odd halves, packed bf16 pairs
-#pragma unroll
-  for (int e = 0; e < 8; ++e) pB[e] = 0u;
+  f32x16 s[2];
+  uint32_t p[2][8];
 
   if (nsel > 0) {
-    // S of block 0, half 0
-    if (nsel >= 3)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * NLOAD) & 15) | (((2 * NLOAD) >> 4) << 14));
-    else if (nsel == 2)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (NLOAD & 15) | ((NLOAD >> 4) << 14));
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sA[e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      sA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          ilv_frag<D, true, false>(ks, kt0 + fo.krow, vt0, fo), as_bf16x8(qb[ks]), sA, 0, 0, 0);
-
-    // blocks before the unit's own block need no mask; the rest (the
-    // diagonal block) come last
+    PpRun<D> r;
+    r.kh = kh;
+    r.vh = vh;
+    r.ord = s_ord;
+    r.Tk = sq.Tk;
+    r.row0 = row0;
+    r.nsel = nsel;
+    r.w = w;
+    r.l = l;
+    r.grp = grp;
+    r.sl2 = sl2;
+    pp_issue<D, 0>(r, 0);
+    pp_issue<D, 1>(r, 1);
+    // block 0 has landed once at most block 1's loads are outstanding
+    pp_wait(r, 0);
+    lds_barrier();
+    // global phase 0 starts: block 2 loads; group 1 sits it out
+    pp_issue<D, 2>(r, 2);
+    if (grp) lds_barrier();
+    pp_matrix<D, true, false>((lds_u8*)pp_k0, (lds_u8*)pp_v0, fo, qb, s, p, oacc);  // S(0)
+    // blocks before the last that need no mask, four at a time with every
+    // slot named at compile time; then the others (masked blocks go last)
+    const int last = nsel - 1;
+    const int nu = nun < last ? nun : last;
+    int x = 0;
 #pragma unroll 1
-    for (int x = 0; x < nun; ++x)
-      ilv_block<D, false>(run, x, fo, qb, sA, sB, pA, pB, oacc, m_run, l_run);
-#pragma unroll 1
-    for (int x = nun; x < nsel; ++x)
-      ilv_block<D, true>(run, x, fo, qb, sA, sB, pA, pB, oacc, m_run, l_run);
-    // PV of half 1 of the last block
-    const lds_u8* Vl = vt0 + ((nsel - 1) % kIlvVS) * TG::TILE + HALF;
-#pragma unroll
-    for (int u = 0; u < D / 16; ++u) {
-      const int k2 = u / (D / 32), dt = u % (D / 32);
-      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          ilv_frag<D, false, true>(u, kt0, Vl, fo), ilv_pfrag(pB, k2), oacc[dt], 0, 0, 0);
+    for (; x + 3 < nu; x += 4) {
+      pp_block<D, false, true, 0>(r, x, fo, qb, s, p, oacc, m_run, l_run);
+      pp_block<D, false, true, 1>(r, x + 1, fo, qb, s, p, oacc, m_run, l_run);
+      pp_block<D, false, true, 2>(r, x + 2, fo, qb, s, p, oacc, m_run, l_run);
+      pp_block<D, false, true, 3>(r, x + 3, fo, qb, s, p, oacc, m_run, l_run);
     }
+#pragma unroll 1
+    for (; x < nu; ++x) pp_block<D, false, true, -1>(r, x, fo, qb, s, p, oacc, m_run, l_run);
+#pragma unroll 1
+    for (; x < last; ++x) pp_block<D, true, true, -1>(r, x, fo, qb, s, p, oacc, m_run, l_run);
+    if (last < nun)
+      pp_block<D, false, false, -1>(r, last, fo, qb, s, p, oacc, m_run, l_run);
+    else
+      pp_block<D, true, false, -1>(r, last, fo, qb, s, p, oacc, m_run, l_run);
+    lds_barrier();
+    if (!grp) lds_barrier();  // group 0 sits out the last global phase
   }
 
   // finalize: row of this lane = lr; dims of oacc[dt][e] = dt*32 + (e/4)*8 + half*4 + e%4
@@ -1080,7 +1092,7 @@ hipError_t launch_attn_d(const PyrGeom& g, int dtype, const void* q, const void*
     const bf16_t* vv = static_cast<const bf16_t*>(v);
     bf16_t* oo = static_cast<bf16_t*>(o);
     if (nh == 4)
-      hipLaunchKernelGGL((attn_prefill_ilv<D>), grid, dim3(512), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
+      hipLaunchKernelGGL((attn_prefill_pp<D>), grid, dim3(512), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
     else if (nh == 2)
       hipLaunchKernelGGL((attn_prefill_mfma<D, 4, 1>), grid, dim3(256), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
     else
