@@ -216,7 +216,7 @@ def cpu_baseline(cfg, q, k, v, n_units, backward=False):
 def attn_kernel_name(cfg):
     """The attention kernel the library runs for this workload."""
     if cfg.decode:
-        return "attn_decode_split+combine"
+        return "attn_decode_mfma+combine" if cfg.dtype.itemsize == 2 else "attn_decode_split+combine"
     if cfg.dtype.itemsize != 2:
         return "attn_prefill_valu"
     return "attn_prefill_pp" if cfg.group % 4 == 0 else "attn_prefill_mfma"

@@ -22,10 +22,12 @@
 //    exponentials, bf16 packing), then they swap.
 //  * attn_prefill_valu: fp32 (or any dtype) reference-precision path, one
 //    thread per query row, fp32 dot products.
-//  * attn_decode_split + attn_decode_combine: decode (one query token per
-//    sequence).  The selected blocks of a unit are split across workgroups so
-//    the HBM-bound KV stream fills the chip; partial (max, sum, O) triples go to
-//    the workspace and are merged with the LogSumExp rule.
+//  * attn_decode_mfma (bf16) / attn_decode_split (fp32) + attn_decode_combine:
+//    decode (one query token per sequence).  The selected blocks of a unit are
+//    split across workgroups so the HBM-bound KV stream fills the chip; partial
+//    (max, sum, O) triples go to the workspace and are merged with the
+//    LogSumExp rule.  The bf16 kernel scores and accumulates on the matrix
+//    cores, the query rows padded to a 16-wide tile.
 #include <math.h>
 
 #include "pyr_device.h"
@@ -1017,6 +1019,200 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_split(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode, bf16, on the matrix cores.  One workgroup (4 waves) per (unit,
+// split); the workgroup walks the split's blocks one at a time and wave w
+// takes keys [16w, 16w+16) of every block, keeping its own online softmax
+// over them (the four partial states are merged at the end).  Per block and
+// wave: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys x 16 query rows, the
+// G real rows padded with zero rows), the K fragments loaded straight from
+// global memory into registers; then O^T += V^T P^T on
+// v_mfma_f32_16x16x16_bf16, the V tile staged in LDS by direct loads and its
+// transposed fragments read with ds_read_b64_tr_b16, and P^T taken as is
+// from the S^T accumulator layout.  Every byte of K and V is read from HBM
+// once and from LDS at most once; the next block's K and V load while the
+// current one is used.
+// ---------------------------------------------------------------------------
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+
+template <int D>
+__global__ __launch_bounds__(256, 4) void attn_decode_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int32_t* __restrict__ sel, float* __restrict__ ws, PyrGeom g, int nsplit) {
+  using TG = TileGeom<D>;
+  constexpr int KS = D / 32;       // k-steps of the S^T MFMA
+  constexpr int DT = D / 16;       // d tiles of O^T
+  constexpr int TL = TG::CPR / 4;  // V-tile load instructions per wave
+  // two V slots, one array each, so that the LDS reads of one slot do not
+  // wait for the loads into the other
+  __shared__ __align__(16) unsigned char vt0[TG::TILE];
+  __shared__ __align__(16) unsigned char vt1[TG::TILE];
+  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ int s_blk[kDecBlocksPerSplit];
+  __shared__ int s_nb;
+
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lr = l % 16, lg = l / 16;
+  const int split = (int)(blockIdx.x % nsplit);
+  const int64_t bhk = blockIdx.x / nsplit;  // unit (decode: one query block)
+  const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
+  const int G = g.G;
+  const float sl2 = g.scale * PYR_LOG2E;
+  const int64_t qpos = g.Tk - 1;
+  const bf16_t* kh = k + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
+  const bf16_t* vh = v + ((int64_t)bi * g.Hk + hk) * g.Tks * D;
+
+  // Q^T B fragments: lane holds query row lr (zero past G), d = 32*ks + 8*lg .. +7
+  uint4 qb[KS];
+  {
+    const bf16_t* qrow = q + ((int64_t)bi * g.Hq + (int64_t)hk * G + (lr < G ? lr : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qb[ks] = lr < G ? ld16(qrow + ks * 32 + 8 * lg) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // this split's valid blocks
+  if (tid == 0) {
+    const int32_t* srow = sel + bhk * (g.K + 1);
+    const int jb0 = split * kDecBlocksPerSplit;
+    const int jb1 = min(g.K + 1, jb0 + kDecBlocksPerSplit);
+    int n = 0;
+    for (int jj = jb0; jj < jb1; ++jj) {
+      const int j = srow[jj];
+      if (j >= 0 && j < g.nb) s_blk[n++] = j;
+    }
+    s_nb = n;
+  }
+  __syncthreads();
+  const int nblk = s_nb;
+
+  // loads of block b: this wave's K fragments into registers (key 16w + lr,
+  // d = 32*ks + 8*lg), and a quarter of the V tile into vt (rows past the
+  // sequence repeat its last row; the mask gives them no weight)
+  auto load = [&](int b, uint4 (&kr)[KS], unsigned char* vt) {
+    const int64_t key0 = (int64_t)s_blk[b] * PYR_BLOCK;
+    const int64_t lim = g.Tk - 1 - key0;
+    const int last = lim < PYR_BLOCK - 1 ? (int)lim : PYR_BLOCK - 1;
+    const int kk = 16 * w + lr;
+    const bf16_t* krow = kh + (key0 + (kk < last ? kk : last)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kr[ks] = ld16_nt(krow + ks * 32 + 8 * lg);
+#pragma unroll
+    for (int tt = 0; tt < TL; ++tt) {
+      const int t = tt * 4 + w;
+      const int p = t * 64 + l, row = p / TG::CPR, sc = p % TG::CPR;
+      const int rr = row < last ? row : last;
+      const bf16_t* va = vh + (key0 + rr) * D + (sc ^ TG::swz_v(row)) * 8;
+      __builtin_amdgcn_global_load_lds((const void*)va, (lds_void*)(vt + t * 1024), 16, 0, 0);
+    }
+  };
+  // per-lane byte offset of the V^T fragment of d tile dt: row 16w + 4*lg +
+  // lr / 4, columns 16*dt + 4*(lr % 4) .. +3 (the transposed read hands lane
+  // lr of group lg the values V[16w + 4*lg + i][16*dt + lr], i = 0..3: the A
+  // operand of the 16x16x16 MFMA)
+  int voff[DT];
+  {
+    const int r = 16 * w + 4 * lg + lr / 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int c = 16 * dt + 4 * (lr % 4);
+      voff[dt] = r * TG::ROW + (((c >> 3) ^ TG::swz_v(r)) << 4) + (c & 7) * 2;
+    }
+  }
+
+  f32x4 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // block b from kc and vc; block b+1 starts loading into kn and vn
+  auto step = [&](int b, const uint4 (&kc)[KS], uint4 (&kn)[KS], const unsigned char* vc,
+                  unsigned char* vn) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block b
+    lds_barrier();  // every wave's part of V(b) has landed; block b-1's slot is free
+    if (b + 1 < nblk) load(b + 1, kn, vn);
+    // S^T for this wave's 16 keys: lane column lr (query row), rows 4*lg + e (keys)
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[ks]), as_bf16x8(qb[ks]), s, 0, 0, 0);
+    const int64_t kp0 = (int64_t)s_blk[b] * PYR_BLOCK + 16 * w + 4 * lg;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (kp0 + e > qpos) s[e] = -INFINITY;
+      mx = fmaxf(mx, s[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float mneg = m_new == -INFINITY ? 0.f : -m_new;
+    const float alpha = m_run == m_new ? 1.f : __builtin_amdgcn_exp2f(m_run + mneg);
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    bf16x4_t pb;
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, mneg));
+      ps += p;
+      pb[e] = (__bf16)p;
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    const s16x4v pf = __builtin_bit_cast(s16x4v, pb);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const s16x4 vf =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((const lds_u8*)vc + voff[dt]));
+      oacc[dt] *= alpha;
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4v, vf), pf,
+                                                           oacc[dt], 0, 0, 0);
+    }
+  };
+  uint4 k0[KS], k1[KS];
+  if (nblk > 0) load(0, k0, vt0);
+#pragma unroll 1
+  for (int b = 0; b < nblk; b += 2) {
+    step(b, k0, k1, vt0, vt1);
+    if (b + 1 < nblk) step(b + 1, k1, k0, vt1, vt0);
+  }
+
+  // merge the four waves' states: lane holds row lr, d = 16*dt + 4*lg + e
+  __syncthreads();  // the V slots are free: waves 0-1 park their sums in vt0, 2-3 in vt1
+  float* s_o = reinterpret_cast<float*>(w < 2 ? vt0 : vt1) + (w % 2) * 16 * D;
+  if (lg == 0) {
+    s_m[w][lr] = m_run;
+    s_l[w][lr] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_o[lr * D + 16 * dt + 4 * lg + e] = oacc[dt][e];
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
+    float m = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) m = fmaxf(m, s_m[ww][r]);
+    float lsum = 0.f, acc = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[ww][r] - m);
+      const float* so = reinterpret_cast<const float*>(ww < 2 ? vt0 : vt1) + (ww % 2) * 16 * D;
+      lsum += a * s_l[ww][r];
+      acc += a * so[r * D + d];
+    }
+    float* dst = ws + (((int64_t)bhk * G + r) * nsplit + split) * (D + 2);
+    if (d == 0) {
+      dst[0] = m;
+      dst[1] = lsum;
+    }
+    dst[2 + d] = acc;
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(64) void attn_decode_combine(const float* __restrict__ ws,
                                                           T* __restrict__ o,
@@ -1065,10 +1261,9 @@ hipError_t launch_attn_d(const PyrGeom& g, int dtype, const void* q, const void*
     const int ns = decode_splits(g.K);
     float* wsf = static_cast<float*>(ws);
     if (dtype == 1) {
-      hipLaunchKernelGGL((attn_decode_split<bf16_t, D>), dim3((unsigned)(units * ns)),
-                         dim3(kDecThreads), 0, st, static_cast<const bf16_t*>(q),
-                         static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), sel, wsf,
-                         g, ns);
+      hipLaunchKernelGGL((attn_decode_mfma<D>), dim3((unsigned)(units * ns)), dim3(256), 0, st,
+                         static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                         static_cast<const bf16_t*>(v), sel, wsf, g, ns);
       hipLaunchKernelGGL((attn_decode_combine<bf16_t, D>), dim3((unsigned)(units * g.G)),
                          dim3(64), 0, st, wsf, static_cast<bf16_t*>(o), lse, g, ns);
     } else {
