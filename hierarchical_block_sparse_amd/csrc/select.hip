@@ -411,7 +411,9 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
     blank_unit(g, unit, sel, trace_ids, trace_scores);
     return;
   }
-  const int diag = i;
+  // decode: one query block whose token sits at kv_len - 1; its G rows (one
+  // per query head) fill the first M tile of wave 0, every other row is idle
+  const int diag = g.decode ? (int)((g.Tk - 1) / PYR_BLOCK) : i;
   const int Ku = unit_budget(g, hk);
   const int RW = MT * 16;  // rows per wave
   const float sl2 = g.scale * PYR_LOG2E;
@@ -427,19 +429,28 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int ra = w * RW + mt * 16 + (l % 16);
-    const int h = ra / PYR_BLOCK, t = ra % PYR_BLOCK;
-    const int64_t tok = min<int64_t>((int64_t)i * PYR_BLOCK + t, sq.Tq - 1);
+    int h;
+    int64_t tok;
+    if (g.decode) {
+      h = ra < g.G ? ra : g.G - 1;
+      tok = 0;
+    } else {
+      h = ra / PYR_BLOCK;
+      tok = min<int64_t>((int64_t)i * PYR_BLOCK + ra % PYR_BLOCK, sq.Tq - 1);
+    }
     const bf16_t* qrow = q + (sq.q0 + ((int64_t)hk * g.G + h) * sq.qhs + tok) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) qa[mt][ks] = ld16(qrow + ks * 32 + 8 * (l / 16));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rc = w * RW + mt * 16 + 4 * (l / 16) + j;
-      if ((int64_t)i * PYR_BLOCK + rc % PYR_BLOCK < sq.Tq) rowvalid |= 1u << (mt * 4 + j);
+      const bool real = g.decode ? rc < g.G : (int64_t)i * PYR_BLOCK + rc % PYR_BLOCK < sq.Tq;
+      if (real) rowvalid |= 1u << (mt * 4 + j);
     }
   }
 
-  const bool full = (int64_t)(i + 1) * PYR_BLOCK <= sq.Tq;  // every row of the unit is real
+  // every row of the unit is real
+  const bool full = !g.decode && (int64_t)(i + 1) * PYR_BLOCK <= sq.Tq;
   // plane 1 of the slab: the split rows
   const unsigned char* split =
       reinterpret_cast<const unsigned char*>(pyr + (bhk * g.planes + 1) * g.n_tot * D);
@@ -620,7 +631,8 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
 }
 
 int mfma_tiles(const PyrGeom& g, int dtype) {
-  if (dtype != 1 || g.decode) return 0;
+  if (dtype != 1) return 0;
+  if (g.decode) return g.G <= 16 ? 1 : 0;  // the G rows in one 16-row tile
   switch (g.G) {
     case 1: return 1;
     case 2: return 2;
