@@ -48,7 +48,7 @@ struct SelLayout {
   int cmax;  // candidate capacity: b*K + b - 1, rounded up to the chunk size
   int off_kept, off_kscore, off_cand, off_score, off_rank, off_part, off_misc, off_hl, off_zbuf;
   int total;  // bytes
-  __host__ __device__ SelLayout(int K, int b, int D, bool mfma) {
+  __host__ __device__ SelLayout(int K, int b, int D, bool mfma, int waves = kWaves) {
     cmax = (b * K + b - 1 + kChunk - 1) / kChunk * kChunk;
     const int kp = (K + 3) & ~3;
     int o = 0;
@@ -58,7 +58,7 @@ struct SelLayout {
     off_score = o;  o += 4 * cmax;  // 16-byte aligned: read as float4
     off_rank = o;   o += 4 * cmax;
     if (mfma) {
-      off_part = o;  o += 8 * kWaves * cmax;                // float2 [wave][candidate]
+      off_part = o;  o += 8 * waves * cmax;                 // float2 [wave][candidate]
       off_misc = o;  o += 4 * (PYR_MAX_LEVELS + 4);         // int ancestors, kept count
       off_hl = off_zbuf = o;
     } else {
@@ -136,6 +136,7 @@ __device__ __forceinline__ void keep_chunk(int j, uint32_t kj, int C, uint32_t T
 // order.  *margin gets the K-th best score minus the best rejected one (NaN
 // when nothing is rejected).  The trace row is g.K wide: slots past K hold -1
 // (ids) and NaN (scores), slot g.K of the scores the best rejected score.
+template <int NT>
 __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* cand,
                                 const float* score, int* rank, int* kept, float* kscore,
                                 int* nkept, int K, float* margin, int32_t* tr_ids,
@@ -201,10 +202,10 @@ __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* c
   }
   __syncthreads();
   if (tr_ids) {
-    for (int j = tid; j < g.K; j += kThreads) tr_ids[level * g.K + j] = j < K ? kept[j] : -1;
+    for (int j = tid; j < g.K; j += NT) tr_ids[level * g.K + j] = j < K ? kept[j] : -1;
   }
   if (tr_scores) {
-    for (int j = tid; j < g.K; j += kThreads)
+    for (int j = tid; j < g.K; j += NT)
       tr_scores[level * (g.K + 1) + j] = j < K ? kscore[j] : NAN;
   }
 }
@@ -231,6 +232,7 @@ __device__ __forceinline__ bool fallback_due(const PyrGeom& g, int level, int kk
 
 // Candidates of one level into cand[]; returns the count.  Must be called by
 // every thread (ends with a barrier).
+template <int NT>
 __device__ int build_candidates(const PyrGeom& g, int level, const int* s_anc, const int* kept,
                                 int nkept, int* cand) {
   const int b = g.branching;
@@ -245,42 +247,45 @@ __device__ int build_candidates(const PyrGeom& g, int level, const int* s_anc, c
     base = s_anc[level + 1] * b;
     C = nchild + (anc - base);
   }
-  for (int j = threadIdx.x; j < C; j += kThreads)
+  for (int j = threadIdx.x; j < C; j += NT)
     cand[j] = j < nchild ? kept[j / b] * b + j % b : base + (j - nchild);
   __syncthreads();
   return C;
 }
 
 // Levels with <= K candidates keep them all (no scoring).
+template <int NT>
 __device__ void keep_all(const PyrGeom& g, int C, int level, const int* cand, int* kept,
                          int* nkept, int32_t* tr_ids, float* tr_scores) {
   const int K = g.K;
-  for (int j = threadIdx.x; j < K; j += kThreads) {
+  for (int j = threadIdx.x; j < K; j += NT) {
     const int id = j < C ? cand[j] : -1;
     kept[j] = id;
     if (tr_ids) tr_ids[level * K + j] = id;
   }
   if (tr_scores)
-    for (int j = threadIdx.x; j <= K; j += kThreads) tr_scores[level * (K + 1) + j] = NAN;
+    for (int j = threadIdx.x; j <= K; j += NT) tr_scores[level * (K + 1) + j] = NAN;
   if (threadIdx.x == 0) *nkept = C;
   __syncthreads();
 }
 
+template <int NT>
 __device__ __forceinline__ void write_route(const PyrGeom& g, int64_t unit, const int* kept,
                                             int nk, int diag, int32_t* sel) {
   int32_t* out = sel + unit * (g.K + 1);
-  for (int j = threadIdx.x; j <= g.K; j += kThreads) out[j] = j < nk ? kept[j] : (j == nk ? diag : -1);
+  for (int j = threadIdx.x; j <= g.K; j += NT) out[j] = j < nk ? kept[j] : (j == nk ? diag : -1);
 }
 
 // A unit past the end of a shorter packed sequence: its route row (and trace)
 // hold nothing.
+template <int NT>
 __device__ void blank_unit(const PyrGeom& g, int64_t unit, int32_t* sel, int32_t* trace_ids,
                            float* trace_scores) {
-  for (int j = threadIdx.x; j <= g.K; j += kThreads) sel[unit * (g.K + 1) + j] = -1;
+  for (int j = threadIdx.x; j <= g.K; j += NT) sel[unit * (g.K + 1) + j] = -1;
   if (trace_ids)
-    for (int j = threadIdx.x; j < g.L * g.K; j += kThreads) trace_ids[unit * g.L * g.K + j] = -1;
+    for (int j = threadIdx.x; j < g.L * g.K; j += NT) trace_ids[unit * g.L * g.K + j] = -1;
   if (trace_scores)
-    for (int j = threadIdx.x; j < g.L * (g.K + 1); j += kThreads)
+    for (int j = threadIdx.x; j < g.L * (g.K + 1); j += NT)
       trace_scores[unit * g.L * (g.K + 1) + j] = NAN;
 }
 
@@ -295,28 +300,28 @@ typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
 // Split rows of chunk c's candidates (plane 1 of the pyramid: per node a bf16
 // hi row and a bf16 lo row, 4D bytes) into one LDS stage with direct 16-byte
 // loads, no register staging.  Load t of a thread fills stage chunk
-// p = t * kThreads + tid (the 64 lanes of a wave fill 1 KiB in lane order):
+// p = t * NT + tid (the 64 lanes of a wave fill 1 KiB in lane order):
 // candidate p / CPC, row part (p % CPC) / CPR (hi, lo), stored chunk q =
 // p % CPR, which holds logical chunk q ^ (candidate % CPR) of that row, so the
 // 16 candidates of an MFMA B fragment lie in different banks.  Positions past
 // C load candidate 0 (finite values that are never scored).
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void issue_chunk(const unsigned char* split, const int* cand, int C,
                                             int c, unsigned char* stage, int w, int l) {
   constexpr int CPR = D / 8;       // 16-byte chunks per bf16 row
   constexpr int CPC = 2 * CPR;     // per candidate (hi, lo)
-  constexpr int PER = kChunk * CPC / kThreads;
-  static_assert(kChunk * CPC % kThreads == 0, "chunk must split evenly");
+  constexpr int PER = kChunk * CPC / NT;
+  static_assert(kChunk * CPC % NT == 0, "chunk must split evenly");
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
-    const int p = t * kThreads + w * 64 + l;
+    const int p = t * NT + w * 64 + l;
     const int cc = p / CPC, part = (p % CPC) / CPR, q = p % CPR;
     const int j = c * kChunk + cc;
     const int node = cand[j < C ? j : 0];
     const unsigned char* src =
         split + (int64_t)node * 4 * D + part * 2 * D + ((q ^ (cc % CPR)) << 4);
     __builtin_amdgcn_global_load_lds((const void*)src,
-                                     (lds_void*)(stage + (t * kThreads + w * 64) * 16), 16, 0, 0);
+                                     (lds_void*)(stage + (t * NT + w * 64) * 16), 16, 0, 0);
   }
 }
 
@@ -369,9 +374,10 @@ __device__ __forceinline__ void tile_lse(const f32x4 (&acc)[MT], uint32_t rowval
   s = sum32(sum16(s));
 }
 
-// Four M tiles (G = 4) fit 168 VGPRs, so three workgroups share a CU.
-template <int D, int MT>
-__global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const bf16_t* __restrict__ q,
+// NW waves of MT M tiles each.  Four M tiles fit 168 VGPRs, so three
+// four-wave workgroups share a CU (G = 4); G = 8 runs eight such waves.
+template <int D, int MT, int NW>
+__global__ __launch_bounds__(NW * 64, MT == 4 ? (NW == 4 ? 3 : 2) : 1) void select_mfma(const bf16_t* __restrict__ q,
                                                         const float* __restrict__ pyr,
                                                         int32_t* __restrict__ sel,
                                                         int32_t* __restrict__ trace_ids,
@@ -379,13 +385,12 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
                                                         PyrGeom g) {
   constexpr int CPR = D / 8;                               // 16-byte chunks per bf16 row
   constexpr int STAGE = kChunk * 4 * D;                    // bytes per LDS stage
-  constexpr int PER = kChunk * 2 * CPR / kThreads;         // chunk loads per thread
 
   // All LDS is the one dynamic array: with a second __shared__ variable the
   // compiler would give each its own alias scope and wait for every chunk load
   // in flight before any LDS read, undoing the prefetch.
   extern __shared__ __align__(16) unsigned char smem[];
-  const SelLayout lay(g.K, g.branching, D, true);
+  const SelLayout lay(g.K, g.branching, D, true, NW);
   int* kept = reinterpret_cast<int*>(smem + lay.off_kept);
   float* kscore = reinterpret_cast<float*>(smem + lay.off_kscore);
   int* cand = reinterpret_cast<int*>(smem + lay.off_cand);
@@ -408,7 +413,7 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
   const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
   const PyrSeq sq = pyr_seq(g, bi);
   if (i >= sq.nqb) {
-    blank_unit(g, unit, sel, trace_ids, trace_scores);
+    blank_unit<NW * 64>(g, unit, sel, trace_ids, trace_scores);
     return;
   }
   // decode: one query block whose token sits at kv_len - 1; its G rows (one
@@ -459,22 +464,22 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
   __syncthreads();
 
   for (int level = g.L - 1; level >= 0; --level) {
-    const int C = build_candidates(g, level, s_anc, kept, s_nkept, cand);
+    const int C = build_candidates<NW * 64>(g, level, s_anc, kept, s_nkept, cand);
     if (C <= Ku) {
-      keep_all(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
+      keep_all<NW * 64>(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
       continue;
     }
     const unsigned char* lvl = split + g.loff[level] * 4 * D;
     const int nchunks = (C + kChunk - 1) / kChunk;
     // chunk c+1 loads while chunk c is scored; stage of chunk c is c % 2
-    issue_chunk<D>(lvl, cand, C, 0, stages, w, l);
+    issue_chunk<D, NW * 64>(lvl, cand, C, 0, stages, w, l);
     for (int c = 0; c < nchunks; ++c) {
       // this wave's loads of chunk c have landed; after the barrier every
       // wave's have, and the stage of chunk c-1 is free
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       lds_barrier();
       if (c + 1 < nchunks)
-        issue_chunk<D>(lvl, cand, C, c + 1, stages + ((c + 1) % kSelStages) * STAGE, w, l);
+        issue_chunk<D, NW * 64>(lvl, cand, C, c + 1, stages + ((c + 1) % kSelStages) * STAGE, w, l);
       const unsigned char* st = stages + (c % kSelStages) * STAGE;
 #pragma unroll
       for (int nt = 0; nt < kChunk / 16; ++nt) {
@@ -508,10 +513,10 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
       }
     }
     __syncthreads();
-    for (int j = tid; j < C; j += kThreads) {
+    for (int j = tid; j < C; j += NW * 64) {
       float m = -INFINITY, s = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
+      for (int ww = 0; ww < NW; ++ww) {
         const f32x2 p = part[ww * cmax + j];
         lse2_merge(m, s, p.x, p.y);
       }
@@ -520,13 +525,13 @@ __global__ __launch_bounds__(kThreads, MT == 4 ? 3 : 1) void select_mfma(const b
     }
     __syncthreads();
     for (int kk = Ku;;) {
-      top_k_and_trace(g, C, level, cand, score, rank, kept, kscore, &s_nkept, kk, s_margin,
+      top_k_and_trace<NW * 64>(g, C, level, cand, score, rank, kept, kscore, &s_nkept, kk, s_margin,
                       tr_ids, tr_sc);
       if (!fallback_due(g, level, kk, Ku, s_margin)) break;
       kk = C < g.fb_k ? C : g.fb_k;  // keep more of the same candidates
     }
   }
-  write_route(g, unit, kept, s_nkept, diag, sel);
+  write_route<NW * 64>(g, unit, kept, s_nkept, diag, sel);
 }
 
 // ---------------------------------------------------------------------------
@@ -560,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
   const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
   const PyrSeq sq = pyr_seq(g, bi);
   if (i >= sq.nqb) {
-    blank_unit(g, unit, sel, trace_ids, trace_scores);
+    blank_unit<kThreads>(g, unit, sel, trace_ids, trace_scores);
     return;
   }
   int64_t tok0, ntok;
@@ -586,9 +591,9 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
   __syncthreads();
 
   for (int level = g.L - 1; level >= 0; --level) {
-    const int C = build_candidates(g, level, s_anc, kept, s_nkept, cand);
+    const int C = build_candidates<kThreads>(g, level, s_anc, kept, s_nkept, cand);
     if (C <= Ku) {
-      keep_all(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
+      keep_all<kThreads>(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
       continue;
     }
     const float* lvl = slab + g.loff[level] * D;
@@ -621,13 +626,13 @@ __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
       __syncthreads();
     }
     for (int kk = Ku;;) {
-      top_k_and_trace(g, C, level, cand, score, rank, kept, kscore, &s_nkept, kk, s_margin,
+      top_k_and_trace<kThreads>(g, C, level, cand, score, rank, kept, kscore, &s_nkept, kk, s_margin,
                       tr_ids, tr_sc);
       if (!fallback_due(g, level, kk, Ku, s_margin)) break;
       kk = C < g.fb_k ? C : g.fb_k;  // keep more of the same candidates
     }
   }
-  write_route(g, unit, kept, s_nkept, diag, sel);
+  write_route<kThreads>(g, unit, kept, s_nkept, diag, sel);
 }
 
 int mfma_tiles(const PyrGeom& g, int dtype) {
@@ -649,14 +654,16 @@ hipError_t launch_select_d(const PyrGeom& g, int dtype, const void* q, const flo
   if (units == 0) return hipSuccess;
   const int mt = mfma_tiles(g, dtype);
   const dim3 grid((unsigned)((units + 7) / 8 * 8)), block(kThreads);  // whole runs per XCD
-  const size_t lds = SelLayout(g.K, g.branching, D, mt != 0).total;
+  const size_t lds = SelLayout(g.K, g.branching, D, mt != 0, mt == 8 ? 8 : kWaves).total;
   if (mt) {
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     switch (mt) {
-      case 1: hipLaunchKernelGGL((select_mfma<D, 1>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
-      case 2: hipLaunchKernelGGL((select_mfma<D, 2>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
-      case 4: hipLaunchKernelGGL((select_mfma<D, 4>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
-      default: hipLaunchKernelGGL((select_mfma<D, 8>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
+      case 1: hipLaunchKernelGGL((select_mfma<D, 1, 4>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
+      case 2: hipLaunchKernelGGL((select_mfma<D, 2, 4>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
+      case 4: hipLaunchKernelGGL((select_mfma<D, 4, 4>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
+      default:  // G = 8: eight waves of four M tiles
+        hipLaunchKernelGGL((select_mfma<D, 4, 8>), grid, dim3(512), lds, st, qq, pyr, sel, tid_, tsc, g);
+        break;
     }
   } else if (dtype == 1) {
     hipLaunchKernelGGL((select_valu<bf16_t, D>), grid, block, lds, st,
@@ -673,7 +680,7 @@ hipError_t launch_select_d(const PyrGeom& g, int dtype, const void* q, const flo
 size_t pyr_select_lds_bytes(const PyrGeom& g, int dtype) {
   const bool mfma = mfma_tiles(g, dtype) != 0;
   // dynamic layout, plus the candidate stages of the MFMA path (a static array)
-  return SelLayout(g.K, g.branching, g.D, mfma).total +
+  return SelLayout(g.K, g.branching, g.D, mfma, mfma_tiles(g, dtype) == 8 ? 8 : kWaves).total +
          (mfma ? (size_t)kSelStages * kChunk * 4 * g.D : 0);
 }
 
