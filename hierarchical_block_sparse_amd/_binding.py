@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libpyr.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "pyr.h")
 
 PYR_F32, PYR_BF16 = 0, 1
+ABI_VERSION = 3  # PYR_ABI_VERSION of the include/pyr.h these wrappers marshal for
 STATUS = {0: "PYR_OK", 1: "PYR_ERR_NULL", 2: "PYR_ERR_INVALID", 3: "PYR_ERR_UNSUPPORTED",
           4: "PYR_ERR_MISALIGNED", 5: "PYR_ERR_WORKSPACE", 6: "PYR_ERR_HIP"}
 
@@ -80,6 +81,9 @@ def lib():
         ]:
             fn = getattr(L, name)
             fn.restype, fn.argtypes = res, args
+        if L.pyr_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.pyr_abi_version()}, these "
+                               f"wrappers need {ABI_VERSION}: rebuild it")
         _lib_handle = L
     return _lib_handle
 
