@@ -55,6 +55,8 @@ def parse():
                     help="units of the workload the oracle runs for the CPU baseline (0: skip)")
     ap.add_argument("--packed", action="store_true",
                     help="cut the workload's tokens into a packed batch of mixed-length sequences")
+    ap.add_argument("--fused", action="store_true",
+                    help="selection and attention in one pyr_select_attn call per step")
     ap.add_argument("--backward", action="store_true",
                     help="time the training pass (forward + backward of the attention)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -83,11 +85,23 @@ def calibrate_copy():
 # algorithmic work (the per-unit figures are derived in the design doc)
 # ---------------------------------------------------------------------------
 
+def _num_blocks(n_tokens):
+    """64-token blocks covering n_tokens tokens (the last may be ragged)."""
+    return -(-n_tokens // 64)
+
+
+def _level_sizes(n_blocks, b):
+    """Nodes per pyramid level, finest first, down to the single root."""
+    sizes = [n_blocks] if n_blocks > 0 else []
+    while sizes and sizes[-1] > 1:
+        sizes.append(-(-sizes[-1] // b))
+    return sizes
+
+
 def attn_work(cfg):
     """(flops, bytes) of the attention over the selection: every attended
     (query row, key) pair costs 4d flops (QK^T and PV); bytes = Q read + O write
     + the gathered K and V tiles of every selected block, once per unit."""
-    from oracle.reference import num_blocks  # geometry only
     s = 2 if cfg.dtype.itemsize == 2 else 4
     d, G, K = cfg.head_dim, cfg.group, cfg.top_k
     bh = cfg.batch * cfg.n_kv_heads
@@ -97,7 +111,7 @@ def attn_work(cfg):
         flops = bh * G * keys * 4 * d
         byts = bh * (2 * G * d * s + 2 * keys * d * s)
         return flops, byts
-    nqb = num_blocks(cfg.q_len, 64)
+    nqb = _num_blocks(cfg.q_len)
     pairs = sum(min(K, i) * 64 * 64 + 64 * 65 // 2 for i in range(nqb))
     tiles = sum(min(K, i) + 1 for i in range(nqb))
     flops = bh * G * pairs * 4 * d
@@ -130,9 +144,8 @@ def scored_candidates(cfg):
     """Total candidates scored over all units (levels with more than K
     candidates), from the selection geometry: every scored level of a unit
     has b*K children of kept nodes plus the ancestor's fully-past children."""
-    from oracle.reference import level_sizes, num_blocks
     b, K = cfg.branching, cfg.top_k
-    sizes = level_sizes(num_blocks(cfg.kv_len, 64), b)
+    sizes = _level_sizes(_num_blocks(cfg.kv_len), b)
     L = len(sizes)
     diags = [(cfg.kv_len - 1) // 64] if cfg.decode else range(-(-cfg.q_len // 64))
     total = 0
@@ -222,17 +235,27 @@ def attn_kernel_name(cfg):
     return "attn_prefill_pp" if cfg.group % 4 == 0 else "attn_prefill_mfma"
 
 
+def fused_kernel(cfg):
+    """Whether pyr_select_attn runs as one launch for this workload (bfloat16
+    prefill, four query heads per KV head, branching * (top_k + 1) <= 192)."""
+    import torch
+    return (cfg.dtype == torch.bfloat16 and not cfg.decode and cfg.group == 4
+            and cfg.branching * (cfg.top_k + 1) <= 192)
+
+
 def kernel_traffic(workload, kind="attn"):
     """HBM bytes per dispatch of the dominant kernel from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_pmc.json")
-    src = os.path.join(ROOT, "hierarchical_block_sparse_amd", "csrc", f"{kind}.hip")
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(src, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
-        if rec.get("attn_src_sha256") != digest:
+        # the SHA-256 of the kernel's source files, concatenated in the listed order
+        h = hashlib.sha256()
+        for name in rec.get("sources", [f"{kind}.hip"]):
+            with open(os.path.join(ROOT, "hierarchical_block_sparse_amd", "csrc", name), "rb") as f:
+                h.update(f.read())
+        if rec.get("attn_src_sha256") != h.hexdigest():
             return None
         return rec.get("bytes_per_dispatch")
     except (OSError, ValueError):
@@ -256,6 +279,9 @@ def main():
     cfg = W.CONFIGS[args.workload]
     if args.backward and (cfg.decode or cfg.dtype != torch.bfloat16):
         print(json.dumps({"error": "the backward runs on bfloat16 prefill workloads"}), flush=True)
+        sys.exit(2)
+    if args.fused and (cfg.decode or args.backward):
+        print(json.dumps({"error": "--fused takes a prefill workload, forward only"}), flush=True)
         sys.exit(2)
     if args.packed and (cfg.decode or args.backward or cfg.batch != 1):
         print(json.dumps({"error": "--packed takes a batch-1 prefill workload, forward only"}),
@@ -306,12 +332,18 @@ def main():
             H.pyr_build_pyramid(p, k, pyr, stream)
         if events:
             events[1].record(stream)
-        H.pyr_select_topk(p, q, pyr, sel, None, None, stream)
-        if events:
-            events[2].record(stream)
-        H.pyr_block_sparse_attn(p, q, k, v, sel, o, lse, ws, stream)
-        if events:
-            events[3].record(stream)
+        if args.fused:
+            H.pyr_select_attn(p, q, k, v, pyr, sel, o, lse, ws, None, None, stream)
+            if events:
+                events[2].record(stream)
+                events[3].record(stream)
+        else:
+            H.pyr_select_topk(p, q, pyr, sel, None, None, stream)
+            if events:
+                events[2].record(stream)
+            H.pyr_block_sparse_attn(p, q, k, v, sel, o, lse, ws, stream)
+            if events:
+                events[3].record(stream)
         if args.backward:
             H.pyr_block_sparse_attn_bwd(p, q, k, v, sel, o, lse, dout, dq, dk, dv, bws, stream)
             if events:
@@ -337,14 +369,17 @@ def main():
     a_flops = sum(attn_work(c)[0] for c in parts)
     a_bytes = sum(attn_work(c)[1] for c in parts)
     if lengths:
-        from oracle.reference import level_sizes  # geometry only
-        b_bytes = sum(build_bytes(c, sum(level_sizes(-(-c.kv_len // 64), c.branching)),
-                                  H.pyr_pyramid_planes(p)) for c in parts)
+        # each sequence's pyramid: the nodes of a dense problem of its length
+        b_bytes = sum(build_bytes(c, H.pyr_pyramid_nodes(H.Problem(
+            1, c.n_q_heads, c.n_kv_heads, c.head_dim, c.q_len, c.kv_len, c.branching, c.top_k,
+            c.dtype)), H.pyr_pyramid_planes(p)) for c in parts)
     else:
         b_bytes = build_bytes(cfg, H.pyr_pyramid_nodes(p), H.pyr_pyramid_planes(p))
     s_flops = sum(select_work(c, scored_candidates(c))[0] for c in parts)
     s_bytes = sum(select_work(c, scored_candidates(c))[1] for c in parts)
     t_build, t_sel, t_attn = (x / 1e3 for x in stage_ms[:3])
+    if args.fused:   # one launch: the stage of the selection holds both
+        t_sel = t_attn = stage_ms[1] / 1e3
     achieved = a_flops / t_attn / 1e12
     traffic = kernel_traffic(cfg.name + ("_packed" if lengths else ""))
     line = {
@@ -392,6 +427,29 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.fused:
+        # one kernel does the selection's scoring and the attention: its
+        # algorithmic flops are both (scores counted once per dot product)
+        f_flops = a_flops + s_flops
+        t_f = stage_ms[1] / 1e3
+        line["config"]["step"] = "build+select_attn (one fused launch)"
+        line["roofline"] = {
+            "kernel": "select_attend" if fused_kernel(cfg) else "select+attn (two launches)",
+            "bound": "mfma",
+            "achieved": round(f_flops / t_f / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(f_flops / t_f / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": kernel_traffic(cfg.name + ("_packed" if lengths else "") + "_fused"),
+            "algorithmic_flops_per_launch": f_flops,
+            "attention_flops": a_flops,
+            "selection_flops": s_flops,
+            "avg_launch_ms": round(stage_ms[1], 4),
+        }
+        line["stages"] = {
+            "build": line["stages"]["build"],
+            "select_attn": {"ms": round(stage_ms[1], 4), "TFLOP/s": round(f_flops / t_f / 1e12, 2)},
+        }
     if lengths:
         line["metric"] = METRIC_PACKED
         line["config"].update({

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libpyr.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "pyr.h")
 
 PYR_F32, PYR_BF16 = 0, 1
-ABI_VERSION = 3  # PYR_ABI_VERSION of the include/pyr.h these wrappers marshal for
+ABI_VERSION = 4  # PYR_ABI_VERSION of the include/pyr.h these wrappers marshal for
 STATUS = {0: "PYR_OK", 1: "PYR_ERR_NULL", 2: "PYR_ERR_INVALID", 3: "PYR_ERR_UNSUPPORTED",
           4: "PYR_ERR_MISALIGNED", 5: "PYR_ERR_WORKSPACE", 6: "PYR_ERR_HIP"}
 
@@ -72,6 +72,8 @@ def lib():
             ("pyr_budgets_from_entropy", st,
              [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]),
             ("pyr_block_sparse_attn", st, [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+            ("pyr_select_attn", st,
+             [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
             ("pyr_attn_bwd_workspace_bytes", ctypes.c_size_t, [P]),
             ("pyr_block_sparse_attn_bwd", st,
              [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
@@ -295,6 +297,31 @@ def pyr_block_sparse_attn(p: Problem, q, k, v, sel, o, lse=None, workspace=None,
                                        _stream(stream)))
 
 
+def pyr_select_attn(p: Problem, q, k, v, pyramid, sel, o, lse=None, workspace=None,
+                    trace_ids=None, trace_scores=None, stream=None):
+    """Selection and attention in one call (one fused launch where the library
+    has one for the problem): writes sel (and the traces), o and lse."""
+    nqb, L = pyr_num_query_blocks(p), pyr_num_levels(p)
+    _expect(q, "q", p.q_shape, p.dtype)
+    _expect(k, "k", p.kv_shape, p.dtype)
+    _expect(v, "v", p.kv_shape, p.dtype)
+    _expect(pyramid, "pyramid", pyramid_shape(p), torch.float32)
+    _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
+    _expect(trace_ids, "trace_ids", (p.batch, p.n_kv_heads, nqb, L, p.top_k), torch.int32)
+    _expect(trace_scores, "trace_scores", (p.batch, p.n_kv_heads, nqb, L, p.top_k + 1),
+            torch.float32)
+    _expect(o, "o", p.q_shape, p.dtype)
+    _expect(lse, "lse", p.lse_shape, torch.float32)
+    nbytes = 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace: must be a contiguous cuda tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().pyr_select_attn(_cp(p), _ptr(q), _ptr(k), _ptr(v), _ptr(pyramid), _ptr(sel),
+                                 _ptr(trace_ids), _ptr(trace_scores), _ptr(o), _ptr(lse),
+                                 _ptr(workspace), nbytes, _stream(stream)))
+
+
 def pyr_attn_bwd_workspace_bytes(p: Problem) -> int:
     return lib().pyr_attn_bwd_workspace_bytes(_cp(p))
 
@@ -368,8 +395,9 @@ def problem_for(q, k, branching: int, top_k: int, scale: float = 0.0) -> Problem
 
 
 def forward(q, k, v, branching: int, top_k: int, scale: float = 0.0, pyramid=None,
-            with_trace: bool = False):
-    """The whole path: build the pyramid (unless given), select, attend.
+            with_trace: bool = False, fused: bool = False):
+    """The whole path: build the pyramid (unless given), select, attend (with
+    fused=True, selection and attention in one pyr_select_attn call).
     Returns (o, lse, sel, pyramid[, (trace_ids, trace_scores)])."""
     p = problem_for(q, k, branching, top_k, scale)
     if pyramid is None:
@@ -377,10 +405,13 @@ def forward(q, k, v, branching: int, top_k: int, scale: float = 0.0, pyramid=Non
         pyr_build_pyramid(p, k, pyramid)
     sel = alloc_sel(p, q.device)
     trace = alloc_trace(p, q.device) if with_trace else (None, None)
-    pyr_select_topk(p, q, pyramid, sel, *trace)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    pyr_block_sparse_attn(p, q, k, v, sel, o, lse, alloc_workspace(p, q.device))
+    if fused:
+        pyr_select_attn(p, q, k, v, pyramid, sel, o, lse, alloc_workspace(p, q.device), *trace)
+    else:
+        pyr_select_topk(p, q, pyramid, sel, *trace)
+        pyr_block_sparse_attn(p, q, k, v, sel, o, lse, alloc_workspace(p, q.device))
     if with_trace:
         return o, lse, sel, pyramid, trace
     return o, lse, sel, pyramid

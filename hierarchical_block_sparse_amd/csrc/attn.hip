@@ -32,6 +32,7 @@
 
 #include "pyr_device.h"
 #include "pyr_internal.h"
+#include "select_core.h"
 
 namespace {
 
@@ -631,28 +632,21 @@ __device__ __forceinline__ void pp_block(const PpRun<D>& r, int x, const FragOff
   pp_matrix<D, DO_S, true>((lds_u8*)pp_k<JN>(x + 1), (lds_u8*)pp_v<J>(x), fo, qb, s, p, oacc);
 }
 
+// Attention of one unit's four query heads sub*4 .. sub*4+3 of KV head hk by
+// the eight waves of the workgroup.  s_sel holds the unit's route row (K+1
+// entries, visible to every thread); s_ord and s_cnt are LDS scratch.  Must be
+// called by every thread.
 template <int D>
-__global__ __launch_bounds__(512, 2) void attn_prefill_pp(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const int32_t* __restrict__ sel, bf16_t* __restrict__ o, float* __restrict__ lse, PyrGeom g,
-    int wg_per_unit) {
+__device__ __forceinline__ void pp_unit(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                        const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
+                                        float* __restrict__ lse, const PyrGeom& g, int hk, int i,
+                                        int sub, const PyrSeq& sq, const int* s_sel, int* s_ord,
+                                        int* s_cnt) {
   using TG = TileGeom<D>;
-  constexpr int NT = 512;
-  constexpr int NLOAD = 2 * (TG::CPR / 8);  // tile-load instructions per block per wave
   static_assert(TG::TILE <= kPpTile, "tile slots are sized for d <= 128");
-  __shared__ int s_sel[kMaxSel];
-  __shared__ int s_ord[kMaxSel];
-  __shared__ int s_n, s_nun;
-
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int half = l / 32, lr = l % 32;
-  const int sub = (int)(blockIdx.x % wg_per_unit);
-  int bi, hk, i;
-  int64_t unit;
-  unit_of(g, blockIdx.x / wg_per_unit, bi, hk, i, unit);
-  const PyrSeq sq = pyr_seq(g, bi);
-  if (i >= sq.nqb) return;  // past the end of a shorter packed sequence
   // waves 2h and 2h+1 take the two 32-row halves of head sub*4 + h; waves
   // 0-3 form group 0, waves 4-7 group 1
   const int h = hk * g.G + sub * 4 + w / 2;
@@ -660,8 +654,6 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_pp(
   const int64_t row0 = (int64_t)i * PYR_BLOCK + (w % 2) * 32;
   const float sl2 = g.scale * PYR_LOG2E;
 
-  for (int jj = tid; jj <= g.K; jj += NT) s_sel[jj] = sel[unit * (g.K + 1) + jj];
-  __syncthreads();
   // route order: valid blocks before the unit's own block first (no mask
   // needed), then the rest (the diagonal block)
   if (w == 0) {
@@ -680,12 +672,12 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_pp(
       if (pass == 0) nun = n;
     }
     if (l == 0) {
-      s_n = n;
-      s_nun = nun;
+      s_cnt[0] = n;
+      s_cnt[1] = nun;
     }
   }
   __syncthreads();
-  const int nsel = s_n, nun = s_nun;
+  const int nsel = s_cnt[0], nun = s_cnt[1];
   const bf16_t* kh = k + (sq.k0 + hk * sq.khs) * D;
   const bf16_t* vh = v + (sq.k0 + hk * sq.khs) * D;
 
@@ -774,6 +766,63 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_pp(
     }
   if (lse && half == 0)
     lse[sq.q0 + h * sq.qhs + tok] = lt > 0.f ? (m_run + log2f(lt)) * PYR_LN2 : -INFINITY;
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 2) void attn_prefill_pp(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const int32_t* __restrict__ sel, bf16_t* __restrict__ o, float* __restrict__ lse, PyrGeom g,
+    int wg_per_unit) {
+  __shared__ int s_sel[kMaxSel];
+  __shared__ int s_ord[kMaxSel];
+  __shared__ int s_cnt[2];
+  const int sub = (int)(blockIdx.x % wg_per_unit);
+  int bi, hk, i;
+  int64_t unit;
+  unit_of(g, blockIdx.x / wg_per_unit, bi, hk, i, unit);
+  const PyrSeq sq = pyr_seq(g, bi);
+  if (i >= sq.nqb) return;  // past the end of a shorter packed sequence
+  for (int jj = threadIdx.x; jj <= g.K; jj += 512) s_sel[jj] = sel[unit * (g.K + 1) + jj];
+  __syncthreads();
+  pp_unit<D>(q, k, v, o, lse, g, hk, i, sub, sq, s_sel, s_ord, s_cnt);
+}
+
+// ---------------------------------------------------------------------------
+// Fused selection and attention (bf16 prefill, four query heads per KV head):
+// one workgroup of eight waves per unit finds the unit's route on the matrix
+// cores (eight waves of two 16-row M tiles) and then attends over it with the
+// ping-pong schedule, in one launch.  The selection's LDS lives in the
+// attention's tile slots, free until the first tile load: its layout in V
+// slot 0, its two candidate stages in K slots 0 and 1.  The route reaches the
+// attention through LDS; it is also written to sel.  Units go in the
+// attention's heavy-first order, which deals one (batch, KV head) slab to
+// each XCD when there are eight of them, so an XCD's L2 holds one pyramid.
+// ---------------------------------------------------------------------------
+constexpr int kFusedWaves = 8;
+
+template <int D>
+__global__ __launch_bounds__(512, 2) void select_attend(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ pyr, int32_t* __restrict__ sel, int32_t* __restrict__ trace_ids,
+    float* __restrict__ trace_scores, bf16_t* __restrict__ o, float* __restrict__ lse, PyrGeom g) {
+  static_assert(kSelStages * kChunk * 4 * D <= 2 * kPpTile, "a candidate stage fits a K slot");
+  __shared__ int s_sel[kMaxSel];
+  __shared__ int s_ord[kMaxSel];
+  __shared__ int s_cnt[2];
+  int bi, hk, i;
+  int64_t unit;
+  unit_of(g, blockIdx.x, bi, hk, i, unit);
+  select_mfma_unit<D, 2, kFusedWaves>(q, pyr, sel, trace_ids, trace_scores, g, unit, pp_v0, pp_k0,
+                                      pp_k1);
+  const PyrSeq sq = pyr_seq(g, bi);
+  if (i >= sq.nqb) return;  // past the end of a shorter packed sequence (route blanked)
+  // the route row, as the selection wrote it: kept blocks, the diagonal, -1
+  const SelLayout lay(g.K, g.branching, D, true, kFusedWaves);
+  const int* kept = reinterpret_cast<const int*>(pp_v0 + lay.off_kept);
+  const int nk = reinterpret_cast<const int*>(pp_v0 + lay.off_misc)[PYR_MAX_LEVELS];
+  for (int j = threadIdx.x; j <= g.K; j += 512) s_sel[j] = j < nk ? kept[j] : (j == nk ? i : -1);
+  __syncthreads();
+  pp_unit<D>(q, k, v, o, lse, g, hk, i, 0, sq, s_sel, s_ord, s_cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -1301,6 +1350,35 @@ hipError_t launch_attn_d(const PyrGeom& g, int dtype, const void* q, const void*
 }
 
 }  // namespace
+
+bool pyr_select_attend_fused(const PyrGeom& g, int dtype) {
+  return dtype == 1 && !g.decode && g.G == 4 && g.K + 1 <= kMaxSel &&
+         SelLayout(g.K, g.branching, g.D, true, kFusedWaves).total <= kPpTile;
+}
+
+hipError_t pyr_launch_select_attend(const PyrGeom& g, int dtype, const void* q, const void* k,
+                                    const void* v, const float* pyr, int32_t* sel,
+                                    int32_t* trace_ids, float* trace_scores, void* o, float* lse,
+                                    void* ws, hipStream_t st) {
+  if (!pyr_select_attend_fused(g, dtype)) {
+    const hipError_t e = pyr_launch_select(g, dtype, q, pyr, sel, trace_ids, trace_scores, st);
+    if (e != hipSuccess) return e;
+    return pyr_launch_attn(g, dtype, q, k, v, sel, o, lse, ws, st);
+  }
+  const int64_t units = (int64_t)g.B * g.Hk * g.nqb;
+  if (units == 0 || g.Tq == 0) return hipSuccess;
+  const bf16_t* qq = static_cast<const bf16_t*>(q);
+  const bf16_t* kk = static_cast<const bf16_t*>(k);
+  const bf16_t* vv = static_cast<const bf16_t*>(v);
+  bf16_t* oo = static_cast<bf16_t*>(o);
+  if (g.D == 64)
+    hipLaunchKernelGGL((select_attend<64>), dim3((unsigned)units), dim3(512), 0, st, qq, kk, vv,
+                       pyr, sel, trace_ids, trace_scores, oo, lse, g);
+  else
+    hipLaunchKernelGGL((select_attend<128>), dim3((unsigned)units), dim3(512), 0, st, qq, kk, vv,
+                       pyr, sel, trace_ids, trace_scores, oo, lse, g);
+  return hipGetLastError();
+}
 
 size_t pyr_attn_ws_bytes(const PyrGeom& g) {
   if (!g.decode) return 0;

@@ -253,6 +253,37 @@ pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void
                     "pyr_block_sparse_attn launch");
 }
 
+pyr_status pyr_select_attn(const pyr_problem* p, const void* q, const void* k, const void* v,
+                           const float* pyramid, int32_t* sel, int32_t* trace_ids,
+                           float* trace_scores, void* o, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  PyrGeom g;
+  pyr_status s = resolve(p, &g);
+  if (s != PYR_OK) return s;
+  const bool empty = (int64_t)g.B * g.Hk * g.nqb == 0 || g.Tq == 0 || (g.cu && g.Tqs == 0);
+  if (!empty && (!q || !k || !v || !pyramid || !sel || !o))
+    return fail(PYR_ERR_NULL, "q, k, v, pyramid, sel or o is NULL");
+  if (!empty && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pyramid) ||
+                 !aligned16(sel) || !aligned16(o) || (lse && !aligned16(lse)) ||
+                 (trace_ids && !aligned16(trace_ids)) ||
+                 (trace_scores && !aligned16(trace_scores))))
+    return fail(PYR_ERR_MISALIGNED, "tensors must be 16-byte aligned");
+  const size_t need = pyr_attn_ws_bytes(g);
+  if (!empty && need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PYR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!empty && need > 0 && !aligned16(workspace))
+    return fail(PYR_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  if (empty) return PYR_OK;
+  if (!pyr_select_attend_fused(g, p->dtype) && pyr_select_lds_bytes(g, p->dtype) > 160 * 1024)
+    return fail(PYR_ERR_UNSUPPORTED, "selection needs %zu bytes of LDS (> 160 KiB)",
+                pyr_select_lds_bytes(g, p->dtype));
+  return hip_status(pyr_launch_select_attend(g, p->dtype, q, k, v, pyramid, sel, trace_ids,
+                                             trace_scores, o, lse, workspace, stream),
+                    "pyr_select_attn launch");
+}
+
 pyr_status pyr_append_pyramid(const pyr_problem* p, const void* k, int64_t old_len,
                               float* pyramid, hipStream_t stream) {
   g_err[0] = 0;

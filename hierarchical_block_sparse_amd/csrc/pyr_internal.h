@@ -92,6 +92,14 @@ size_t pyr_attn_ws_bytes(const PyrGeom& g);
 hipError_t pyr_launch_attn(const PyrGeom& g, int dtype, const void* q, const void* k,
                            const void* v, const int32_t* sel, void* o, float* lse, void* ws,
                            hipStream_t st);
+// Selection then attention: one fused launch where pyr_select_attend_fused
+// holds (bf16 prefill, four query heads per KV head, the selection's layout
+// fits one tile slot), else the two launchers above in turn.
+bool pyr_select_attend_fused(const PyrGeom& g, int dtype);
+hipError_t pyr_launch_select_attend(const PyrGeom& g, int dtype, const void* q, const void* k,
+                                    const void* v, const float* pyr, int32_t* sel,
+                                    int32_t* trace_ids, float* trace_scores, void* o, float* lse,
+                                    void* ws, hipStream_t st);
 // Backward of the attention (bfloat16 prefill): workspace bytes and launcher.
 size_t pyr_attn_bwd_ws_bytes(const PyrGeom& g);
 // Upper bound on the work items of the key-gradient kernel (its grid size).

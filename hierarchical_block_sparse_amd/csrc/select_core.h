@@ -1,0 +1,528 @@
+// Selection device code shared by the selection kernels and the fused
+// select-and-attend kernel: the LDS layout, unit order, ranking, candidate
+// sets and the MFMA scoring of one unit.  Everything is in an unnamed
+// namespace, so each translation unit that includes it has its own copy.
+#pragma once
+
+#include <math.h>
+
+#include "pyr_device.h"
+#include "pyr_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = 32;   // candidates per LDS chunk (MFMA path): two 16-wide N tiles
+constexpr int kZbuf = 8192;  // fp32 scratch for the generic path
+constexpr int kSelStages = 2;  // candidate chunks in LDS (MFMA path): one scored while one loads
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Dynamic LDS layout shared by host (sizing) and device.
+struct SelLayout {
+  int cmax;  // candidate capacity: b*K + b - 1, rounded up to the chunk size
+  int off_kept, off_kscore, off_cand, off_score, off_rank, off_part, off_misc, off_hl, off_zbuf;
+  int total;  // bytes
+  __host__ __device__ SelLayout(int K, int b, int D, bool mfma, int waves = kWaves) {
+    cmax = (b * K + b - 1 + kChunk - 1) / kChunk * kChunk;
+    const int kp = (K + 3) & ~3;
+    int o = 0;
+    off_kept = o;   o += 4 * kp;
+    off_kscore = o; o += 4 * kp;
+    off_cand = o;   o += 4 * cmax;
+    off_score = o;  o += 4 * cmax;  // 16-byte aligned: read as float4
+    off_rank = o;   o += 4 * cmax;
+    if (mfma) {
+      off_part = o;  o += 8 * waves * cmax;                 // float2 [wave][candidate]
+      off_misc = o;  o += 4 * (PYR_MAX_LEVELS + 4);         // int ancestors, kept count
+      off_hl = off_zbuf = o;
+    } else {
+      off_part = off_hl = off_misc = o;
+      off_zbuf = o;  o += 4 * kZbuf;
+    }
+    total = o;
+  }
+};
+
+// Unit of this workgroup.  The dispatcher deals workgroups to the eight XCDs
+// in turn (workgroup w runs on XCD w % 8), so XCD x takes the contiguous run
+// of units [x * U8, (x + 1) * U8): its L2 then holds the pooled keys of only
+// the (batch, KV head) slabs of its run.  Within a run the units go from the
+// last (heaviest) query block down.  Returns false for the idle workgroups
+// past the end of a short run.
+__device__ __forceinline__ bool sel_unit(const PyrGeom& g, int64_t& unit) {
+  const int64_t U = (int64_t)g.B * g.Hk * g.nqb;
+  const int64_t U8 = (U + 7) / 8;
+  const int64_t x = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int64_t end = min<int64_t>((x + 1) * U8, U);
+  unit = end - 1 - k;
+  return unit >= x * U8;
+}
+
+// Ancestor of the diagonal block at every level: anc[l] = diag / b^l.
+__device__ void ancestors(const PyrGeom& g, int diag, int* s_anc) {
+  if (threadIdx.x == 0) {
+    int a = diag;
+    for (int l = 0; l < g.L; ++l) {
+      s_anc[l] = a;
+      a /= g.branching;
+    }
+  }
+}
+
+// Order-preserving map of a score to an unsigned key: a larger score gives a
+// larger key, -inf gives 0x007fffff, and 0 is left free to mark "no candidate"
+// (scores are never NaN).
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// One 64-candidate chunk of the in-order compaction of the kept set.
+__device__ __forceinline__ void keep_chunk(int j, uint32_t kj, int C, uint32_t T, int need,
+                                           unsigned long long lt, const int* cand,
+                                           const float* score, int* kept, float* kscore,
+                                           int& pos, int& ties, uint32_t& rej) {
+  const bool eq = kj == T && j < C;
+  const unsigned long long em = __ballot(eq);
+  const bool keep = kj > T || (eq && ties + __popcll(em & lt) < need);
+  const unsigned long long km = __ballot(keep);
+  if (keep) {
+    const int p = pos + __popcll(km & lt);
+    kept[p] = cand[j];
+    kscore[p] = score[j];
+  } else if (j < C && kj > rej) {
+    rej = kj;
+  }
+  pos += __popcll(km);
+  ties += __popcll(em);
+}
+
+// Keep the top K of C >= K candidates in ascending index order and write the
+// trace.  Candidates are ascending by node index, so "lower index wins a tie"
+// is "lower position wins": the kept set is every candidate with a score above
+// the K-th largest, T, plus the first (by position) of those equal to T until
+// there are K.  Wave 0 finds T two bits at a time (the largest key with at
+// least K keys >= it) with ballots over the candidates, four per lane in
+// registers (more are re-read from LDS), then compacts the kept set in index
+// order.  *margin gets the K-th best score minus the best rejected one (NaN
+// when nothing is rejected).  The trace row is g.K wide: slots past K hold -1
+// (ids) and NaN (scores), slot g.K of the scores the best rejected score.
+template <int NT>
+__device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* cand,
+                                const float* score, int* rank, int* kept, float* kscore,
+                                int* nkept, int K, float* margin, int32_t* tr_ids,
+                                float* tr_scores) {
+  const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
+  const int nch = (C + 63) / 64;
+  if (w == 0) {
+    uint32_t kr[4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int j = ch * 64 + l;
+      kr[ch] = j < C ? score_key(score[j]) : 0u;
+    }
+    uint32_t* keys = reinterpret_cast<uint32_t*>(rank);
+    for (int ch = 4; ch < nch; ++ch) {
+      const int j = ch * 64 + l;
+      keys[j] = j < C ? score_key(score[j]) : 0u;
+    }
+    // two bits per step: the largest of T | (d << bit), d = 3, 2, 1, that
+    // still has at least K keys at or above it
+    uint32_t T = 0;
+    for (int bit = 30; bit >= 0; bit -= 2) {
+      const uint32_t t1 = T | (1u << bit), t2 = T | (2u << bit), t3 = T | (3u << bit);
+      int c1 = 0, c2 = 0, c3 = 0;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        c1 += __popcll(__ballot(kr[ch] >= t1));
+        c2 += __popcll(__ballot(kr[ch] >= t2));
+        c3 += __popcll(__ballot(kr[ch] >= t3));
+      }
+      for (int ch = 4; ch < nch; ++ch) {
+        const uint32_t kj = keys[ch * 64 + l];
+        c1 += __popcll(__ballot(kj >= t1));
+        c2 += __popcll(__ballot(kj >= t2));
+        c3 += __popcll(__ballot(kj >= t3));
+      }
+      T = c3 >= K ? t3 : (c2 >= K ? t2 : (c1 >= K ? t1 : T));
+    }
+    int above = 0;  // candidates strictly above T (fewer than K)
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) above += __popcll(__ballot(kr[ch] > T));
+    for (int ch = 4; ch < nch; ++ch) above += __popcll(__ballot(keys[ch * 64 + l] > T));
+    const int need = K - above;  // ties at T to keep, lowest positions first
+    const unsigned long long lt = (1ull << l) - 1ull;
+    int pos = 0, ties = 0;
+    uint32_t rej = 0;  // best rejected key of this lane
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+      if (ch < nch)
+        keep_chunk(ch * 64 + l, kr[ch], C, T, need, lt, cand, score, kept, kscore, pos, ties, rej);
+    for (int ch = 4; ch < nch; ++ch)
+      keep_chunk(ch * 64 + l, keys[ch * 64 + l], C, T, need, lt, cand, score, kept, kscore, pos,
+                 ties, rej);
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint32_t r2 = (uint32_t)__shfl_xor((int)rej, o, 64);
+      rej = r2 > rej ? r2 : rej;
+    }
+    if (l == 0) {
+      if (tr_scores) tr_scores[level * (g.K + 1) + g.K] = key_score(rej);  // best rejected
+      *margin = key_score(T) - key_score(rej);
+      *nkept = K;
+    }
+  }
+  __syncthreads();
+  if (tr_ids) {
+    for (int j = tid; j < g.K; j += NT) tr_ids[level * g.K + j] = j < K ? kept[j] : -1;
+  }
+  if (tr_scores) {
+    for (int j = tid; j < g.K; j += NT)
+      tr_scores[level * (g.K + 1) + j] = j < K ? kscore[j] : NAN;
+  }
+}
+
+// Nodes kept per level for the units of KV head hk: the head's budget when
+// budgets are given (clamped to [1, K]), else K.
+__device__ __forceinline__ int unit_budget(const PyrGeom& g, int hk) {
+  if (!g.k_head) return g.K;
+  const int k = g.k_head[hk];
+  return k < 1 ? 1 : (k > g.K ? g.K : k);
+}
+
+// Confidence fallback, decided after the finest level's top-Ku: when the
+// margin between the Ku-th best score and the best rejected one is below
+// g.fb_margin, the level is ranked again keeping the best g.fb_k candidates
+// (all of them if there are fewer).  Must be called by every thread; the
+// result is uniform.
+__device__ __forceinline__ bool fallback_due(const PyrGeom& g, int level, int kk, int Ku,
+                                             const float* margin) {
+  if (level != 0 || kk != Ku || g.fb_k <= Ku) return false;
+  __syncthreads();  // the trace of the first pass has read kept[]; *margin is visible
+  return *margin < g.fb_margin;
+}
+
+// Candidates of one level into cand[]; returns the count.  Must be called by
+// every thread (ends with a barrier).
+template <int NT>
+__device__ int build_candidates(const PyrGeom& g, int level, const int* s_anc, const int* kept,
+                                int nkept, int* cand) {
+  const int b = g.branching;
+  const int anc = s_anc[level];
+  int C, base, nchild;
+  if (level == g.L - 1) {
+    C = anc;
+    nchild = 0;
+    base = 0;
+  } else {
+    nchild = nkept * b;
+    base = s_anc[level + 1] * b;
+    C = nchild + (anc - base);
+  }
+  for (int j = threadIdx.x; j < C; j += NT)
+    cand[j] = j < nchild ? kept[j / b] * b + j % b : base + (j - nchild);
+  __syncthreads();
+  return C;
+}
+
+// Levels with <= K candidates keep them all (no scoring).
+template <int NT>
+__device__ void keep_all(const PyrGeom& g, int C, int level, const int* cand, int* kept,
+                         int* nkept, int32_t* tr_ids, float* tr_scores) {
+  const int K = g.K;
+  for (int j = threadIdx.x; j < K; j += NT) {
+    const int id = j < C ? cand[j] : -1;
+    kept[j] = id;
+    if (tr_ids) tr_ids[level * K + j] = id;
+  }
+  if (tr_scores)
+    for (int j = threadIdx.x; j <= K; j += NT) tr_scores[level * (K + 1) + j] = NAN;
+  if (threadIdx.x == 0) *nkept = C;
+  __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ void write_route(const PyrGeom& g, int64_t unit, const int* kept,
+                                            int nk, int diag, int32_t* sel) {
+  int32_t* out = sel + unit * (g.K + 1);
+  for (int j = threadIdx.x; j <= g.K; j += NT) out[j] = j < nk ? kept[j] : (j == nk ? diag : -1);
+}
+
+// A unit past the end of a shorter packed sequence: its route row (and trace)
+// hold nothing.
+template <int NT>
+__device__ void blank_unit(const PyrGeom& g, int64_t unit, int32_t* sel, int32_t* trace_ids,
+                           float* trace_scores) {
+  for (int j = threadIdx.x; j <= g.K; j += NT) sel[unit * (g.K + 1) + j] = -1;
+  if (trace_ids)
+    for (int j = threadIdx.x; j < g.L * g.K; j += NT) trace_ids[unit * g.L * g.K + j] = -1;
+  if (trace_scores)
+    for (int j = threadIdx.x; j < g.L * (g.K + 1); j += NT)
+      trace_scores[unit * g.L * (g.K + 1) + j] = NAN;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 prefill path: MFMA scoring.  MT = 16-row M tiles per wave.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
+
+// Split rows of chunk c's candidates (plane 1 of the pyramid: per node a bf16
+// hi row and a bf16 lo row, 4D bytes) into one LDS stage with direct 16-byte
+// loads, no register staging.  Load t of a thread fills stage chunk
+// p = t * NT + tid (the 64 lanes of a wave fill 1 KiB in lane order):
+// candidate p / CPC, row part (p % CPC) / CPR (hi, lo), stored chunk q =
+// p % CPR, which holds logical chunk q ^ (candidate % CPR) of that row, so the
+// 16 candidates of an MFMA B fragment lie in different banks.  Positions past
+// C load candidate 0 (finite values that are never scored).
+template <int D, int NT>
+__device__ __forceinline__ void issue_chunk(const unsigned char* split, const int* cand, int C,
+                                            int c, unsigned char* stage, int w, int l) {
+  constexpr int CPR = D / 8;       // 16-byte chunks per bf16 row
+  constexpr int CPC = 2 * CPR;     // per candidate (hi, lo)
+  constexpr int PER = kChunk * CPC / NT;
+  static_assert(kChunk * CPC % NT == 0, "chunk must split evenly");
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int p = t * NT + w * 64 + l;
+    const int cc = p / CPC, part = (p % CPC) / CPR, q = p % CPR;
+    const int j = c * kChunk + cc;
+    const int node = cand[j < C ? j : 0];
+    const unsigned char* src =
+        split + (int64_t)node * 4 * D + part * 2 * D + ((q ^ (cc % CPR)) << 4);
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (lds_void*)(stage + (t * NT + w * 64) * 16), 16, 0, 0);
+  }
+}
+
+// Combine a value with that of the lane's partner in the other 16-lane row
+// (xor 16) or the other 32-lane half (xor 32).  A swap hands each lane the
+// pair (even, odd) of the two lanes, so a symmetric combine needs no select.
+__device__ __forceinline__ float max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LogSumExp (log2 domain: max m and sum s of 2^(x - m)) of one wave's rows for
+// the 16 candidates of an N tile; lane l ends with the value of candidate
+// l % 16.  Row j of M tile mt in the C layout is row 4*(l/16) + j, so a
+// candidate's rows are spread over the four 16-lane rows: the maximum is
+// taken across them first, which makes the partial sums share one reference
+// and combine by plain addition.  FULL skips the per-row validity bits.
+template <int MT, bool FULL>
+__device__ __forceinline__ void tile_lse(const f32x4 (&acc)[MT], uint32_t rowvalid, float sl2,
+                                         float& m, float& s) {
+  float mr = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (FULL || (rowvalid >> (mt * 4 + j) & 1u)) mr = fmaxf(mr, acc[mt][j]);
+  mr = max32(max16(mr));
+  m = mr * sl2;
+  s = 0.f;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (FULL || (rowvalid >> (mt * 4 + j) & 1u))
+          s += __builtin_amdgcn_exp2f(fmaf(acc[mt][j], sl2, -m));
+  }
+  s = sum32(sum16(s));
+}
+
+// Selection of one unit on the matrix cores by NW waves of MT M tiles each.
+// smem: the dynamic layout SelLayout(K, b, D, true, NW); st0 and st1: the two
+// candidate stages (kChunk * 4 * D bytes each), LDS of their own so that
+// writes to the layout do not wait for the stage loads in flight.  Must be
+// called by every thread of the workgroup.  Leaves the finest kept set in
+// the layout's kept[] and its size in the kept count, and writes the route
+// row (and trace) of the unit.
+template <int D, int MT, int NW>
+__device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
+                                                 const float* __restrict__ pyr,
+                                                 int32_t* __restrict__ sel,
+                                                 int32_t* __restrict__ trace_ids,
+                                                 float* __restrict__ trace_scores,
+                                                 const PyrGeom& g, int64_t unit,
+                                                 unsigned char* smem, unsigned char* st0,
+                                                 unsigned char* st1) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per bf16 row
+  const SelLayout lay(g.K, g.branching, D, true, NW);
+  int* kept = reinterpret_cast<int*>(smem + lay.off_kept);
+  float* kscore = reinterpret_cast<float*>(smem + lay.off_kscore);
+  int* cand = reinterpret_cast<int*>(smem + lay.off_cand);
+  float* score = reinterpret_cast<float*>(smem + lay.off_score);
+  int* rank = reinterpret_cast<int*>(smem + lay.off_rank);
+  lds_f32x2* part = (lds_f32x2*)(smem + lay.off_part);
+  int* s_anc = reinterpret_cast<int*>(smem + lay.off_misc);
+  int& s_nkept = s_anc[PYR_MAX_LEVELS];
+  float* s_margin = reinterpret_cast<float*>(s_anc + PYR_MAX_LEVELS + 1);
+
+  const int tid = threadIdx.x, l = tid % 64;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int i = (int)(unit % g.nqb);
+  const int64_t bhk = unit / g.nqb;  // b * Hk + hk
+  const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
+  const PyrSeq sq = pyr_seq(g, bi);
+  if (i >= sq.nqb) {
+    blank_unit<NW * 64>(g, unit, sel, trace_ids, trace_scores);
+    return;
+  }
+  // decode: one query block whose token sits at kv_len - 1; its G rows (one
+  // per query head) fill the first M tile of wave 0, every other row is idle
+  const int diag = g.decode ? (int)((g.Tk - 1) / PYR_BLOCK) : i;
+  const int Ku = unit_budget(g, hk);
+  const int RW = MT * 16;  // rows per wave
+  const float sl2 = g.scale * PYR_LOG2E;
+  const int cmax = lay.cmax;
+
+  if (tid == 0) s_nkept = 0;
+  ancestors(g, diag, s_anc);
+
+  // Q fragments (A operand): lane holds row (l % 16) of each M tile and the
+  // 8 consecutive d at 32*ks + 8*(l/16).
+  uint4 qa[MT][D / 32];
+  uint32_t rowvalid = 0;  // bit (mt*4 + j): C-layout row 4*(l/16)+j of tile mt is a real row
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int ra = w * RW + mt * 16 + (l % 16);
+    int h;
+    int64_t tok;
+    if (g.decode) {
+      h = ra < g.G ? ra : g.G - 1;
+      tok = 0;
+    } else {
+      h = ra / PYR_BLOCK;
+      tok = min<int64_t>((int64_t)i * PYR_BLOCK + ra % PYR_BLOCK, sq.Tq - 1);
+    }
+    const bf16_t* qrow = q + (sq.q0 + ((int64_t)hk * g.G + h) * sq.qhs + tok) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qa[mt][ks] = ld16(qrow + ks * 32 + 8 * (l / 16));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rc = w * RW + mt * 16 + 4 * (l / 16) + j;
+      const bool real = g.decode ? rc < g.G : (int64_t)i * PYR_BLOCK + rc % PYR_BLOCK < sq.Tq;
+      if (real) rowvalid |= 1u << (mt * 4 + j);
+    }
+  }
+
+  // every row of the unit is real
+  const bool full = !g.decode && (int64_t)(i + 1) * PYR_BLOCK <= sq.Tq;
+  // plane 1 of the slab: the split rows
+  const unsigned char* split =
+      reinterpret_cast<const unsigned char*>(pyr + (bhk * g.planes + 1) * g.n_tot * D);
+  int32_t* tr_ids = trace_ids ? trace_ids + unit * g.L * g.K : nullptr;
+  float* tr_sc = trace_scores ? trace_scores + unit * g.L * (g.K + 1) : nullptr;
+  __syncthreads();
+
+  for (int level = g.L - 1; level >= 0; --level) {
+    const int C = build_candidates<NW * 64>(g, level, s_anc, kept, s_nkept, cand);
+    if (C <= Ku) {
+      keep_all<NW * 64>(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
+      continue;
+    }
+    const unsigned char* lvl = split + g.loff[level] * 4 * D;
+    const int nchunks = (C + kChunk - 1) / kChunk;
+    // chunk c+1 loads while chunk c is scored; stage of chunk c is c % 2
+    issue_chunk<D, NW * 64>(lvl, cand, C, 0, st0, w, l);
+    for (int c = 0; c < nchunks; ++c) {
+      // this wave's loads of chunk c have landed; after the barrier every
+      // wave's have, and the stage of chunk c-1 is free
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      lds_barrier();
+      if (c + 1 < nchunks)
+        issue_chunk<D, NW * 64>(lvl, cand, C, c + 1, (c + 1) & 1 ? st1 : st0, w, l);
+      const unsigned char* st = c & 1 ? st1 : st0;
+#pragma unroll
+      for (int nt = 0; nt < kChunk / 16; ++nt) {
+        if (c * kChunk + nt * 16 >= C) break;  // uniform
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // B fragment: candidate r = nt*16 + l%16, logical chunk 4*ks + l/16
+        // of its hi and lo rows, stored at that chunk ^ (r % CPR)
+        const int r = nt * 16 + (l % 16);
+        const unsigned char* row = st + r * 4 * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const int off = ((4 * ks + l / 16) ^ (r % CPR)) << 4;
+          const bf16x8 bhv = as_bf16x8(*reinterpret_cast<const uint4*>(row + off));
+          const bf16x8 blv = as_bf16x8(*reinterpret_cast<const uint4*>(row + 2 * D + off));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), bhv, acc[mt], 0, 0, 0);
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), blv, acc[mt], 0, 0, 0);
+          }
+        }
+        // this wave's LogSumExp over its rows, per candidate (lane column l % 16)
+        float m, s;
+        if (full)
+          tile_lse<MT, true>(acc, rowvalid, sl2, m, s);
+        else
+          tile_lse<MT, false>(acc, rowvalid, sl2, m, s);
+        const int cn = c * kChunk + nt * 16 + l;
+        if (l < 16 && cn < C) part[w * cmax + cn] = f32x2{m, s};
+      }
+    }
+    __syncthreads();
+    for (int j = tid; j < C; j += NW * 64) {
+      float m = -INFINITY, s = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const f32x2 p = part[ww * cmax + j];
+        lse2_merge(m, s, p.x, p.y);
+      }
+      const float sc = (m + log2f(s)) * PYR_LN2;
+      score[j] = sc == sc ? sc : -INFINITY;  // a NaN score ranks last
+    }
+    __syncthreads();
+    for (int kk = Ku;;) {
+      top_k_and_trace<NW * 64>(g, C, level, cand, score, rank, kept, kscore, &s_nkept, kk, s_margin,
+                      tr_ids, tr_sc);
+      if (!fallback_due(g, level, kk, Ku, s_margin)) break;
+      kk = C < g.fb_k ? C : g.fb_k;  // keep more of the same candidates
+    }
+  }
+  write_route<NW * 64>(g, unit, kept, s_nkept, diag, sel);
+}
+
+// NW waves of MT M tiles each.  Four M tiles fit 168 VGPRs, so three
+// four-wave workgroups share a CU (G = 4); G = 8 runs eight such waves.
+template <int D, int MT, int NW>
+__global__ __launch_bounds__(NW * 64, MT == 4 ? (NW == 4 ? 3 : 2) : 1) void select_mfma(
+    const bf16_t* __restrict__ q, const float* __restrict__ pyr, int32_t* __restrict__ sel,
+    int32_t* __restrict__ trace_ids, float* __restrict__ trace_scores, PyrGeom g) {
+  constexpr int STAGE = kChunk * 4 * D;  // bytes per LDS stage
+  static_assert(kSelStages == 2, "two candidate stages");
+  // The layout is the one dynamic array: with a second __shared__ variable
+  // the compiler would give each its own alias scope and wait for every chunk
+  // load in flight before any LDS read, undoing the prefetch.
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ __attribute__((aligned(16))) unsigned char stages[kSelStages * STAGE];
+  int64_t unit;
+  if (!sel_unit(g, unit)) return;
+  select_mfma_unit<D, MT, NW>(q, pyr, sel, trace_ids, trace_scores, g, unit, smem, stages,
+                              stages + STAGE);
+}
+
+}  // namespace

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PYR_ABI_VERSION 3
+#define PYR_ABI_VERSION 4
 
 typedef enum pyr_status {
   PYR_OK = 0,
@@ -233,6 +233,28 @@ pyr_status pyr_budgets_from_entropy(const float* entropy, int32_t n_heads, int32
 pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void* k,
                                  const void* v, const int32_t* sel, void* o, float* lse,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Selection and attention in one call (PISA abstract: the kernels fuse the
+ * hierarchical routing with the LogSumExp scoring; PHBA §A.1.3: the forward
+ * kernel works straight from the query-centric routes).  Arguments as in
+ * pyr_select_topk and pyr_block_sparse_attn: q, k, v, pyramid (inputs), sel,
+ * trace_ids, trace_scores (NULL allowed for the traces), o, lse (NULL
+ * allowed) and the attention's workspace (outputs / scratch).
+ * For bfloat16 prefill problems with four query heads per KV head and
+ * branching * (top_k + 1) <= 192 (the selection's on-chip state then fits in
+ * one of the attention's tile slots), one launch runs both steps per unit: the
+ * route reaches the attention in LDS (and is written to sel), and the unit's
+ * q is fetched from HBM once.  The route is the coarse-to-fine top-K of
+ * pyr_select_topk; its scores are summed over the unit's rows in another
+ * order, so a unit may differ from pyr_select_topk's route where two scores
+ * tie within fp32 rounding.  o and lse are, bit for bit, what
+ * pyr_block_sparse_attn computes over the sel written.  Other problems run
+ * pyr_select_topk's and pyr_block_sparse_attn's kernels in turn.  Errors as
+ * for those two calls. */
+pyr_status pyr_select_attn(const pyr_problem* p, const void* q, const void* k, const void* v,
+                           const float* pyramid, int32_t* sel, int32_t* trace_ids,
+                           float* trace_scores, void* o, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* ---- decode: pyramid maintenance ---- */
 

@@ -36,19 +36,24 @@ def problem(cfg: W.Config) -> H.Problem:
                      cfg.kv_len, cfg.branching, cfg.top_k, cfg.dtype)
 
 
-def run_device(cfg: W.Config, q, k, v, trace=True, sel_in=None):
+def run_device(cfg: W.Config, q, k, v, trace=True, sel_in=None, fused=False):
     """Build, select (with trace) and attend on the device.  With sel_in the
-    attention runs over those route rows instead of the device selection."""
+    attention runs over those route rows instead of the device selection;
+    with fused, selection and attention run in one pyr_select_attn call."""
     p = problem(cfg)
     pyr = H.alloc_pyramid(p)
     H.pyr_build_pyramid(p, k, pyr)
     sel = H.alloc_sel(p)
     tids, tsc = H.alloc_trace(p) if trace else (None, None)
-    H.pyr_select_topk(p, q, pyr, sel, tids, tsc)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    route = sel if sel_in is None else sel_in.to(torch.int32).to(q.device).contiguous()
-    H.pyr_block_sparse_attn(p, q, k, v, route, o, lse, H.alloc_workspace(p))
+    if fused:
+        assert sel_in is None
+        H.pyr_select_attn(p, q, k, v, pyr, sel, o, lse, H.alloc_workspace(p), tids, tsc)
+    else:
+        H.pyr_select_topk(p, q, pyr, sel, tids, tsc)
+        route = sel if sel_in is None else sel_in.to(torch.int32).to(q.device).contiguous()
+        H.pyr_block_sparse_attn(p, q, k, v, route, o, lse, H.alloc_workspace(p))
     torch.cuda.synchronize()
     return dict(pyr=pyr, sel=sel, tids=tids, tsc=tsc, o=o, lse=lse)
 

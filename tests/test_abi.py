@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     assert {"pyr_build_pyramid", "pyr_select_topk", "pyr_block_sparse_attn"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert H.pyr_abi_version() == 3
+    assert H.pyr_abi_version() == 4
 
 
 def test_single_hip_runtime_in_process():
@@ -362,3 +362,45 @@ def test_budgets_from_entropy_matches_the_oracle():
     assert lib.pyr_budgets_from_entropy(ent, 2, 8, 3, 2, out) == 2
     assert lib.pyr_budgets_from_entropy(None, 2, 8, 1, 4, out) == 1
     assert lib.pyr_budgets_from_entropy(None, 0, 8, 1, 4, None) == 0
+
+
+def _sa(p, ptrs, ws=None, nbytes=0):
+    """Call pyr_select_attn with the ten tensor pointers `ptrs` (q, k, v,
+    pyramid, sel, trace_ids, trace_scores, o, lse) and a workspace."""
+    return _status("pyr_select_attn", ctypes.byref(p.c()), *ptrs, ws, nbytes, None)
+
+
+def test_select_attn_validation_before_launch():
+    ptr = ctypes.c_void_p(16)
+    p = _p()
+    full = [ptr, ptr, ptr, ptr, ptr, None, None, ptr, None]
+    for i in (0, 1, 2, 3, 4, 7):           # q, k, v, pyramid, sel, o may not be NULL
+        ptrs = list(full)
+        ptrs[i] = None
+        s, msg = _sa(p, ptrs)
+        assert s == 1 and "NULL" in msg, i
+    for i in range(9):                     # every pointer given must be 16-byte aligned
+        ptrs = [ptr] * 9
+        ptrs[i] = ctypes.c_void_p(24)
+        assert _sa(p, ptrs)[0] == 4, i
+    s, _ = _sa(_p(top_k=0), full)          # invalid problem
+    assert s == 2
+    pd = _p(q_len=1, kv_len=8192)          # decode needs the attention's workspace
+    need = H.pyr_attn_workspace_bytes(pd)
+    s, msg = _sa(pd, full)
+    assert s == 5 and "workspace" in msg
+    assert _sa(pd, full, ptr, need - 1)[0] == 5
+    for kw in (dict(batch=0), dict(q_len=0, kv_len=0)):   # empty problems: nothing to do
+        assert _sa(_p(**kw), [None] * 9)[0] == 0
+
+
+def test_select_attn_binding_rejects_wrong_shapes_on_host():
+    p = _p(q_len=128, kv_len=128)
+    q = torch.zeros((1, 4, 128, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, 128, 128), dtype=torch.bfloat16)
+    pyr = torch.zeros(H.pyramid_shape(p))
+    sel = torch.zeros((1, 2, 2, 9), dtype=torch.int32)
+    with pytest.raises(ValueError):        # sel one slot short
+        H.pyr_select_attn(p, q, k, k, pyr, sel[..., :8].contiguous(), q)
+    with pytest.raises(ValueError):        # every shape right, but host tensors
+        H.pyr_select_attn(p, q, k, k, pyr, sel, q)

@@ -34,18 +34,29 @@ def _sample_units(cfg, rng, n_slabs, n_per_slab):
     return pick, units
 
 
-@pytest.mark.parametrize("name,n_slabs,n_per_slab", [
-    ("mha_32k", 2, 12),
-    ("gqa_128k", 2, 12),
-    ("prefill_1m", 1, 16),
-    ("decode_256k", 6, 0),
-])
-def test_fullsize_sampled(name, n_slabs, n_per_slab):
+@pytest.mark.parametrize("name,n_slabs,n_per_slab,fused", [
+    ("mha_32k", 2, 12, False),
+    ("gqa_128k", 2, 12, False),
+    ("gqa_128k", 2, 12, True),
+    ("prefill_1m", 1, 16, False),
+    ("decode_256k", 6, 0, False),
+], ids=["mha_32k", "gqa_128k", "gqa_128k_fused", "prefill_1m", "decode_256k"])
+def test_fullsize_sampled(name, n_slabs, n_per_slab, fused):
     cfg = W.CONFIGS[name]
-    GH.log(f"full-size {name}: B={cfg.batch} Hq={cfg.n_q_heads} Hk={cfg.n_kv_heads} "
-           f"Tq={cfg.q_len} Tk={cfg.kv_len} b={cfg.branching} K={cfg.top_k}")
+    GH.log(f"full-size {name}{' (pyr_select_attn)' if fused else ''}: B={cfg.batch} "
+           f"Hq={cfg.n_q_heads} Hk={cfg.n_kv_heads} Tq={cfg.q_len} Tk={cfg.kv_len} "
+           f"b={cfg.branching} K={cfg.top_k}")
     q, k, v = W.make_inputs(cfg, "cuda")
-    dev = GH.run_device(cfg, q, k, v)
+    dev = GH.run_device(cfg, q, k, v, fused=fused)
+    if fused:   # the attention half equals the separate kernel's over the same routes
+        p = GH.problem(cfg)
+        o2 = torch.empty_like(q)
+        lse2 = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        H.pyr_block_sparse_attn(p, q, k, v, dev["sel"], o2, lse2, H.alloc_workspace(p))
+        torch.cuda.synchronize()
+        assert torch.equal(dev["o"].view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(dev["lse"], lse2)
+        del o2, lse2
     rng = np.random.default_rng(77)
     slabs, units = _sample_units(cfg, rng, n_slabs, n_per_slab)
     scale = 1.0 / math.sqrt(cfg.head_dim)
