@@ -82,7 +82,7 @@ def calibrate_copy():
 
 
 # ---------------------------------------------------------------------------
-# algorithmic work (the per-unit figures are derived in the design doc)
+# algorithmic work (per-unit bytes and flops from the definitions of the steps)
 # ---------------------------------------------------------------------------
 
 def _num_blocks(n_tokens):
@@ -265,7 +265,7 @@ def kernel_traffic(workload, kind="attn"):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     if args.calibrate_copy:

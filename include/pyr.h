@@ -80,7 +80,7 @@ typedef enum pyr_status {
   PYR_OK = 0,
   PYR_ERR_NULL = 1,        /* a required pointer is NULL                        */
   PYR_ERR_INVALID = 2,     /* a size or parameter is out of range               */
-  PYR_ERR_UNSUPPORTED = 3, /* valid, but outside what this build implements     */
+  PYR_ERR_UNSUPPORTED = 3, /* valid, but outside what this library implements   */
   PYR_ERR_MISALIGNED = 4,  /* a tensor pointer is not 16-byte aligned           */
   PYR_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
   PYR_ERR_HIP = 6          /* a HIP launch failed (text in pyr_last_error)      */
