@@ -363,6 +363,20 @@ def main():
     stage_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
                 for i in range(n_stage)]
     ms_per_step = elapsed * 1e3 / args.steps
+
+    # the same steps from cold caches: 1 GiB written before each step evicts the
+    # L2s and the 256 MB Infinity Cache; timed by the events only
+    cold_ms = None
+    if not args.backward:
+        print(f"# timing {args.steps} cold-cache steps", file=sys.stderr, flush=True)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for s in range(args.steps):
+            flush.fill_(s & 0xFF)
+            step(ev[s])
+        torch.cuda.synchronize()
+        cold_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+                   for i in range(n_stage)]
+        del flush
     tokens = cfg.batch * (1 if cfg.decode else cfg.q_len)
     value = tokens / (ms_per_step / 1e3)
 
@@ -427,6 +441,14 @@ def main():
         },
         "cpu_baseline": None,
     }
+    tokens_sa = tokens / ((stage_ms[1] + stage_ms[2]) / 1e3)
+    line["stages"]["tokens_per_s_select_attn_only"] = round(tokens_sa, 1)
+    if cold_ms is not None:
+        line["stages"]["cold_cache"] = {
+            "note": "same steps after writing 1 GiB (L2 and Infinity Cache evicted); event time only",
+            "ms_per_step": round(sum(cold_ms), 4),
+            "stage_ms": [round(x, 4) for x in cold_ms],
+        }
     if args.fused:
         # one kernel does the selection's scoring and the attention: its
         # algorithmic flops are both (scores counted once per dot product)
