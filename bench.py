@@ -235,6 +235,21 @@ def attn_kernel_name(cfg):
     return "attn_prefill_pp" if cfg.group % 4 == 0 else "attn_prefill_mfma"
 
 
+def planted_recall(cfg, sel):
+    """Fraction of the planted (unit, key block) pairs whose block is in the
+    unit's route row: a quality indicator of the selection, not a gate."""
+    from hierarchical_block_sparse_amd import workloads as W
+    plants = W.planted_blocks(cfg)
+    if not plants:
+        return None
+    rows = sel.cpu().numpy()
+    hit = total = 0
+    for (bi, hk, i), blocks in plants.items():
+        hit += len(blocks & set(rows[bi, hk, i].tolist()))
+        total += len(blocks)
+    return hit / total
+
+
 def fused_kernel(cfg):
     """Whether pyr_select_attn runs as one launch for this workload (bfloat16
     prefill, four query heads per KV head, branching * (top_k + 1) <= 192)."""
@@ -441,6 +456,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not lengths:
+        line["planted_recall"] = planted_recall(cfg, sel)
     tokens_sa = tokens / ((stage_ms[1] + stage_ms[2]) / 1e3)
     line["stages"]["tokens_per_s_select_attn_only"] = round(tokens_sa, 1)
     if cold_ms is not None:

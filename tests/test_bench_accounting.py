@@ -54,3 +54,18 @@ def test_attention_flops_count_visible_pairs(nqb, K):
     tiles = sum(min(K, i) + 1 for i in range(nqb))
     assert byts == 2 * G * T * d * 2 + tiles * 2 * 64 * d * 2
     assert math.isclose(bench.attn_work(cfg.with_(batch=3))[0], 3 * flops)
+
+
+def test_planted_recall_bounds():
+    """Every block listed (K >= query blocks) gives recall 1, no block gives 0,
+    and listing exactly the planted blocks of each unit gives 1 as well."""
+    cfg = W.Config("acct", 2, 4, 2, 64 * 12, 64 * 12, 16, torch.float32, 2, 12, 3, seed=9)
+    nqb = 12
+    full = torch.tensor(np.broadcast_to(np.arange(13) - 1, (2, 2, nqb, 13)).copy(), dtype=torch.int32)
+    assert bench.planted_recall(cfg, full) == 1.0
+    assert bench.planted_recall(cfg, torch.full((2, 2, nqb, 13), -1, dtype=torch.int32)) == 0.0
+    exact = torch.full((2, 2, nqb, 13), -1, dtype=torch.int32)
+    for (bi, hk, i), blocks in W.planted_blocks(cfg).items():
+        exact[bi, hk, i, :len(blocks)] = torch.tensor(sorted(blocks), dtype=torch.int32)
+    assert bench.planted_recall(cfg, exact) == 1.0
+    assert bench.planted_recall(cfg.with_(n_planted=0), full) is None
