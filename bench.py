@@ -59,6 +59,8 @@ def parse():
                     help="selection and attention in one pyr_select_attn call per step")
     ap.add_argument("--backward", action="store_true",
                     help="time the training pass (forward + backward of the attention)")
+    ap.add_argument("--cold-steps", type=int, default=-1,
+                    help="cold-cache steps timed after the warm ones (-1: as many as --steps; 0: none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 device-to-device copies of 1 GiB (counter calibration)")
     return ap.parse_args()
@@ -382,14 +384,15 @@ def main():
     # the same steps from cold caches: 1 GiB written before each step evicts the
     # L2s and the 256 MB Infinity Cache; timed by the events only
     cold_ms = None
-    if not args.backward:
-        print(f"# timing {args.steps} cold-cache steps", file=sys.stderr, flush=True)
+    n_cold = min(args.steps if args.cold_steps < 0 else args.cold_steps, args.steps)
+    if not args.backward and n_cold > 0:
+        print(f"# timing {n_cold} cold-cache steps", file=sys.stderr, flush=True)
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        for s in range(args.steps):
+        for s in range(n_cold):
             flush.fill_(s & 0xFF)
             step(ev[s])
         torch.cuda.synchronize()
-        cold_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+        cold_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(n_cold)) / n_cold
                    for i in range(n_stage)]
         del flush
     tokens = cfg.batch * (1 if cfg.decode else cfg.q_len)
