@@ -413,6 +413,11 @@ def main():
     if args.fused:   # one launch: the stage of the selection holds both
         t_sel = t_attn = stage_ms[1] / 1e3
     achieved = a_flops / t_attn / 1e12
+    # the attention's bound: MFMA where a gathered byte feeds many flops (four
+    # or more query heads per KV head: 225 flop/B at 128K, 452 at 1M), the
+    # gather bandwidth where it feeds few (one head per KV head: 59 flop/B) and
+    # for decode (one query row per head)
+    hbm_bound = cfg.decode or a_flops / a_bytes < 100
     traffic = kernel_traffic(cfg.name + ("_packed" if lengths else ""))
     line = {
         "metric": METRIC,
@@ -436,11 +441,11 @@ def main():
         },
         "roofline": {
             "kernel": attn_kernel_name(cfg),
-            "bound": "mfma" if not cfg.decode else "hbm",
-            "achieved": round(achieved, 2) if not cfg.decode else round(a_bytes / t_attn / 1e9, 1),
-            "peak": PEAK_BF16_TFLOPS if not cfg.decode else PEAK_HBM_GBS,
-            "unit": "TFLOP/s" if not cfg.decode else "GB/s",
-            "frac": round((achieved / PEAK_BF16_TFLOPS) if not cfg.decode
+            "bound": "mfma" if not hbm_bound else "hbm",
+            "achieved": round(achieved, 2) if not hbm_bound else round(a_bytes / t_attn / 1e9, 1),
+            "peak": PEAK_BF16_TFLOPS if not hbm_bound else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if not hbm_bound else "GB/s",
+            "frac": round((achieved / PEAK_BF16_TFLOPS) if not hbm_bound
                           else (a_bytes / t_attn / 1e9 / PEAK_HBM_GBS), 4),
             "traffic": traffic,
             "algorithmic_flops_per_launch": a_flops,
@@ -453,6 +458,7 @@ def main():
             "select": {"ms": round(stage_ms[1], 4), "GB/s": round(s_bytes / t_sel / 1e9, 1),
                        "TFLOP/s_fp32_equiv": round(s_flops / t_sel / 1e12, 2)},
             "attn": {"ms": round(stage_ms[2], 4), "TFLOP/s": round(achieved, 2),
+                     "mfma_frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "GB/s_gathered": round(a_bytes / t_attn / 1e9, 1)},
             "build_plus_select_hbm_frac": (round((b_bytes + s_bytes) / (t_build + t_sel) / 1e9 / PEAK_HBM_GBS, 4)
                                            if not cfg.decode else None),

@@ -119,6 +119,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
   __shared__ __align__(16) unsigned char tiles[NSTAGE][2][TG::TILE];  // [stage][K, V]
   __shared__ int s_sel[kMaxSel];
   __shared__ int s_n;
+  // the raw route row, in the last stage's V tile (free until its first load)
+  static_assert(kMaxSel * 4 <= TG::TILE, "route row fits a tile");
+  int* s_raw = reinterpret_cast<int*>(tiles[NSTAGE - 1][1]);
 
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
   const int half = l / 32, lr = l % 32;
@@ -137,16 +140,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_prefill_mfma(
   const bf16_t* kh = k + (sq.k0 + hk * sq.khs) * D;
   const bf16_t* vh = v + (sq.k0 + hk * sq.khs) * D;
 
-  for (int jj = tid; jj <= g.K; jj += NT) s_sel[jj] = sel[unit * (g.K + 1) + jj];
+  for (int jj = tid; jj <= g.K; jj += NT) s_raw[jj] = sel[unit * (g.K + 1) + jj];
 
-  __syncthreads();  // s_sel visible
-  if (tid == 0) {   // compact the route row in place: entries outside [0, nb) are skipped
-    int n = 0;
-    for (int jj = 0; jj <= g.K; ++jj) {
-      const int j = s_sel[jj];
-      if (j >= 0 && j < sq.nb) s_sel[n++] = j;
-    }
-    s_n = n;
+  __syncthreads();  // s_raw visible
+  if (w == 0) {     // compact the route row: entries outside [0, nb) and repeats are skipped
+    const int n = route_compact_wave(s_raw, g.K + 1, sq.nb, s_sel, 0, [](int) { return true; });
+    if (l == 0) s_n = n;
   }
   __syncthreads();
   const int nsel = s_n;
@@ -656,21 +655,12 @@ __device__ __forceinline__ void pp_unit(const bf16_t* __restrict__ q, const bf16
 
   // route order: valid blocks before the unit's own block first (no mask
   // needed), then the rest (the diagonal block)
+  // (entries outside [0, nb) and repeats of an earlier entry are skipped)
   if (w == 0) {
-    int n = 0, nun = 0;
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll 1
-      for (int base = 0; base <= g.K; base += 64) {
-        const int jj = base + l;
-        const int j = jj <= g.K ? s_sel[jj] : -1;
-        const bool ok = j >= 0 && j < sq.nb && ((pass == 0) == (j < i));
-        const unsigned long long m = __ballot(ok);
-        if (ok) s_ord[n + __popcll(m & ((1ull << l) - 1ull))] = j;
-        n += __popcll(m);
-      }
-      if (pass == 0) nun = n;
-    }
+    const int nun = route_compact_wave(s_sel, g.K + 1, sq.nb, s_ord, 0,
+                                       [i](int j) { return j < i; });
+    const int n = route_compact_wave(s_sel, g.K + 1, sq.nb, s_ord, nun,
+                                     [i](int j) { return j >= i; });
     if (l == 0) {
       s_cnt[0] = n;
       s_cnt[1] = nun;
@@ -867,7 +857,8 @@ __global__ __launch_bounds__(64) void attn_prefill_valu(const T* __restrict__ q,
   __syncthreads();
   for (int jj = 0; jj <= g.K; ++jj) {
     const int j = s_sel[jj];
-    if (j < 0 || j >= sq.nb) continue;  // uniform across the workgroup
+    // outside [0, nb) or a repeat of an earlier entry: uniform across the workgroup
+    if (!route_entry_used(s_sel, jj, j, sq.nb)) continue;
     const int64_t key0 = (int64_t)j * PYR_BLOCK;
     __syncthreads();
     for (int s = t; s < 64 * (D / VEC); s += 64) {
@@ -996,13 +987,14 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_split(
       rv[sl] = ok ? ld16_nt(vh + kp * D + c) : make_uint4(0, 0, 0, 0);
     }
   };
+  // entries outside [0, nb) and repeats of an earlier entry of the row are skipped
   int jj = jb0;
-  while (jj < jb1 && !(srow[jj] >= 0 && srow[jj] < g.nb)) ++jj;
+  while (jj < jb1 && !route_entry_used(srow, jj, srow[jj], g.nb)) ++jj;
   if (jj < jb1) fetch(srow[jj]);
   while (jj < jb1) {
     const int j = srow[jj];
     int nx = jj + 1;
-    while (nx < jb1 && !(srow[nx] >= 0 && srow[nx] < g.nb)) ++nx;
+    while (nx < jb1 && !route_entry_used(srow, nx, srow[nx], g.nb)) ++nx;
     __syncthreads();  // previous tile consumed, q staged
 #pragma unroll
     for (int sl = 0; sl < SLOTS; ++sl) {
@@ -1120,17 +1112,21 @@ __global__ __launch_bounds__(256, 4) void attn_decode_mfma(
     for (int ks = 0; ks < KS; ++ks)
       qb[ks] = lr < G ? ld16(qrow + ks * 32 + 8 * lg) : make_uint4(0u, 0u, 0u, 0u);
   }
-  // this split's valid blocks
-  if (tid == 0) {
-    const int32_t* srow = sel + bhk * (g.K + 1);
-    const int jb0 = split * kDecBlocksPerSplit;
-    const int jb1 = min(g.K + 1, jb0 + kDecBlocksPerSplit);
-    int n = 0;
-    for (int jj = jb0; jj < jb1; ++jj) {
-      const int j = srow[jj];
-      if (j >= 0 && j < g.nb) s_blk[n++] = j;
-    }
-    s_nb = n;
+  // this split's blocks: its entries of the route row that are used (block
+  // ids in [0, nb) that no earlier entry of the whole row repeats)
+  const int jb0 = split * kDecBlocksPerSplit;
+  const int jb1 = min(g.K + 1, jb0 + kDecBlocksPerSplit);
+  // the row's entries up to this split's last, in V slot 1 (free until block 1 loads)
+  static_assert(kMaxSel * 4 <= TG::TILE, "route row fits a tile");
+  int* s_row = reinterpret_cast<int*>(vt1);
+  for (int jj = tid; jj < jb1; jj += 256) s_row[jj] = sel[bhk * (g.K + 1) + jj];
+  __syncthreads();
+  if (w == 0) {
+    const int jj = jb0 + l;
+    const bool ok = l < kDecBlocksPerSplit && jj < jb1 && route_entry_used(s_row, jj, s_row[jj], g.nb);
+    const unsigned long long m = __ballot(ok);
+    if (ok) s_blk[__popcll(m & ((1ull << l) - 1ull))] = s_row[jj];
+    if (l == 0) s_nb = __popcll(m);
   }
   __syncthreads();
   const int nblk = s_nb;
@@ -1391,3 +1387,4 @@ hipError_t pyr_launch_attn(const PyrGeom& g, int dtype, const void* q, const voi
   return g.D == 64 ? launch_attn_d<64>(g, dtype, q, k, v, sel, o, lse, ws, st)
                    : launch_attn_d<128>(g, dtype, q, k, v, sel, o, lse, ws, st);
 }
+

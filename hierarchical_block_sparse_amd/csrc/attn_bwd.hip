@@ -1,12 +1,13 @@
 // Backward of the block-sparse causal attention for a fixed route table, on
 // gfx950.
 //
-// PHBA (Prefix-State Hybrid Block Attention) §A.1.4: the sparse backward
-// enumerates, block-major, the query rows that access each key block and
-// recomputes the sparse scores and probabilities on chip from the forward's
-// log-sum-exp, with no stored probability tensor; §A.1: during training the
-// routing decisions are reformatted as block-major integer metadata.  The route
-// itself is a discrete choice and gets no gradient.  With P = exp(scale q k^T -
+// PHBA (Prefix-State Hybrid Block Attention) §A.1 and §A.1.4 describe the
+// sparse backward; here it takes this form.  The key gradients walk, for each
+// key block, the list of query blocks whose routes contain it, built from a
+// per-slab bitmap with one bit per (key block, query block) pair.  P is
+// rebuilt in registers from the stored log-sum-exp of every row, so no
+// probability tensor ever reaches memory.  The route itself is a discrete
+// choice and gets no gradient.  With P = exp(scale q k^T -
 // lse) over the visible keys of the selected blocks:
 //   dP = dO v^T,  D = rowsum(dO * O),  dS = P (dP - D),
 //   dQ = scale dS k,  dK = scale dS^T q,  dV = P^T dO   (dK, dV summed over
@@ -434,6 +435,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq(
   __shared__ __align__(16) unsigned char st1[2 * TG::TILE];
   __shared__ __align__(16) unsigned char st2[2 * TG::TILE];
   __shared__ int s_sel[kMaxSelB + 1];
+  // the raw route row, in stage 2 (free until its first tile load)
+  static_assert(kMaxSelB * 4 <= 2 * TG::TILE, "route row fits a stage");
+  int* s_raw = reinterpret_cast<int*>(st2);
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -456,14 +460,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq(
     s_.t8 = tl.t8;
   }
 
-  // compact route row (entries outside [0, nb) are skipped); count in s_sel[kMaxSelB]
-  if (tid == 0) {
-    int n = 0;
-    for (int jj = 0; jj <= g.K; ++jj) {
-      const int j = sel[ublk * (g.K + 1) + jj];
-      if (j >= 0 && j < g.nb) s_sel[n++] = j;
-    }
-    s_sel[kMaxSelB] = n;
+  // compact the route row (entries outside [0, nb) and repeats of an earlier
+  // entry are skipped, as the key gradients' bitmap counts a block once);
+  // count in s_sel[kMaxSelB]
+  for (int jj = tid; jj <= g.K; jj += NT) s_raw[jj] = sel[ublk * (g.K + 1) + jj];
+  __syncthreads();
+  if (w == 0) {
+    const int n = route_compact_wave(s_raw, g.K + 1, g.nb, s_sel, 0, [](int) { return true; });
+    if (l == 0) s_sel[kMaxSelB] = n;
   }
   __syncthreads();
   const int nsel = s_sel[kMaxSelB];

@@ -294,6 +294,17 @@ pyr_status pyr_append_pyramid(const pyr_problem* p, const void* k, int64_t old_l
   if (old_len <= 0 || old_len > g.Tk)
     return fail(PYR_ERR_INVALID, "old_len %lld outside (0, kv_len = %lld]", (long long)old_len,
                 (long long)g.Tk);
+  // Without a capacity the layout follows the length itself: the pyramid of
+  // old_len has the layout of the new length only when both lengths cover
+  // the same number of 64-token blocks (else every level above the finest
+  // moves, and so does the slab stride).
+  if (p->kv_capacity == 0 &&
+      (old_len + PYR_BLOCK - 1) / PYR_BLOCK != (g.Tk + PYR_BLOCK - 1) / PYR_BLOCK)
+    return fail(PYR_ERR_INVALID,
+                "old_len %lld and kv_len %lld cover different block counts: the pyramid's "
+                "layout would change; pass the same kv_capacity (>= kv_len) to the build and "
+                "every append",
+                (long long)old_len, (long long)g.Tk);
   if ((int64_t)g.B * g.Hk == 0 || old_len == g.Tk) return PYR_OK;
   if (!k || !pyramid) return fail(PYR_ERR_NULL, "k or pyramid is NULL");
   if (!aligned16(k) || !aligned16(pyramid))

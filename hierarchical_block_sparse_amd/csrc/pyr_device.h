@@ -108,3 +108,34 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
+
+// A route row is a set of key blocks (PHBA §A.1.2 routes to distinct strictly
+// preceding blocks; its block-major metadata lists each (query, block) pair
+// once): entry jj of a row, holding block j, is used only when j is a block
+// id in [0, nb) and no earlier entry of the row holds j.  The loop reads every
+// earlier entry without an early exit, so the reads can be issued together.
+__device__ __forceinline__ bool route_entry_used(const int* row, int jj, int j, int nb) {
+  if (j < 0 || j >= nb) return false;
+  bool first = true;
+  for (int x = 0; x < jj; ++x) first = first && row[x] != j;
+  return first;
+}
+
+// One whole wave appends to out[n0..) the used entries of the route row
+// raw[0..cnt) (both in LDS, raw visible to the wave) that also satisfy
+// keep(j), in row order; returns the new count, uniform across the wave.
+template <typename Keep>
+__device__ __forceinline__ int route_compact_wave(const int* raw, int cnt, int nb, int* out,
+                                                  int n0, Keep keep) {
+  const int l = threadIdx.x % 64;
+  int n = n0;
+  for (int base = 0; base < cnt; base += 64) {
+    const int jj = base + l;
+    const int j = jj < cnt ? raw[jj] : -1;
+    const bool ok = jj < cnt && route_entry_used(raw, jj, j, nb) && keep(j);
+    const unsigned long long m = __ballot(ok);
+    if (ok) out[n + __popcll(m & ((1ull << l) - 1ull))] = j;
+    n += __popcll(m);
+  }
+  return n;
+}

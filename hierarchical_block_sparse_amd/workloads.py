@@ -186,14 +186,15 @@ def make_grad_out(cfg: Config, device="cpu"):
     return _randn(shape, gen, device, torch.float32).to(cfg.dtype)
 
 
-def make_route(cfg: Config, with_invalid: bool = True):
+def make_route(cfg: Config, with_invalid: bool = True, repeats: bool = False):
     """A synthetic prefill route table [B, Hk, nqb, K+1] int32 (CPU): every row
     lists its diagonal block, then up to K distinct other blocks drawn uniformly
     from all blocks (future ones included: they are fully masked), in random
-    order, -1 padded; with_invalid puts an out-of-range id (nb) into some rows.
-    Used to drive the attention and its backward over routes the selection
-    would not produce."""
-    rng = np.random.default_rng(4000 + cfg.seed)
+    order, -1 padded; with_invalid puts an out-of-range id (nb) into some rows;
+    repeats lists one or two of a row's blocks a second time in about half of
+    the rows that have free slots.  Used to drive the attention and its
+    backward over routes the selection would not produce."""
+    rng = np.random.default_rng(4000 + cfg.seed + (7 if repeats else 0))
     nb = -(-cfg.kv_len // cfg.block)
     nqb = -(-cfg.q_len // cfg.block)
     K = cfg.top_k
@@ -206,6 +207,10 @@ def make_route(cfg: Config, with_invalid: bool = True):
                 row = [i] + [int(x) for x in rng.choice(others, size=n, replace=False)]
                 if with_invalid and n < K and rng.random() < 0.25:
                     row.append(nb)
+                if repeats and len(row) < K + 1 and rng.random() < 0.5:
+                    free = K + 1 - len(row)
+                    row += [row[int(rng.integers(len(row)))]
+                            for _ in range(int(rng.integers(1, min(2, free) + 1)))]
                 rng.shuffle(row)
                 out[bi, hk, i, :len(row)] = row
     return torch.from_numpy(out)

@@ -123,22 +123,31 @@ typedef struct pyr_problem {
 
 /* ---- geometry helpers (host-only, no device work; -1 on invalid input) ---- */
 
-/* Number of pyramid levels L, finest (64-token blocks) to the single root:
+/* PISA abstract: keys are pooled into O(log N) levels, each coarser level
+ * pooling b nodes of the one below.  Number of pyramid levels L, finest
+ * (64-token blocks) to the single root:
  * n_0 = ceil(C/64), n_{l+1} = ceil(n_l / b) until n = 1, with C the capacity
  * (kv_capacity, or kv_len when that is 0).  Levels above the root of the valid
  * keys hold one node: the mean of all of them. */
 int32_t pyr_num_levels(const pyr_problem* p);
 /* Node offset of a level inside one (batch, KV head) pyramid slab (finest
- * level first; levels are concatenated). */
+ * level first; levels are concatenated; PISA abstract, pooled levels). */
 int64_t pyr_level_offset(const pyr_problem* p, int32_t level);
-/* Nodes per (batch, KV head) slab: sum of all level sizes at the capacity. */
+/* Nodes per (batch, KV head) slab: sum of all level sizes at the capacity
+ * (PISA abstract: O(N) pooled nodes over the O(log N) levels). */
 int64_t pyr_pyramid_nodes(const pyr_problem* p);
 /* Planes of a pyramid slab: 1 for float32 problems, 2 for bfloat16 problems
- * (plane 1 repeats plane 0 split into bfloat16 pairs, see pyr_build_pyramid). */
+ * (plane 1 repeats plane 0 split into bfloat16 pairs, see pyr_build_pyramid;
+ * PHBA §A.1.2 keeps block summaries in fp32). */
 int32_t pyr_pyramid_planes(const pyr_problem* p);
-/* Query blocks per (batch, KV head): ceil(q_len/64) in prefill, 1 in decode. */
+/* Query blocks per (batch, KV head): ceil(q_len/64) in prefill, 1 in decode
+ * (PISA abstract: selection runs per query block). */
 int64_t pyr_num_query_blocks(const pyr_problem* p);
-/* Bytes of device workspace pyr_block_sparse_attn needs (0 if none). */
+/* Bytes of device workspace pyr_block_sparse_attn needs (0 if none): decode
+ * splits a unit's selected blocks over several workgroups and merges their
+ * partial online-softmax states (PHBA §A.1.3 keeps those accumulators on
+ * chip within one query tile; decode has one query token per unit, so its
+ * blocks are split to fill the GPU). */
 size_t pyr_attn_workspace_bytes(const pyr_problem* p);
 
 /* ---- the hot path ---- */
@@ -220,7 +229,8 @@ pyr_status pyr_budgets_from_entropy(const float* entropy, int32_t n_heads, int32
  * accumulation over routed blocks loaded straight from their original
  * layouts, writing output and log-sum-exp).  Query token t at position
  * pos(t) attends to every key s <= pos(t) of the blocks listed in its unit's
- * route row (entries < 0 are ignored).
+ * route row.  A route row is a set: entries < 0 are ignored and a block
+ * listed more than once is attended once.
  *   q, k, v    [B, Hq, q_len, d], [B, Hk, kv_len, d] x2, p->dtype    (input)
  *   sel        [B, Hk, nqb, K+1] int32 route rows (any valid block ids;
  *              pyr_select_topk writes them)                          (input)
@@ -290,9 +300,9 @@ pyr_status pyr_append_pyramid(const pyr_problem* p, const void* k, int64_t old_l
 size_t pyr_attn_bwd_workspace_bytes(const pyr_problem* p);
 
 /* Gradients of pyr_block_sparse_attn with respect to q, k and v (PHBA §A.1.4:
- * the route is fixed, the sparse scores and probabilities are recomputed on
- * chip from the forward's log-sum-exp, and the query rows that use each key
- * block are enumerated block-major for the key gradients).  With P the
+ * sparse backward for a fixed route; the kernels rebuild P on chip from the
+ * forward's log-sum-exp and list, for each key block, the query blocks that
+ * route to it when they form the key gradients).  With P the
  * forward's probabilities over each row's visible keys, dP = dout v^T,
  * D = rowsum(dout * o) and dS = P * (dP - D):
  *   dq = scale dS k,   dk = scale dS^T q,   dv = P^T dout,
@@ -301,9 +311,8 @@ size_t pyr_attn_bwd_workspace_bytes(const pyr_problem* p);
  * bfloat16 rounding per output.
  *   q, k, v    the forward's inputs, shapes as in pyr_block_sparse_attn (input)
  *   sel        the forward's route rows [B, Hk, nqb, K+1]; entries outside
- *              [0, ceil(kv_len/64)) are ignored.  A block listed twice in one
- *              row counts twice in dq but once in dk and dv, so rows must list
- *              each block at most once (pyr_select_topk's rows do)     (input)
+ *              [0, ceil(kv_len/64)) are ignored and a block listed more
+ *              than once counts once, as in the forward            (input)
  *   o, lse     the forward's output [B, Hq, q_len, d] and log-sum-exp
  *              [B, Hq, q_len] float32 (both required)                  (input)
  *   dout       dL/do, [B, Hq, q_len, d] bfloat16                       (input)

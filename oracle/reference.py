@@ -65,6 +65,12 @@ Readings of the pages this oracle rests on (the pages leave these open):
       keeps the best min(F, C) of the same candidates instead (F > K_h).
       Entropy budgets: K_h = clamp(round(total * H_h / sum H), k_min, k_max),
       rounding half up, an equal split when sum H = 0.
+  R18 A route row is a set of blocks: the attention of a query reads each
+      routed block once, however often the row lists it.  PHBA routes every
+      query to top-K distinct strictly preceding blocks (§A.1.2) and its
+      block-major metadata enumerates each (query, block) pair once (§A.1,
+      §A.1.4); a row the selection writes never repeats a block, so this only
+      fixes the meaning of rows written by hand.
 """
 
 from __future__ import annotations
@@ -363,6 +369,7 @@ def attend_rows(rows: np.ndarray, row_pos: np.ndarray, k_bh: np.ndarray, v_bh: n
     s <= its own position.  Returns (o [R, d], lse [R]) in float64.
     """
     Tk = k_bh.shape[0]
+    blocks = list(dict.fromkeys(int(j) for j in blocks))      # R18: each block once
     key_pos = np.concatenate([np.arange(j * block, min((j + 1) * block, Tk)) for j in blocks])
     kk = np.asarray(k_bh[key_pos], dtype=np.float64)
     vv = np.asarray(v_bh[key_pos], dtype=np.float64)
@@ -413,7 +420,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray, bloc
 
 def attend_rows_backward(rows: np.ndarray, row_pos: np.ndarray, k_bh: np.ndarray,
                          v_bh: np.ndarray, blocks: list[int], block: int, scale: float,
-                         d_out: np.ndarray, lse: np.ndarray):
+                         d_out: np.ndarray, lse: np.ndarray, o: np.ndarray | None = None):
     """Gradients of o = softmax(scale * rows k^T) v over the visible keys of
     `blocks` (the same visibility as attend_rows), given d_out = dL/do and the
     forward's lse.  With P the probabilities, dP = d_out v^T,
@@ -421,15 +428,23 @@ def attend_rows_backward(rows: np.ndarray, row_pos: np.ndarray, k_bh: np.ndarray
       d_rows = scale * dS k,  dk = scale * dS^T rows,  dv = P^T d_out.
     Returns (d_rows [R, d], key_pos [S], dk [S, d], dv [S, d]) in float64; the
     key rows dk and dv belong to the key positions key_pos.
+
+    o, when given, is the forward's output over the rows' whole route (the one
+    lse belongs to) and D is taken from it; `blocks` may then be any subset of
+    that route, and dk, dv are those keys' gradients exactly (d_rows is then
+    only the part of the subset).  When o is None, D comes from P over
+    `blocks`, which must be the whole route.
     """
     Tk = k_bh.shape[0]
+    blocks = list(dict.fromkeys(int(j) for j in blocks))      # R18: each block once
     key_pos = np.concatenate([np.arange(j * block, min((j + 1) * block, Tk)) for j in blocks])
     kk = np.asarray(k_bh[key_pos], dtype=np.float64)
     vv = np.asarray(v_bh[key_pos], dtype=np.float64)
     z = scale * (rows @ kk.T)                                  # [R, S]
     visible = key_pos[None, :] <= row_pos[:, None]
     p = np.where(visible, np.exp(z - lse[:, None]), 0.0)       # P from the log-sum-exp
-    o = p @ vv
+    if o is None:
+        o = p @ vv
     dp = d_out @ vv.T
     dsum = (d_out * o).sum(axis=1, keepdims=True)              # D
     ds = p * (dp - dsum)

@@ -239,6 +239,16 @@ def test_append_validation():
     assert s == 1
     s, _ = _status("pyr_append_pyramid", c, ptr, 999, ctypes.c_void_p(20), None)
     assert s == 4
+    # without a capacity the layout follows the length: an append across a
+    # block boundary would move every level above the finest
+    p0 = _p(q_len=1, kv_len=1000)
+    c0 = ctypes.byref(p0.c())
+    for old in (900, 960, 1):
+        s, msg = _status("pyr_append_pyramid", c0, ptr, old, ptr, None)
+        assert s == 2 and "kv_capacity" in msg, (old, msg)
+    # within the last block the layout is unchanged: validation goes on (and
+    # stops at the missing pointer before anything is launched)
+    assert _status("pyr_append_pyramid", c0, None, 961, ptr, None)[0] == 1
 
 
 def test_backward_rejects_capacity():
@@ -404,3 +414,4 @@ def test_select_attn_binding_rejects_wrong_shapes_on_host():
         H.pyr_select_attn(p, q, k, k, pyr, sel[..., :8].contiguous(), q)
     with pytest.raises(ValueError):        # every shape right, but host tensors
         H.pyr_select_attn(p, q, k, k, pyr, sel, q)
+

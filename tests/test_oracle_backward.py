@@ -150,3 +150,87 @@ def test_planted_mistakes_fail_the_pins(bad, monkeypatch):
     monkeypatch.setattr(ref, "attend_rows_backward", bad)
     with pytest.raises(AssertionError):
         test_finite_differences(0)
+
+
+def _repeat_entries(sel, seed):
+    """A copy of sel with K+1 widened by two slots, where about half of the rows
+    list one of their blocks a second (or third) time."""
+    rng = np.random.default_rng(seed)
+    B, Hk, nqb, W = sel.shape
+    out = np.full((B, Hk, nqb, W + 2), -1, np.int32)
+    out[..., :W] = sel
+    for idx in np.ndindex(B, Hk, nqb):
+        row = [int(x) for x in sel[idx] if x >= 0]
+        if rng.random() < 0.5:
+            extra = [row[int(rng.integers(len(row)))] for _ in range(int(rng.integers(1, 3)))]
+            row = row + extra
+            rng.shuffle(row)
+            out[idx][:len(row)] = row
+    return out
+
+
+@pytest.mark.parametrize("seed,Hq,Hk,T,d", [(11, 2, 1, 150, 8), (12, 4, 2, 200, 16)])
+def test_repeated_route_entries_count_once(seed, Hq, Hk, T, d):
+    """Reading R18: a block listed more than once in a route row is attended
+    once.  The masked dense formulation (the route as a set of columns, torch
+    softmax and autograd in float64) gives the forward and the gradients."""
+    q, k, v, do, sel = _case(seed, Hq=Hq, Hk=Hk, T=T, d=d, K=2)
+    rsel = _repeat_entries(sel, seed)
+    assert (np.sort(rsel, axis=-1)[..., 1:] == np.sort(rsel, axis=-1)[..., :-1]).any()
+    group = Hq // Hk
+    mask = torch.from_numpy(_dense_mask(rsel, T, group))
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    z = (tq @ tk.repeat_interleave(group, dim=1).transpose(-1, -2)) / math.sqrt(d)
+    p = torch.softmax(z.masked_fill(~mask, float("-inf")), dim=-1)
+    o_ref = p @ tv.repeat_interleave(group, dim=1)
+    (o_ref * torch.from_numpy(do)).sum().backward()
+    o, _ = ref.attention(q, k, v, rsel, 64)
+    assert np.abs(o - o_ref.detach().numpy()).max() <= 1e-12
+    dq, dk, dv = ref.attention_backward(q, k, v, rsel, 64, do)
+    assert np.abs(tq.grad.numpy() - dq).max() <= 1e-10
+    assert np.abs(tk.grad.numpy() - dk).max() <= 1e-10
+    assert np.abs(tv.grad.numpy() - dv).max() <= 1e-10
+
+
+def test_one_key_block_from_the_forward_output():
+    """Given the forward's o and lse over the whole route, the gradients of the
+    keys of any one routed block come out of attend_rows_backward over that
+    block alone, equal to the rows of the whole-route computation."""
+    rng = np.random.default_rng(21)
+    T, d, R = 6 * 64 + 9, 16, 40
+    k = rng.standard_normal((T, d))
+    v = rng.standard_normal((T, d))
+    rows = rng.standard_normal((R, d))
+    pos = np.sort(rng.integers(5 * 64, T, size=R))
+    g = rng.standard_normal((R, d))
+    blocks = [0, 2, 3, 6]
+    scale = 1 / math.sqrt(d)
+    o, lse = ref.attend_rows(rows, pos, k, v, blocks, 64, scale)
+    _, kp, dk, dv = ref.attend_rows_backward(rows, pos, k, v, blocks, 64, scale, g, lse)
+    for j in blocks:
+        _, kpj, dkj, dvj = ref.attend_rows_backward(rows, pos, k, v, [j], 64, scale, g, lse, o=o)
+        sl = np.isin(kp, kpj)
+        assert np.array_equal(kp[sl], kpj)
+        assert np.abs(dk[sl] - dkj).max() <= 1e-12 * max(1.0, np.abs(dk).max())
+        assert np.abs(dv[sl] - dvj).max() <= 1e-12 * max(1.0, np.abs(dv).max())
+    # without o the one-block call takes D from that block alone: a different
+    # (wrong for a subset) value, which shows that o is what carries D
+    _, _, dk0, _ = ref.attend_rows_backward(rows, pos, k, v, [0], 64, scale, g, lse)
+    assert np.abs(dk0 - dk[np.isin(kp, np.arange(64))]).max() > 1e-6
+
+
+def _attend_counting_repeats(rows, row_pos, k_bh, v_bh, blocks, block, scale):
+    # planted: a block listed twice in a route row is attended twice
+    Tk = k_bh.shape[0]
+    kp = np.concatenate([np.arange(j * block, min((j + 1) * block, Tk)) for j in blocks])
+    z = np.where(kp[None, :] <= row_pos[:, None], scale * rows @ k_bh[kp].T, -np.inf)
+    mx = z.max(axis=1, keepdims=True)
+    p = np.exp(z - mx)
+    den = p.sum(axis=1, keepdims=True)
+    return (p @ v_bh[kp]) / den, mx[:, 0] + np.log(den[:, 0])
+
+
+def test_planted_repeat_counting_fails_the_pin(monkeypatch):
+    monkeypatch.setattr(ref, "attend_rows", _attend_counting_repeats)
+    with pytest.raises(AssertionError):
+        test_repeated_route_entries_count_once(11, 2, 1, 150, 8)
