@@ -11,7 +11,8 @@ from ._binding import (  # noqa: F401
     alloc_trace, alloc_workspace, backward, declared_functions, forward, forward_packed, lib,
     problem_for, problem_for_packed,
     pyr_abi_version, pyr_append_pyramid, pyr_attn_bwd_workspace_bytes, pyr_attn_workspace_bytes,
-    pyr_block_sparse_attn, pyr_block_sparse_attn_bwd, pyr_build_pyramid, pyr_level_offset,
+    pyr_block_sparse_attn, pyr_block_sparse_attn_bwd, pyr_block_sparse_attn_noalloc,
+    pyr_build_pyramid, pyr_level_offset,
     pyr_num_levels, pyr_num_query_blocks, pyr_pyramid_nodes, pyr_pyramid_planes,
     pyr_budgets_from_entropy, pyr_select_attn, pyr_select_topk, pyr_select_topk_budgets,
     pyramid_shape,

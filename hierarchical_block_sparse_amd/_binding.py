@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libpyr.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "pyr.h")
 
 PYR_F32, PYR_BF16 = 0, 1
-ABI_VERSION = 4  # PYR_ABI_VERSION of the include/pyr.h these wrappers marshal for
+ABI_VERSION = 5  # PYR_ABI_VERSION of the include/pyr.h these wrappers marshal for
 STATUS = {0: "PYR_OK", 1: "PYR_ERR_NULL", 2: "PYR_ERR_INVALID", 3: "PYR_ERR_UNSUPPORTED",
           4: "PYR_ERR_MISALIGNED", 5: "PYR_ERR_WORKSPACE", 6: "PYR_ERR_HIP"}
 
@@ -72,6 +72,7 @@ def lib():
             ("pyr_budgets_from_entropy", st,
              [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]),
             ("pyr_block_sparse_attn", st, [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+            ("pyr_block_sparse_attn_noalloc", st, [P, vp, vp, vp, vp, vp, vp, vp]),
             ("pyr_select_attn", st,
              [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
             ("pyr_attn_bwd_workspace_bytes", ctypes.c_size_t, [P]),
@@ -295,6 +296,20 @@ def pyr_block_sparse_attn(p: Problem, q, k, v, sel, o, lse=None, workspace=None,
     _check(lib().pyr_block_sparse_attn(_cp(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
                                        _ptr(o), _ptr(lse), _ptr(workspace), nbytes,
                                        _stream(stream)))
+
+
+def pyr_block_sparse_attn_noalloc(p: Problem, q, k, v, sel, o, lse=None, stream=None):
+    """pyr_block_sparse_attn without a workspace: the library's fixed
+    per-device scratch array holds the decode partials (nothing is allocated)."""
+    nqb = pyr_num_query_blocks(p)
+    _expect(q, "q", p.q_shape, p.dtype)
+    _expect(k, "k", p.kv_shape, p.dtype)
+    _expect(v, "v", p.kv_shape, p.dtype)
+    _expect(sel, "sel", (p.batch, p.n_kv_heads, nqb, p.top_k + 1), torch.int32)
+    _expect(o, "o", p.q_shape, p.dtype)
+    _expect(lse, "lse", p.lse_shape, torch.float32)
+    _check(lib().pyr_block_sparse_attn_noalloc(_cp(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
+                                               _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def pyr_select_attn(p: Problem, q, k, v, pyramid, sel, o, lse=None, workspace=None,

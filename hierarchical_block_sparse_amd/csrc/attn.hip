@@ -30,6 +30,9 @@
 //    cores, the query rows padded to a 16-wide tile.
 #include <math.h>
 
+#include <mutex>
+
+#include "../../include/pyr.h"
 #include "pyr_device.h"
 #include "pyr_internal.h"
 #include "select_core.h"
@@ -1388,3 +1391,61 @@ hipError_t pyr_launch_attn(const PyrGeom& g, int dtype, const void* q, const voi
                    : launch_attn_d<128>(g, dtype, q, k, v, sel, o, lse, ws, st);
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free attention entry point
+// (pyr_block_sparse_attn_noalloc): the decode partial states live in this
+// fixed device array instead of a caller's workspace.  Every GPU the library
+// runs on holds its own copy until the process ends; host code reaches a
+// device's copy only through the address hipGetSymbolAddress returns for it
+// (the array's name is a host-side stand-in, not a device address).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[PYR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device, resolved on first use
+
+// Device address of `scratch` on the device that runs stream st (the current
+// device for the null stream), looked up once per device with that device
+// current.
+hipError_t scratch_of(hipStream_t st, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (st) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(st, &d);
+    if (e != hipSuccess) return e;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t pyr_launch_attn_noalloc(const PyrGeom& g, int dtype, const void* q, const void* k,
+                                   const void* v, const int32_t* sel, void* o, float* lse,
+                                   hipStream_t st) {
+  void* ws = nullptr;
+  if (pyr_attn_ws_bytes(g) > 0) {
+    const hipError_t e = scratch_of(st, &ws);
+    if (e != hipSuccess) return e;
+  }
+  return pyr_launch_attn(g, dtype, q, k, v, sel, o, lse, ws, st);
+}

@@ -253,6 +253,29 @@ pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void
                     "pyr_block_sparse_attn launch");
 }
 
+pyr_status pyr_block_sparse_attn_noalloc(const pyr_problem* p, const void* q, const void* k,
+                                         const void* v, const int32_t* sel, void* o,
+                                         float* lse, hipStream_t stream) {
+  g_err[0] = 0;
+  PyrGeom g;
+  pyr_status s = resolve(p, &g);
+  if (s != PYR_OK) return s;
+  const bool empty = (int64_t)g.B * g.Hk * g.nqb == 0 || g.Tq == 0 || (g.cu && g.Tqs == 0);
+  if (!empty && (!q || !k || !v || !sel || !o)) return fail(PYR_ERR_NULL, "q, k, v, sel or o is NULL");
+  if (!empty && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) ||
+                 !aligned16(o) || (lse && !aligned16(lse))))
+    return fail(PYR_ERR_MISALIGNED, "tensors must be 16-byte aligned");
+  const size_t need = pyr_attn_ws_bytes(g);
+  if (!empty && need > PYR_NOALLOC_SCRATCH_BYTES)
+    return fail(PYR_ERR_WORKSPACE,
+                "this problem needs %zu bytes of scratch; the allocation-free entry point holds "
+                "%zu per device (use pyr_block_sparse_attn with a workspace)",
+                need, (size_t)PYR_NOALLOC_SCRATCH_BYTES);
+  if (empty) return PYR_OK;
+  return hip_status(pyr_launch_attn_noalloc(g, p->dtype, q, k, v, sel, o, lse, stream),
+                    "pyr_block_sparse_attn_noalloc launch");
+}
+
 pyr_status pyr_select_attn(const pyr_problem* p, const void* q, const void* k, const void* v,
                            const float* pyramid, int32_t* sel, int32_t* trace_ids,
                            float* trace_scores, void* o, float* lse, void* workspace,

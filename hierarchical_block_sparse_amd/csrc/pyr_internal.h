@@ -92,6 +92,11 @@ size_t pyr_attn_ws_bytes(const PyrGeom& g);
 hipError_t pyr_launch_attn(const PyrGeom& g, int dtype, const void* q, const void* k,
                            const void* v, const int32_t* sel, void* o, float* lse, void* ws,
                            hipStream_t st);
+// The attention with its workspace (if any) in the library's fixed per-device
+// scratch array; the caller has checked pyr_attn_ws_bytes(g) against its size.
+hipError_t pyr_launch_attn_noalloc(const PyrGeom& g, int dtype, const void* q, const void* k,
+                                   const void* v, const int32_t* sel, void* o, float* lse,
+                                   hipStream_t st);
 // Selection then attention: one fused launch where pyr_select_attend_fused
 // holds (bf16 prefill, four query heads per KV head, the selection's layout
 // fits one tile slot), else the two launchers above in turn.

@@ -74,7 +74,10 @@
 extern "C" {
 #endif
 
-#define PYR_ABI_VERSION 4
+#define PYR_ABI_VERSION 5
+
+/* Bytes of the fixed per-device scratch array of pyr_block_sparse_attn_noalloc. */
+#define PYR_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 typedef enum pyr_status {
   PYR_OK = 0,
@@ -243,6 +246,24 @@ pyr_status pyr_budgets_from_entropy(const float* entropy, int32_t n_heads, int32
 pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void* k,
                                  const void* v, const int32_t* sel, void* o, float* lse,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* pyr_block_sparse_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that must not call hipMalloc, and
+ * harnesses that forbid allocation.  Same arguments, results and errors as
+ * pyr_block_sparse_attn without the workspace: when the problem needs one
+ * (decode: pyr_attn_workspace_bytes(p) > 0), its partial states go to a
+ * device array of PYR_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds
+ * on every GPU it runs on until the process ends (64 sequences x 8 KV heads x
+ * 4 query heads per KV head at top_k = 64 and head_dim = 128 take 9.6 MB).
+ * Problems that need more return PYR_ERR_WORKSPACE before anything is
+ * enqueued.  Nothing is allocated or freed; the first call on a device looks
+ * up that device's array.  Every call on a GPU shares its array and leaves its
+ * contents behind (each call writes every partial it reads), so calls that
+ * can overlap on one GPU -- on different streams, or from several threads --
+ * race and must be ordered by the caller. */
+pyr_status pyr_block_sparse_attn_noalloc(const pyr_problem* p, const void* q, const void* k,
+                                         const void* v, const int32_t* sel, void* o,
+                                         float* lse, hipStream_t stream);
 
 /* Selection and attention in one call (PISA abstract: the kernels fuse the
  * hierarchical routing with the LogSumExp scoring; PHBA §A.1.3: the forward

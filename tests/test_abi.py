@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     assert {"pyr_build_pyramid", "pyr_select_topk", "pyr_block_sparse_attn"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert H.pyr_abi_version() == 4
+    assert H.pyr_abi_version() == 5
 
 
 def test_single_hip_runtime_in_process():
@@ -415,3 +415,23 @@ def test_select_attn_binding_rejects_wrong_shapes_on_host():
     with pytest.raises(ValueError):        # every shape right, but host tensors
         H.pyr_select_attn(p, q, k, k, pyr, sel, q)
 
+
+def test_noalloc_validation_before_launch():
+    """The allocation-free attention entry point validates like
+    pyr_block_sparse_attn (minus the workspace) and refuses, before any HIP
+    call, a problem whose partial states exceed its fixed scratch array."""
+    ptr = ctypes.c_void_p(16)
+    fn = "pyr_block_sparse_attn_noalloc"
+    dec = _p(batch=512, n_q_heads=32, n_kv_heads=8, q_len=1, kv_len=4096, top_k=64)
+    assert H.pyr_attn_workspace_bytes(dec) > 16 << 20
+    s, msg = _status(fn, ctypes.byref(dec.c()), ptr, ptr, ptr, ptr, ptr, None, None)
+    assert s == 5 and "16777216" in msg
+    p = _p()
+    for i in range(5):                     # q, k, v, sel, o may not be NULL
+        ptrs = [ptr] * 5
+        ptrs[i] = None
+        assert _status(fn, ctypes.byref(p.c()), *ptrs, None, None)[0] == 1, i
+    s, _ = _status(fn, ctypes.byref(p.c()), ptr, ptr, ptr, ptr, ptr, ctypes.c_void_p(20), None)
+    assert s == 4
+    bad = _p(head_dim=96)
+    assert _status(fn, ctypes.byref(bad.c()), ptr, ptr, ptr, ptr, ptr, None, None)[0] == 3
