@@ -101,3 +101,31 @@ def test_backward_repeated_route_entries():
         e_fro = float(np.linalg.norm(dd - ref) / max(np.linalg.norm(ref), 1e-30))
         GH.log(f"  {name}: max err {e_max:.2e} of max|ref| {scale:.3e}, rel fro {e_fro:.2e}")
         assert e_max <= 2e-2 and e_fro <= 1e-2, name
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_scores_far_above_the_first_block(d):
+    """Rows whose scores on a later block exceed those on their first block by
+    far more than the 2^64 headroom of a fixed softmax reference: the output
+    must still be exact softmax attention (the kernel recomputes such rows
+    with exact maxima).  Query rows are (32, 0, ...); keys of block 0 are
+    zero, keys of block 3 are (64, 0, ...), so block 3 scores 2048 * scale
+    (about 261 in log2 units at d = 128) and block 0 scores 0."""
+    T = 64 * 8 + 5
+    cfg = C(f"far_scores_d{d}", 1, 8, 2, T, T, d, BF, 4, 8, 0, seed=58)
+    q, k, v = W.make_inputs(cfg, "cuda")
+    q[:, :, 64 * 4:] = 0
+    q[:, :, 64 * 4:, 0] = 32.0
+    k[:, :, 0:64] = 0
+    k[:, :, 3 * 64:4 * 64] = 0
+    k[:, :, 3 * 64:4 * 64, 0] = 64.0
+    nqb = -(-T // 64)
+    route = torch.full((1, 2, nqb, 9), -1, dtype=torch.int32)
+    for i in range(nqb):
+        route[0, :, i, :i + 1] = torch.arange(i + 1)
+    dev = GH.run_device(cfg, q, k, v, trace=False, sel_in=route)
+    e_o, e_l = GH.judge_attention(GH.f64(q), GH.f64(k), GH.f64(v), cfg, route.numpy(), dev["o"],
+                                  dev["lse"], GH.all_units(cfg))
+    tol_o, tol_l = GH.TOL[cfg.dtype]
+    GH.log(f"  {cfg.name}: O err {e_o:.3e}, LSE err {e_l:.3e}")
+    assert e_o <= tol_o and e_l <= tol_l
