@@ -17,7 +17,9 @@ from dataclasses import dataclass, field
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpyr.so")
+# PYR_LIBRARY names another build of the same library (the host-sanitizer build
+# of hierarchical_block_sparse_amd.build, which the CPU ABI tests load).
+LIB_PATH = os.environ.get("PYR_LIBRARY") or os.path.join(_HERE, "libpyr.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "pyr.h")
 
 PYR_F32, PYR_BF16 = 0, 1
