@@ -16,6 +16,12 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 32;   // candidates per LDS chunk (MFMA path): two 16-wide N tiles
 constexpr int kZbuf = 8192;  // fp32 scratch for the generic path
 constexpr int kSelStages = 2;  // candidate chunks in LDS (MFMA path): one scored while one loads
+// Slots after the ancestors in the layout's misc area (4 bytes each).
+enum SelMisc {
+  kNkept = 0,    // kept count
+  kMargin = 1,   // K-th best minus best rejected score (fallback)
+  kMiscSlots = 4
+};
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -35,7 +41,7 @@ struct SelLayout {
     off_rank = o;   o += 4 * cmax;
     if (mfma) {
       off_part = o;  o += 8 * waves * cmax;                 // float2 [wave][candidate]
-      off_misc = o;  o += 4 * (PYR_MAX_LEVELS + 4);         // int ancestors, kept count
+      off_misc = o;  o += 4 * (PYR_MAX_LEVELS + kMiscSlots);  // ancestors, then SelMisc slots
       off_hl = off_zbuf = o;
     } else {
       off_part = off_hl = off_misc = o;
@@ -176,7 +182,7 @@ __device__ void top_k_and_trace(const PyrGeom& g, int C, int level, const int* c
       *nkept = K;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (tr_ids) {
     for (int j = tid; j < g.K; j += NT) tr_ids[level * g.K + j] = j < K ? kept[j] : -1;
   }
@@ -202,7 +208,7 @@ __device__ __forceinline__ int unit_budget(const PyrGeom& g, int hk) {
 __device__ __forceinline__ bool fallback_due(const PyrGeom& g, int level, int kk, int Ku,
                                              const float* margin) {
   if (level != 0 || kk != Ku || g.fb_k <= Ku) return false;
-  __syncthreads();  // the trace of the first pass has read kept[]; *margin is visible
+  lds_barrier();  // the trace of the first pass has read kept[]; *margin is visible
   return *margin < g.fb_margin;
 }
 
@@ -225,7 +231,7 @@ __device__ int build_candidates(const PyrGeom& g, int level, const int* s_anc, c
   }
   for (int j = threadIdx.x; j < C; j += NT)
     cand[j] = j < nchild ? kept[j / b] * b + j % b : base + (j - nchild);
-  __syncthreads();
+  lds_barrier();
   return C;
 }
 
@@ -242,7 +248,7 @@ __device__ void keep_all(const PyrGeom& g, int C, int level, const int* cand, in
   if (tr_scores)
     for (int j = threadIdx.x; j <= K; j += NT) tr_scores[level * (K + 1) + j] = NAN;
   if (threadIdx.x == 0) *nkept = C;
-  __syncthreads();
+  lds_barrier();
 }
 
 template <int NT>
@@ -273,29 +279,36 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
 
-// Split rows of chunk c's candidates (plane 1 of the pyramid: per node a bf16
-// hi row and a bf16 lo row, 4D bytes) into one LDS stage with direct 16-byte
-// loads, no register staging.  Load t of a thread fills stage chunk
-// p = t * NT + tid (the 64 lanes of a wave fill 1 KiB in lane order):
-// candidate p / CPC, row part (p % CPC) / CPR (hi, lo), stored chunk q =
-// p % CPR, which holds logical chunk q ^ (candidate % CPR) of that row, so the
-// 16 candidates of an MFMA B fragment lie in different banks.  Positions past
-// C load candidate 0 (finite values that are never scored).
+// Split rows of list entries [32c, 32c + 32) (plane 1 of the pyramid: per
+// node a bf16 hi row and a bf16 lo row, 4D bytes) into one LDS stage with
+// direct 16-byte loads, no register staging.  Entry jj is candidate
+// cand[pos[jj]] (cand[jj] when pos is null).  Load t of a thread fills stage
+// chunk p = t * NT + tid (the 64 lanes of a wave fill 1 KiB in lane order):
+// entry p / CPC, row part (p % CPC) / CPR (hi, lo), stored chunk q = p % CPR,
+// which holds logical chunk q ^ (entry % CPR) of that row, so the 16 entries
+// of an MFMA B fragment lie in different banks.  Positions past n load entry
+// 0 (finite values that are never scored).
 template <int D, int NT>
-__device__ __forceinline__ void issue_chunk(const unsigned char* split, const int* cand, int C,
-                                            int c, unsigned char* stage, int w, int l) {
+__device__ __forceinline__ void issue_chunk(const unsigned char* split, const int* cand,
+                                            const int* pos, int n, int c, unsigned char* stage,
+                                            int w, int l) {
   constexpr int CPR = D / 8;       // 16-byte chunks per bf16 row
   constexpr int CPC = 2 * CPR;     // per candidate (hi, lo)
   constexpr int PER = kChunk * CPC / NT;
   static_assert(kChunk * CPC % NT == 0, "chunk must split evenly");
+  // opaque to the optimiser, so the per-load offsets below are recomputed
+  // here rather than hoisted out of the level loop into spilled registers
+  uint32_t tl = (uint32_t)(w * 64 + l);
+  asm volatile("" : "+v"(tl));
 #pragma unroll
   for (int t = 0; t < PER; ++t) {
-    const int p = t * NT + w * 64 + l;
-    const int cc = p / CPC, part = (p % CPC) / CPR, q = p % CPR;
-    const int j = c * kChunk + cc;
-    const int node = cand[j < C ? j : 0];
+    const uint32_t p = t * NT + tl;
+    const uint32_t cc = p / CPC, part = (p % CPC) / CPR, q = p % CPR;
+    const int j = c * kChunk + (int)cc;
+    const int jj = j < n ? j : 0;
+    const int node = cand[pos ? pos[jj] : jj];
     const unsigned char* src =
-        split + (int64_t)node * 4 * D + part * 2 * D + ((q ^ (cc % CPR)) << 4);
+        split + (size_t)(uint32_t)node * (4 * D) + (part * 2 * D + ((q ^ (cc % CPR)) << 4));
     __builtin_amdgcn_global_load_lds((const void*)src,
                                      (lds_void*)(stage + (t * NT + w * 64) * 16), 16, 0, 0);
   }
@@ -350,13 +363,160 @@ __device__ __forceinline__ void tile_lse(const f32x4 (&acc)[MT], uint32_t rowval
   s = sum32(sum16(s));
 }
 
+// Exact scores' LogSumExp partials of list entries [0, n) (entry jj is
+// candidate cand[pos[jj]], cand[jj] when pos is null): both planes of the
+// split contracted against the exact bf16 q on the matrix cores, chunks of 32
+// entries through stages st0 / st1.  Per wave and entry the (max, sum) pair
+// of the wave's rows goes to part[w * cmax + entry].  Every thread calls it;
+// the caller's barrier makes the partials visible.  A candidate's partials do
+// not depend on its position in the list or on the other entries.
+template <int D, int MT, int NW>
+__device__ __forceinline__ void score_exact(const unsigned char* lvl, const int* cand,
+                                            const int* pos, int n, const uint4 (&qa)[MT][D / 32],
+                                            uint32_t rowvalid, bool full, float sl2,
+                                            lds_f32x2* part, int cmax, unsigned char* st0,
+                                            unsigned char* st1, int w, int l) {
+  constexpr int CPR = D / 8;
+  const int nchunks = (n + kChunk - 1) / kChunk;
+  // chunk c+1 loads while chunk c is scored; stage of chunk c is c % 2
+  issue_chunk<D, NW * 64>(lvl, cand, pos, n, 0, st0, w, l);
+  for (int c = 0; c < nchunks; ++c) {
+    // this wave's loads of chunk c have landed; after the barrier every
+    // wave's have, and the stage of chunk c-1 is free
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    lds_barrier();
+    if (c + 1 < nchunks)
+      issue_chunk<D, NW * 64>(lvl, cand, pos, n, c + 1, (c + 1) & 1 ? st1 : st0, w, l);
+    const unsigned char* st = c & 1 ? st1 : st0;
+#pragma unroll
+    for (int nt = 0; nt < kChunk / 16; ++nt) {
+      if (c * kChunk + nt * 16 >= n) break;  // uniform
+      f32x4 acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // B fragment: entry r = nt*16 + l%16, logical chunk 4*ks + l/16 of its
+      // hi and lo rows, stored at that chunk ^ (r % CPR)
+      const int r = nt * 16 + (l % 16);
+      const unsigned char* row = st + r * 4 * D;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const int off = ((4 * ks + l / 16) ^ (r % CPR)) << 4;
+        const bf16x8 bhv = as_bf16x8(*reinterpret_cast<const uint4*>(row + off));
+        const bf16x8 blv = as_bf16x8(*reinterpret_cast<const uint4*>(row + 2 * D + off));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), bhv, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), blv, acc[mt], 0, 0, 0);
+        }
+      }
+      // this wave's LogSumExp over its rows, per entry (lane column l % 16)
+      float m, s;
+      if (full)
+        tile_lse<MT, true>(acc, rowvalid, sl2, m, s);
+      else
+        tile_lse<MT, false>(acc, rowvalid, sl2, m, s);
+      const int cn = c * kChunk + nt * 16 + l;
+      if (l < 16 && cn < n) part[w * cmax + cn] = f32x2{m, s};
+    }
+  }
+}
+
+// Merged score of entry j from the waves' partials (natural log; NaN ranks
+// last as -inf).  The exact path and the re-scoring of undecided candidates
+// both use it, so a candidate gets the same bits from either.
+template <int NW>
+__device__ __forceinline__ float merged_score(const lds_f32x2* part, int cmax, int j) {
+  float m = -INFINITY, s = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    const f32x2 p = part[ww * cmax + j];
+    lse2_merge(m, s, p.x, p.y);
+  }
+  const float sc = (m + log2f(s)) * PYR_LN2;
+  return sc == sc ? sc : -INFINITY;
+}
+
+// Number of keys among key[0, n) above kj (keys are distinct and nonzero;
+// n is a multiple of 16, padded with zero keys).  Sixteen keys are read per
+// batch so that one LDS latency covers them.
+__device__ __forceinline__ int count_above(const uint64_t* key, int n, uint64_t kj) {
+  int cnt = 0;
+  for (int i = 0; i < n; i += 16) {
+    ulonglong2 a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = *reinterpret_cast<const ulonglong2*>(key + i + 2 * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cnt += (a[u].x > kj) + (a[u].y > kj);
+  }
+  return cnt;
+}
+
+// Rank key of a score at candidate position j: larger score first, then the
+// lower position (the lower node index: candidates ascend by index).
+__device__ __forceinline__ uint64_t rank_key(float sc, int j) {
+  return ((uint64_t)score_key(sc) << 32) | (uint32_t)~(uint32_t)j;
+}
+
+// Ranking of one scored level without a score trace or fallback, after
+// score_exact and its barrier: every candidate's merged score gets a 64-bit
+// key (score, then the lower position), each thread counts the keys above
+// its candidates' (the ranks, spread over all waves), the candidates ranked
+// below Ku are flagged, and wave 0 compacts them in index order into kept[].
+// The kept set is the one top_k_and_trace keeps from the same scores.
+template <int NW>
+__device__ __forceinline__ void rank_level(const PyrGeom& g, int level, int C, int Ku,
+                                           const SelLayout& lay, unsigned char* smem,
+                                           int32_t* tr_ids, int w, int l) {
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x, cmax = lay.cmax;
+  int* kept = reinterpret_cast<int*>(smem + lay.off_kept);
+  const int* cand = reinterpret_cast<const int*>(smem + lay.off_cand);
+  int* flag = reinterpret_cast<int*>(smem + lay.off_rank);
+  const lds_f32x2* part = (const lds_f32x2*)(smem + lay.off_part);
+  // a key overwrites the wave-0 partial of its own candidate, read just before
+  uint64_t* key = reinterpret_cast<uint64_t*>(smem + lay.off_part);
+  int* misc = reinterpret_cast<int*>(smem + lay.off_misc) + PYR_MAX_LEVELS;
+  const int C16 = (C + 15) & ~15;  // <= cmax, a multiple of 32
+  for (int j = tid; j < C16; j += NT) key[j] = j < C ? rank_key(merged_score<NW>(part, cmax, j), j) : 0ull;
+  lds_barrier();
+  for (int j = tid; j < C; j += NT) flag[j] = count_above(key, C16, key[j]) < Ku;
+  lds_barrier();
+  if (w == 0) {
+    const uint64_t lt = (1ull << l) - 1ull;
+    int nk = 0;
+    for (int j0 = 0; j0 < C; j0 += 256) {
+      // four chunks' flags and ids read together
+      bool f[4];
+      int id[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + 64 * u + l;
+        f[u] = j < C && flag[j] != 0;
+        id[u] = j < C ? cand[j] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint64_t mk = __ballot(f[u]);
+        if (f[u]) kept[nk + __popcll(mk & lt)] = id[u];
+        nk += __popcll(mk);
+      }
+    }
+    if (l == 0) misc[kNkept] = Ku;
+  }
+  lds_barrier();
+  if (tr_ids)
+    for (int j = tid; j < g.K; j += NT) tr_ids[level * g.K + j] = j < Ku ? kept[j] : -1;
+}
+
 // Selection of one unit on the matrix cores by NW waves of MT M tiles each.
 // smem: the dynamic layout SelLayout(K, b, D, true, NW); st0 and st1: the two
 // candidate stages (kChunk * 4 * D bytes each), LDS of their own so that
 // writes to the layout do not wait for the stage loads in flight.  Must be
 // called by every thread of the workgroup.  Leaves the finest kept set in
 // the layout's kept[] and its size in the kept count, and writes the route
-// row (and trace) of the unit.
+// row (and trace) of the unit.  Without a score trace and without a
+// fallback, scored levels are ranked by rank_level; otherwise by
+// top_k_and_trace, which also records scores and the margin.
 template <int D, int MT, int NW>
 __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
                                                  const float* __restrict__ pyr,
@@ -366,7 +526,7 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
                                                  const PyrGeom& g, int64_t unit,
                                                  unsigned char* smem, unsigned char* st0,
                                                  unsigned char* st1) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per bf16 row
+  constexpr int NT = NW * 64;
   const SelLayout lay(g.K, g.branching, D, true, NW);
   int* kept = reinterpret_cast<int*>(smem + lay.off_kept);
   float* kscore = reinterpret_cast<float*>(smem + lay.off_kscore);
@@ -375,8 +535,10 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
   int* rank = reinterpret_cast<int*>(smem + lay.off_rank);
   lds_f32x2* part = (lds_f32x2*)(smem + lay.off_part);
   int* s_anc = reinterpret_cast<int*>(smem + lay.off_misc);
-  int& s_nkept = s_anc[PYR_MAX_LEVELS];
-  float* s_margin = reinterpret_cast<float*>(s_anc + PYR_MAX_LEVELS + 1);
+  int* misc = s_anc + PYR_MAX_LEVELS;
+  float* miscf = reinterpret_cast<float*>(misc);
+  int& s_nkept = misc[kNkept];
+  float* s_margin = miscf + kMargin;
 
   const int tid = threadIdx.x, l = tid % 64;
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -385,7 +547,7 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
   const int bi = (int)(bhk / g.Hk), hk = (int)(bhk % g.Hk);
   const PyrSeq sq = pyr_seq(g, bi);
   if (i >= sq.nqb) {
-    blank_unit<NW * 64>(g, unit, sel, trace_ids, trace_scores);
+    blank_unit<NT>(g, unit, sel, trace_ids, trace_scores);
     return;
   }
   // decode: one query block whose token sits at kv_len - 1; its G rows (one
@@ -394,9 +556,9 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
   const int Ku = unit_budget(g, hk);
   const int RW = MT * 16;  // rows per wave
   const float sl2 = g.scale * PYR_LOG2E;
-  const int cmax = lay.cmax;
+  // no score trace and no fallback: the kept sets come from rank_level
+  const bool ranked = !trace_scores && g.fb_k <= Ku;
 
-  if (tid == 0) s_nkept = 0;
   ancestors(g, diag, s_anc);
 
   // Q fragments (A operand): lane holds row (l % 16) of each M tile and the
@@ -425,7 +587,6 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
       if (real) rowvalid |= 1u << (mt * 4 + j);
     }
   }
-
   // every row of the unit is real
   const bool full = !g.decode && (int64_t)(i + 1) * PYR_BLOCK <= sq.Tq;
   // plane 1 of the slab: the split rows
@@ -433,83 +594,55 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
       reinterpret_cast<const unsigned char*>(pyr + (bhk * g.planes + 1) * g.n_tot * D);
   int32_t* tr_ids = trace_ids ? trace_ids + unit * g.L * g.K : nullptr;
   float* tr_sc = trace_scores ? trace_scores + unit * g.L * (g.K + 1) : nullptr;
-  __syncthreads();
+  lds_barrier();
+  // Coarse levels with at most Ku candidates keep them all.  While every
+  // level above keeps all, the candidates of level l are the nodes before
+  // the diagonal's ancestor, [0, anc[l]); so the first scored level is the
+  // coarsest with anc[l] > Ku, and the kept set above it is [0, anc[top+1]).
+  int top = g.L - 1;
+  while (top >= 0 && s_anc[top] <= Ku) --top;
+  for (int lv = g.L - 1; lv > top; --lv) {
+    if (tr_ids)
+      for (int j = tid; j < g.K; j += NT) tr_ids[lv * g.K + j] = j < s_anc[lv] ? j : -1;
+    if (tr_sc)
+      for (int j = tid; j <= g.K; j += NT) tr_sc[lv * (g.K + 1) + j] = NAN;
+  }
+  const int nabove = top + 1 < g.L ? s_anc[top + 1] : 0;
+  for (int j = tid; j < nabove; j += NT) kept[j] = j;
+  if (tid == 0) s_nkept = nabove;
+  lds_barrier();
 
-  for (int level = g.L - 1; level >= 0; --level) {
-    const int C = build_candidates<NW * 64>(g, level, s_anc, kept, s_nkept, cand);
+  for (int level = top; level >= 0; --level) {
+    const int C = build_candidates<NT>(g, level, s_anc, kept, s_nkept, cand);
     if (C <= Ku) {
-      keep_all<NW * 64>(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
+      keep_all<NT>(g, C, level, cand, kept, &s_nkept, tr_ids, tr_sc);
       continue;
     }
     const unsigned char* lvl = split + g.loff[level] * 4 * D;
-    const int nchunks = (C + kChunk - 1) / kChunk;
-    // chunk c+1 loads while chunk c is scored; stage of chunk c is c % 2
-    issue_chunk<D, NW * 64>(lvl, cand, C, 0, st0, w, l);
-    for (int c = 0; c < nchunks; ++c) {
-      // this wave's loads of chunk c have landed; after the barrier every
-      // wave's have, and the stage of chunk c-1 is free
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      lds_barrier();
-      if (c + 1 < nchunks)
-        issue_chunk<D, NW * 64>(lvl, cand, C, c + 1, (c + 1) & 1 ? st1 : st0, w, l);
-      const unsigned char* st = c & 1 ? st1 : st0;
-#pragma unroll
-      for (int nt = 0; nt < kChunk / 16; ++nt) {
-        if (c * kChunk + nt * 16 >= C) break;  // uniform
-        f32x4 acc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // B fragment: candidate r = nt*16 + l%16, logical chunk 4*ks + l/16
-        // of its hi and lo rows, stored at that chunk ^ (r % CPR)
-        const int r = nt * 16 + (l % 16);
-        const unsigned char* row = st + r * 4 * D;
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const int off = ((4 * ks + l / 16) ^ (r % CPR)) << 4;
-          const bf16x8 bhv = as_bf16x8(*reinterpret_cast<const uint4*>(row + off));
-          const bf16x8 blv = as_bf16x8(*reinterpret_cast<const uint4*>(row + 2 * D + off));
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), bhv, acc[mt], 0, 0, 0);
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[mt][ks]), blv, acc[mt], 0, 0, 0);
-          }
-        }
-        // this wave's LogSumExp over its rows, per candidate (lane column l % 16)
-        float m, s;
-        if (full)
-          tile_lse<MT, true>(acc, rowvalid, sl2, m, s);
-        else
-          tile_lse<MT, false>(acc, rowvalid, sl2, m, s);
-        const int cn = c * kChunk + nt * 16 + l;
-        if (l < 16 && cn < C) part[w * cmax + cn] = f32x2{m, s};
-      }
+    score_exact<D, MT, NW>(lvl, cand, nullptr, C, qa, rowvalid, full, sl2, part, lay.cmax, st0,
+                           st1, w, l);
+    lds_barrier();
+    if (ranked) {
+      rank_level<NW>(g, level, C, Ku, lay, smem, tr_ids, w, l);
+      continue;
     }
-    __syncthreads();
-    for (int j = tid; j < C; j += NW * 64) {
-      float m = -INFINITY, s = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const f32x2 p = part[ww * cmax + j];
-        lse2_merge(m, s, p.x, p.y);
-      }
-      const float sc = (m + log2f(s)) * PYR_LN2;
-      score[j] = sc == sc ? sc : -INFINITY;  // a NaN score ranks last
-    }
-    __syncthreads();
+    for (int j = tid; j < C; j += NT) score[j] = merged_score<NW>(part, lay.cmax, j);
+    lds_barrier();
     for (int kk = Ku;;) {
-      top_k_and_trace<NW * 64>(g, C, level, cand, score, rank, kept, kscore, &s_nkept, kk, s_margin,
-                      tr_ids, tr_sc);
+      top_k_and_trace<NT>(g, C, level, cand, score, rank, kept, kscore, &s_nkept, kk, s_margin,
+                          tr_ids, tr_sc);
       if (!fallback_due(g, level, kk, Ku, s_margin)) break;
       kk = C < g.fb_k ? C : g.fb_k;  // keep more of the same candidates
     }
   }
-  write_route<NW * 64>(g, unit, kept, s_nkept, diag, sel);
+  write_route<NT>(g, unit, kept, s_nkept, diag, sel);
 }
 
-// NW waves of MT M tiles each.  Four M tiles fit 168 VGPRs, so three
-// four-wave workgroups share a CU (G = 4); G = 8 runs eight such waves.
+// NW waves of MT M tiles each, at most 128 VGPRs (four waves per SIMD):
+// four four-wave workgroups (G = 4) or two eight-wave ones (G = 8) share a
+// CU, so other units' scoring fills a unit's ranking and load latency.
 template <int D, int MT, int NW>
-__global__ __launch_bounds__(NW * 64, MT == 4 ? (NW == 4 ? 3 : 2) : 1) void select_mfma(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void select_mfma(
     const bf16_t* __restrict__ q, const float* __restrict__ pyr, int32_t* __restrict__ sel,
     int32_t* __restrict__ trace_ids, float* __restrict__ trace_scores, PyrGeom g) {
   constexpr int STAGE = kChunk * 4 * D;  // bytes per LDS stage

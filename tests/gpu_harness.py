@@ -55,7 +55,36 @@ def run_device(cfg: W.Config, q, k, v, trace=True, sel_in=None, fused=False):
         route = sel if sel_in is None else sel_in.to(torch.int32).to(q.device).contiguous()
         H.pyr_block_sparse_attn(p, q, k, v, route, o, lse, H.alloc_workspace(p))
     torch.cuda.synchronize()
+    if trace:
+        check_fast_selection(p, q, k, v, pyr, sel, tids, o if fused else None,
+                             lse if fused else None)
     return dict(pyr=pyr, sel=sel, tids=tids, tsc=tsc, o=o, lse=lse)
+
+
+def check_fast_selection(p, q, k, v, pyr, sel, tids, o=None, lse=None):
+    """Without a score trace the selection scores on the hi plane alone and
+    re-scores exactly only the candidates its error bound leaves undecided:
+    its route rows and trace ids must be those of the traced (every candidate
+    scored exactly) selection, bit for bit -- with the id trace and without
+    any trace.  With o and lse (a fused call) the fused launch without traces
+    must also give the same outputs."""
+    sel_f, sel_n = H.alloc_sel(p), H.alloc_sel(p)
+    tids_f = torch.full_like(tids, -7)
+    if o is None:
+        H.pyr_select_topk(p, q, pyr, sel_f, tids_f, None)
+        H.pyr_select_topk(p, q, pyr, sel_n)
+    else:
+        o_n, lse_n = torch.empty_like(o), torch.empty_like(lse)
+        H.pyr_select_attn(p, q, k, v, pyr, sel_f, torch.empty_like(o), None,
+                          H.alloc_workspace(p), tids_f, None)
+        H.pyr_select_attn(p, q, k, v, pyr, sel_n, o_n, lse_n, H.alloc_workspace(p))
+    torch.cuda.synchronize()
+    assert torch.equal(sel_f, sel), "route rows with the id trace only differ from the exact ones"
+    assert torch.equal(sel_n, sel), "route rows without traces differ from the exact ones"
+    assert torch.equal(tids_f, tids), "trace ids without the score trace differ"
+    if o is not None:
+        assert torch.equal(o_n.view(torch.int16), o.view(torch.int16))
+        assert torch.equal(lse_n, lse)
 
 
 def oracle_levels(k64, cfg, bh=None):

@@ -85,6 +85,14 @@ def test_budgets_and_fallback(name, dtype, d, Hq, Hk, b, K, budgets, fb_k):
     H.pyr_select_topk_budgets(p, q, pyr, sel, kh, fb_k, tau, tids, tsc)
     torch.cuda.synchronize()
     GH.log(f"case {name}: budgets {budgets}, fallback {fb_k} below margin {tau:.4f}")
+    if not fb_k:
+        # no fallback: without the score trace the bf16 pass with bounded
+        # re-scoring runs, and must keep the same nodes bit for bit
+        sel_f = H.alloc_sel(p)
+        tids_f = torch.full_like(tids, -7)
+        H.pyr_select_topk_budgets(p, q, pyr, sel_f, kh, 0, 0.0, tids_f, None)
+        torch.cuda.synchronize()
+        assert torch.equal(sel_f, sel) and torch.equal(tids_f, tids)
     sel_h, tids_h = sel.cpu().numpy(), tids.cpu().numpy()
     counts = {"exact": 0, "near_tie": 0, "fail": 0}
     fell = ambiguous = 0
