@@ -187,13 +187,10 @@ pyr_status pyr_build_pyramid(const pyr_problem* p, const void* k, float* pyramid
  *   trace_scores NULL or [B, Hk, nqb, L, K+1] float32: the scores of those
  *                kept nodes in the same order, then the best rejected score;
  *                NaN where a level was not scored or a slot is unused (output)
- * bfloat16 problems score on the matrix cores.  With trace_scores given,
- * every candidate is scored on both planes of the split (the exact scores).
- * Without it, candidates are scored once on the hi plane; a candidate whose
- * bf16-pass score, widened by its error bound (scale * max_r |q_r| * |hi| *
- * 2^-8 and an fp32 slack), lies clear of the K-th / (K+1)-th boundary is
- * kept or dropped on that score, and the rest are scored exactly.  The kept
- * sets, route rows and trace_ids are the same either way, bit for bit.
+ * Ranking does not depend on the traces: with or without trace_scores the
+ * kept sets, route rows and trace_ids are the same, bit for bit (without it,
+ * and without a fallback, the kernel ranks by counting on all its waves
+ * instead of recording scores and margins on one).
  */
 pyr_status pyr_select_topk(const pyr_problem* p, const void* q, const float* pyramid,
                            int32_t* sel, int32_t* trace_ids, float* trace_scores,
