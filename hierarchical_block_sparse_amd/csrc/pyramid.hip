@@ -10,15 +10,18 @@
 // selection's matrix-core scorer, so that the scorer can stream them into LDS
 // without converting.
 //
-// Two kernels:
+// Launches:
 //  * build_chunk: one workgroup per chunk of `chunk` = b^s consecutive 64-token
 //    blocks of one (batch, KV head).  It streams the chunk's keys from HBM once
 //    (16-byte loads, several blocks in flight per thread), reduces each block
-//    to its mean, then folds the chunk's nodes up s levels inside LDS.  This is
-//    the HBM-bound pass: every key byte is read exactly once.
-//  * build_level: one launch per remaining level (above level s), one thread
-//    per (node, column) of every slab, reading the children from the output
-//    slab (a few hundred KiB at most, in L2).
+//    to its mean -- the rows a wave holds are summed across its lanes with
+//    lane swaps, the waves' sums through LDS -- then folds the chunk's nodes
+//    up s levels inside LDS.  This is the HBM-bound pass: every key byte is
+//    read exactly once.
+//  * build_fold: the levels above s, t per launch (b^(t-1) <= 64): one
+//    workgroup per group of b^t nodes of the level below computes the first
+//    level from the children in the slab (in L2) and folds the rest in LDS.
+//    At 128K tokens (b = 4) one launch covers levels 3..6; at 1M, two.
 // A parent is the token-weighted mean of its children, so a ragged last block
 // or a ragged last node gives the exact token mean.
 #include "pyr_device.h"
@@ -46,6 +49,17 @@ __device__ __forceinline__ void put_node(const PyrGeom& g, float* slab, int64_t 
   }
 }
 
+// Sum of x over the lanes of a wave that share lane % TPR (the row groups of
+// one column slice): lane swaps for the 16- and 32-lane partners, a shuffle
+// below that.  Every lane of the group ends with the same sum.
+template <int TPR>
+__device__ __forceinline__ float rowgroup_sum(float x) {
+#pragma unroll
+  for (int o = TPR; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+  if (TPR <= 16) x = sum16(x);
+  return sum32(x);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
                                                         float* __restrict__ pyr, PyrGeom g,
@@ -55,12 +69,14 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
   constexpr int TPR = D / VEC;          // threads per key row
   constexpr int RPP = kThreads / TPR;   // rows per pass of the workgroup
   constexpr int PASSES = PYR_BLOCK / RPP;
+  constexpr int NWV = kThreads / 64;    // waves
   static_assert(PYR_BLOCK % RPP == 0, "rows per pass must divide the block");
+  static_assert(TPR >= 8 && TPR <= 32 && 64 % TPR == 0, "a row spans 8 to 32 lanes");
 
-  __shared__ float part[kBatch][RPP][D];
+  __shared__ __align__(16) float part[kBatch][NWV][D];  // per-wave row sums
   __shared__ float nodes[2][kChunkMax][D];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
   const int64_t bh = blockIdx.x / chunks_per_bh;
   const int c = blockIdx.x % chunks_per_bh;
   const PyrSeq sq = pyr_seq(g, (int)(bh / g.Hk));
@@ -73,8 +89,11 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
   const int col = (tid % TPR) * VEC;
   const int r0 = tid / TPR;
 
-  for (int jb = 0; jb < nblk; jb += kBatch) {
-    uint4 raw[kBatch][PASSES];
+  // The keys of batch jb+kBatch are loaded while batch jb's sums cross the
+  // waves through LDS: a batch's registers are free once reduced, and the
+  // LDS-only barriers do not wait for loads in flight.
+  uint4 raw[kBatch][PASSES];
+  auto load_batch = [&](int jb) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
 #pragma unroll
@@ -86,6 +105,9 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
           raw[u][p] = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  load_batch(0);
+  for (int jb = 0; jb < nblk; jb += kBatch) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       float acc[VEC];
@@ -99,22 +121,28 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
         for (int e = 0; e < VEC; ++e) acc[e] += x[e];
       }
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) part[u][r0][col + e] = acc[e];
+      for (int e = 0; e < VEC; ++e) acc[e] = rowgroup_sum<TPR>(acc[e]);
+      if (l < TPR) {
+        float4* dst = reinterpret_cast<float4*>(&part[u][w][col]);
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+      }
     }
-    __syncthreads();
+    if (jb + kBatch < nblk) load_batch(jb + kBatch);
+    lds_barrier();
     for (int idx = tid; idx < kBatch * D; idx += kThreads) {
       const int u = idx / D, dcol = idx % D;
       if (jb + u < nblk) {
         float s = 0.f;
 #pragma unroll
-        for (int r = 0; r < RPP; ++r) s += part[u][r][dcol];
+        for (int ww = 0; ww < NWV; ++ww) s += part[u][ww][dcol];
         const int64_t m = blk0 + jb + u;
         const float mean = s / (float)pyr_node_tokens(sq.Tk, g.branching, 0, m);
         nodes[0][jb + u][dcol] = mean;
         put_node<D>(g, slab, g.loff[0] + m, dcol, mean);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // Fold the chunk up s levels inside LDS (token-weighted means).
@@ -153,33 +181,113 @@ __device__ __forceinline__ int64_t level_valid(int64_t nb, int b, int lvl) {
   return nb;
 }
 
-// One level above the chunks: one thread per (node, column), nodes of every
-// slab spread over the whole grid (a level is one launch, the launches of
-// consecutive levels are ordered by the stream).
+constexpr int kFoldThreads = 512;
+constexpr int kFoldNodes = 64;  // nodes of the first folded level one workgroup holds in LDS
+
+// Levels lo+1 .. lo+t of one (batch, KV head), one workgroup per group of
+// b^t consecutive level-lo nodes (b^(t-1) <= kFoldNodes).  The first level
+// is computed from the children read from the slab (in L2: written by the
+// previous launch), with every thread's loads in flight together; the
+// remaining t-1 levels are folded in LDS.  Every level produced is written.
 template <int D>
-__global__ __launch_bounds__(kThreads) void build_level(float* __restrict__ pyr, PyrGeom g,
-                                                        int lvl, int wg_per_bh) {
-  const int64_t bh = blockIdx.x / wg_per_bh;
-  const int64_t idx = (int64_t)(blockIdx.x % wg_per_bh) * kThreads + threadIdx.x;
-  const PyrSeq sq = pyr_seq(g, (int)(bh / g.Hk));
+__global__ __launch_bounds__(kFoldThreads) void build_fold(float* __restrict__ pyr, PyrGeom g,
+                                                           int lo, int t, int groups_per_bh) {
+  __shared__ __align__(16) float nodes[2][kFoldNodes][D];
+  constexpr int C4 = D / 4;  // float4 column groups per node
   const int b = g.branching;
-  const int64_t n_below = level_valid(sq.nb, b, lvl - 1);
-  const int64_t n_here = sq.nb ? level_valid(sq.nb, b, lvl) : 0;
-  const int64_t m = idx / D;
-  if (m >= n_here) return;
-  const int dcol = (int)(idx % D);
+  int gn1 = 1;  // first-level nodes per group: b^(t-1)
+  for (int i = 1; i < t; ++i) gn1 *= b;
+  const int64_t bh = blockIdx.x / groups_per_bh;
+  const int grp = blockIdx.x % groups_per_bh;
+  const PyrSeq sq = pyr_seq(g, (int)(bh / g.Hk));
+  if (sq.nb == 0) return;
+  const int64_t n_lo = level_valid(sq.nb, b, lo);
+  const int64_t n_hi = level_valid(sq.nb, b, lo + 1);
+  const int64_t first1 = (int64_t)grp * gn1;  // first level-(lo+1) node of the group
+  if (first1 >= n_hi) return;
+  const int cnt1 = (int)min<int64_t>(gn1, n_hi - first1);
   float* slab = pyr + bh * g.planes * g.n_tot * D;
-  const float* below = slab + g.loff[lvl - 1] * D;
-  float num = 0.f, den = 0.f;
-  for (int j = 0; j < b; ++j) {
-    const int64_t cidx = m * b + j;
-    if (cidx < n_below) {
-      const float w = (float)pyr_node_tokens(sq.Tk, b, lvl - 1, cidx);
-      num += below[cidx * D + dcol] * w;
-      den += w;
+  const float* below = slab + g.loff[lo] * D;
+
+  // level lo+1: one float4 column group of one node per work item; a
+  // thread's PER items read their children four at a time, loads first
+  constexpr int PER = kFoldNodes * C4 / kFoldThreads;
+  static_assert(kFoldNodes * C4 % kFoldThreads == 0, "items must split evenly");
+  float4 num[PER];
+  float den[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    num[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    den[u] = 0.f;
+  }
+  for (int j0 = 0; j0 < b; j0 += 4) {
+    float4 x[PER][4];
+    float wv[PER][4];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = u * kFoldThreads + threadIdx.x;
+      const int64_t node = first1 + idx / C4;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t cidx = node * b + j0 + jj;
+        const bool ok = idx < cnt1 * C4 && j0 + jj < b && cidx < n_lo;
+        x[u][jj] = ok ? *reinterpret_cast<const float4*>(below + cidx * D + 4 * (idx % C4))
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        wv[u][jj] = ok ? (float)pyr_node_tokens(sq.Tk, b, lo, cidx) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        num[u].x += x[u][jj].x * wv[u][jj];
+        num[u].y += x[u][jj].y * wv[u][jj];
+        num[u].z += x[u][jj].z * wv[u][jj];
+        num[u].w += x[u][jj].w * wv[u][jj];
+        den[u] += wv[u][jj];
+      }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = u * kFoldThreads + threadIdx.x;
+    if (idx < cnt1 * C4) {
+      const int m = idx / C4, c4 = idx % C4;
+      const float mean[4] = {num[u].x / den[u], num[u].y / den[u], num[u].z / den[u],
+                             num[u].w / den[u]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        nodes[0][m][4 * c4 + e] = mean[e];
+        put_node<D>(g, slab, g.loff[lo + 1] + first1 + m, 4 * c4 + e, mean[e]);
+      }
     }
   }
-  put_node<D>(g, slab, g.loff[lvl] + m, dcol, num / den);
+  __syncthreads();
+  // levels lo+2 .. lo+t in LDS
+  int cur = 0, n_below = cnt1;
+  int64_t first_below = first1;
+  for (int lvl = lo + 2; lvl <= lo + t; ++lvl) {
+    const int n_here = (n_below + b - 1) / b;
+    const int64_t first_here = first_below / b;
+    for (int idx = threadIdx.x; idx < n_here * D; idx += kFoldThreads) {
+      const int m = idx / D, dcol = idx % D;
+      float num = 0.f, den = 0.f;
+      for (int j = 0; j < b; ++j) {
+        const int cidx = m * b + j;
+        if (cidx < n_below) {
+          const float w = (float)pyr_node_tokens(sq.Tk, b, lvl - 1, first_below + cidx);
+          num += nodes[cur][cidx][dcol] * w;
+          den += w;
+        }
+      }
+      const float mean = num / den;
+      nodes[cur ^ 1][m][dcol] = mean;
+      put_node<D>(g, slab, g.loff[lvl] + first_here + m, dcol, mean);
+    }
+    __syncthreads();
+    cur ^= 1;
+    n_below = n_here;
+    first_below = first_here;
+  }
 }
 
 __device__ __forceinline__ float key_f32(float x) { return x; }
@@ -269,12 +377,18 @@ hipError_t launch_build_t(const PyrGeom& g, const void* k, float* pyr, hipStream
                      dim3(kThreads), 0, st, static_cast<const T*>(k), pyr, g, chunk, s,
                      chunks_per_bh);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  for (int lvl = s + 1; lvl < g.L && e == hipSuccess; ++lvl) {
-    const int64_t wg = ((int64_t)g.lsize[lvl] * D + kThreads - 1) / kThreads;  // longest sequence
-    hipLaunchKernelGGL((build_level<D>), dim3((unsigned)(n_bh * wg)), dim3(kThreads), 0, st, pyr,
-                       g, lvl, (int)wg);
+  // the levels above s, as many per launch as one workgroup's LDS allows
+  for (int lo = s; lo + 1 < g.L && e == hipSuccess;) {
+    int t = 1, gn1 = 1;
+    while (lo + t + 1 < g.L && (int64_t)gn1 * g.branching <= kFoldNodes) {
+      gn1 *= g.branching;
+      ++t;
+    }
+    const int64_t groups = ((int64_t)g.lsize[lo + 1] + gn1 - 1) / gn1;  // longest sequence
+    hipLaunchKernelGGL((build_fold<D>), dim3((unsigned)(n_bh * groups)), dim3(kFoldThreads), 0, st,
+                       pyr, g, lo, t, (int)groups);
     e = hipGetLastError();
+    lo += t;
   }
   return e;
 }

@@ -314,26 +314,6 @@ __device__ __forceinline__ void issue_chunk(const unsigned char* split, const in
   }
 }
 
-// Combine a value with that of the lane's partner in the other 16-lane row
-// (xor 16) or the other 32-lane half (xor 32).  A swap hands each lane the
-// pair (even, odd) of the two lanes, so a symmetric combine needs no select.
-__device__ __forceinline__ float max16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // LogSumExp (log2 domain: max m and sum s of 2^(x - m)) of one wave's rows for
 // the 16 candidates of an N tile; lane l ends with the value of candidate
 // l % 16.  Row j of M tile mt in the C layout is row 4*(l/16) + j, so a
