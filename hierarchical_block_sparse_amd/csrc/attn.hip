@@ -656,26 +656,9 @@ __device__ __forceinline__ void pp_unit(const bf16_t* __restrict__ q, const bf16
   const int64_t row0 = (int64_t)i * PYR_BLOCK + (w % 2) * 32;
   const float sl2 = g.scale * PYR_LOG2E;
 
-  // route order: valid blocks before the unit's own block first (no mask
-  // needed), then the rest (the diagonal block)
-  // (entries outside [0, nb) and repeats of an earlier entry are skipped)
-  if (w == 0) {
-    const int nun = route_compact_wave(s_sel, g.K + 1, sq.nb, s_ord, 0,
-                                       [i](int j) { return j < i; });
-    const int n = route_compact_wave(s_sel, g.K + 1, sq.nb, s_ord, nun,
-                                     [i](int j) { return j >= i; });
-    if (l == 0) {
-      s_cnt[0] = n;
-      s_cnt[1] = nun;
-    }
-  }
-  __syncthreads();
-  const int nsel = s_cnt[0], nun = s_cnt[1];
-  const bf16_t* kh = k + (sq.k0 + hk * sq.khs) * D;
-  const bf16_t* vh = v + (sq.k0 + hk * sq.khs) * D;
-
   // Q^T fragments (B operand): lane holds query row lr and d = ks*16 + 8*half .. +7.
   // Rows past the end of a ragged last block load the last row; they are never stored.
+  // Issued first, so that they are in flight while the route is ordered.
   const bf16_t* qh = q + (sq.q0 + h * sq.qhs) * D;
   uint4 qb[D / 16];
   {
@@ -683,6 +666,25 @@ __device__ __forceinline__ void pp_unit(const bf16_t* __restrict__ q, const bf16
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qb[ks] = ld16(qh + tok * D + ks * 16 + 8 * half);
   }
+
+  // route order: valid blocks before the unit's own block first (no mask
+  // needed), then the rest (the diagonal block)
+  // (entries outside [0, nb) and repeats of an earlier entry are skipped)
+  if (w == 0) {
+    const uint32_t used = route_used_mask(s_sel, g.K + 1, sq.nb);
+    const int nun = route_compact_used(s_sel, g.K + 1, used, s_ord, 0,
+                                       [i](int j) { return j < i; });
+    const int n = route_compact_used(s_sel, g.K + 1, used, s_ord, nun,
+                                     [i](int j) { return j >= i; });
+    if (l == 0) {
+      s_cnt[0] = n;
+      s_cnt[1] = nun;
+    }
+  }
+  lds_barrier();  // the order is in LDS; the Q loads stay in flight
+  const int nsel = s_cnt[0], nun = s_cnt[1];
+  const bf16_t* kh = k + (sq.k0 + hk * sq.khs) * D;
+  const bf16_t* vh = v + (sq.k0 + hk * sq.khs) * D;
 
   const FragOffsets<D> fo(l);
   f32x16 oacc[D / 32];

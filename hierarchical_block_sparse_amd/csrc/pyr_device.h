@@ -141,21 +141,57 @@ __device__ __forceinline__ bool route_entry_used(const int* row, int jj, int j, 
   return first;
 }
 
+// Whole-wave form of route_entry_used for the entries c*64 + lane of a row
+// raw[0..cnt) (in LDS, visible to the wave): bit c of the result is set when
+// entry c*64 + lane is used.  Each lane holds its entry in a register and
+// compares it with every earlier entry taken with readlane (one uniform lane
+// index per step), so the check costs a few vector instructions per entry
+// instead of an LDS read per earlier entry.  At most 32 chunks (cnt <= 2048).
+__device__ __forceinline__ uint32_t route_used_mask(const int* raw, int cnt, int nb) {
+  const int l = threadIdx.x % 64;
+  uint32_t used = 0;
+  for (int c = 0; c * 64 < cnt; ++c) {
+    const int jj = c * 64 + l;
+    const int j = jj < cnt ? raw[jj] : -1;
+    bool first = j >= 0 && j < nb;
+    // every entry of the earlier chunks
+    // (no short-circuit: every lane takes part in every readlane)
+    for (int b = 0; b < c; ++b) {
+      const int e = raw[b * 64 + l];
+      for (int x = 0; x < 64; ++x) first = first & (__builtin_amdgcn_readlane(e, x) != j);
+    }
+    // the entries of this chunk before the lane's
+    const int nx = cnt - c * 64 < 64 ? cnt - c * 64 : 64;
+    for (int x = 0; x < nx; ++x) first = first & !((x < l) & (__builtin_amdgcn_readlane(j, x) == j));
+    if (first) used |= 1u << c;
+  }
+  return used;
+}
+
+// One whole wave appends to out[n0..) the entries of the route row raw[0..cnt)
+// marked in `used` (route_used_mask) that also satisfy keep(j), in row order;
+// returns the new count, uniform across the wave.
+template <typename Keep>
+__device__ __forceinline__ int route_compact_used(const int* raw, int cnt, uint32_t used, int* out,
+                                                  int n0, Keep keep) {
+  const int l = threadIdx.x % 64;
+  int n = n0;
+  for (int c = 0; c * 64 < cnt; ++c) {
+    const int jj = c * 64 + l;
+    const int j = jj < cnt ? raw[jj] : -1;
+    const bool ok = (used >> c & 1u) && keep(j);
+    const unsigned long long m = __ballot(ok);
+    if (ok) out[n + __popcll(m & ((1ull << l) - 1ull))] = j;
+    n += __popcll(m);
+  }
+  return n;
+}
+
 // One whole wave appends to out[n0..) the used entries of the route row
 // raw[0..cnt) (both in LDS, raw visible to the wave) that also satisfy
 // keep(j), in row order; returns the new count, uniform across the wave.
 template <typename Keep>
 __device__ __forceinline__ int route_compact_wave(const int* raw, int cnt, int nb, int* out,
                                                   int n0, Keep keep) {
-  const int l = threadIdx.x % 64;
-  int n = n0;
-  for (int base = 0; base < cnt; base += 64) {
-    const int jj = base + l;
-    const int j = jj < cnt ? raw[jj] : -1;
-    const bool ok = jj < cnt && route_entry_used(raw, jj, j, nb) && keep(j);
-    const unsigned long long m = __ballot(ok);
-    if (ok) out[n + __popcll(m & ((1ull << l) - 1ull))] = j;
-    n += __popcll(m);
-  }
-  return n;
+  return route_compact_used(raw, cnt, route_used_mask(raw, cnt, nb), out, n0, keep);
 }
