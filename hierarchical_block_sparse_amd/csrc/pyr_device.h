@@ -143,27 +143,36 @@ __device__ __forceinline__ bool route_entry_used(const int* row, int jj, int j, 
 
 // Whole-wave form of route_entry_used for the entries c*64 + lane of a row
 // raw[0..cnt) (in LDS, visible to the wave): bit c of the result is set when
-// entry c*64 + lane is used.  Each lane holds its entry in a register and
-// compares it with every earlier entry taken with readlane (one uniform lane
-// index per step), so the check costs a few vector instructions per entry
-// instead of an LDS read per earlier entry.  At most 32 chunks (cnt <= 2048).
+// entry c*64 + lane is used.  Each lane holds its entry in a register; for
+// every earlier entry x, taken with readlane (one uniform lane index per
+// step), the compare j == x is itself the 64-lane mask of the lanes holding
+// the same block, so a step is one readlane, one compare and a few scalar
+// mask operations, with no per-lane branch.  At most 32 chunks (cnt <= 2048).
 __device__ __forceinline__ uint32_t route_used_mask(const int* raw, int cnt, int nb) {
   const int l = threadIdx.x % 64;
   uint32_t used = 0;
   for (int c = 0; c * 64 < cnt; ++c) {
     const int jj = c * 64 + l;
     const int j = jj < cnt ? raw[jj] : -1;
-    bool first = j >= 0 && j < nb;
-    // every entry of the earlier chunks
-    // (no short-circuit: every lane takes part in every readlane)
+    unsigned long long dup = 0;  // bit l: an earlier entry holds lane l's block
+    // every entry of the earlier chunks (all earlier than this chunk's)
     for (int b = 0; b < c; ++b) {
       const int e = raw[b * 64 + l];
-      for (int x = 0; x < 64; ++x) first = first & (__builtin_amdgcn_readlane(e, x) != j);
+#pragma unroll 8
+      for (int x = 0; x < 64; ++x) dup |= __ballot(j == __builtin_amdgcn_readlane(e, x));
     }
-    // the entries of this chunk before the lane's
+    // the entries of this chunk before the lane's: lanes above x
     const int nx = cnt - c * 64 < 64 ? cnt - c * 64 : 64;
-    for (int x = 0; x < nx; ++x) first = first & !((x < l) & (__builtin_amdgcn_readlane(j, x) == j));
-    if (first) used |= 1u << c;
+    const int nx8 = (nx + 7) & ~7;  // lanes past cnt hold -1, which no block equals
+    for (int x0 = 0; x0 < nx8; x0 += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int x = x0 + u;
+        const unsigned long long above = x == 63 ? 0ull : ~((2ull << x) - 1ull);
+        dup |= __ballot(j == __builtin_amdgcn_readlane(j, x)) & above;
+      }
+    }
+    if (j >= 0 && j < nb && !((dup >> l) & 1ull)) used |= 1u << c;
   }
   return used;
 }
