@@ -73,7 +73,9 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
   static_assert(PYR_BLOCK % RPP == 0, "rows per pass must divide the block");
   static_assert(TPR >= 8 && TPR <= 32 && 64 % TPR == 0, "a row spans 8 to 32 lanes");
 
-  __shared__ __align__(16) float part[kBatch][NWV][D];  // per-wave row sums
+  // per-wave row sums; rows padded by 4 floats so that the 4 waves' sums of a
+  // column sit in 4 different banks when one lane reads them
+  __shared__ __align__(16) float part[kBatch][NWV][D + 4];
   __shared__ float nodes[2][kChunkMax][D];
 
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
@@ -123,9 +125,19 @@ __global__ __launch_bounds__(kThreads) void build_chunk(const T* __restrict__ k,
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc[e] = rowgroup_sum<TPR>(acc[e]);
       if (l < TPR) {
+        // with two 16-byte halves per lane (VEC = 8), lane l stores half
+        // ((l >> 2) ^ (l >> 3)) & 1 first: each store's 16-byte chunks
+        // 2l + h are then distinct modulo 8 within lanes 0-7 and 8-15, and
+        // modulo 16 over lanes 0-15 (no bank conflict at 128 or 256 bytes
+        // per LDS cycle)
         float4* dst = reinterpret_cast<float4*>(&part[u][w][col]);
+        constexpr int NH = VEC / 4;
+        const int flip = NH == 2 ? ((l >> 2) ^ (l >> 3)) & 1 : 0;
 #pragma unroll
-        for (int e = 0; e < VEC; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+        for (int hh = 0; hh < NH; ++hh) {
+          const int h = hh ^ flip;
+          dst[h] = make_float4(acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]);
+        }
       }
     }
     if (jb + kBatch < nblk) load_batch(jb + kBatch);
@@ -254,11 +266,9 @@ __global__ __launch_bounds__(kFoldThreads) void build_fold(float* __restrict__ p
       const int m = idx / C4, c4 = idx % C4;
       const float mean[4] = {num[u].x / den[u], num[u].y / den[u], num[u].z / den[u],
                              num[u].w / den[u]};
+      *reinterpret_cast<float4*>(&nodes[0][m][4 * c4]) = make_float4(mean[0], mean[1], mean[2], mean[3]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        nodes[0][m][4 * c4 + e] = mean[e];
-        put_node<D>(g, slab, g.loff[lo + 1] + first1 + m, 4 * c4 + e, mean[e]);
-      }
+      for (int e = 0; e < 4; ++e) put_node<D>(g, slab, g.loff[lo + 1] + first1 + m, 4 * c4 + e, mean[e]);
     }
   }
   __syncthreads();
