@@ -36,7 +36,28 @@ CASES = [
     # so a row spans several splits and a repeat can sit in a later split
     C("rep_decode_bf16", 3, 8, 2, 1, 64 * 40 + 5, 128, BF, 4, 12, 0, seed=55),
     C("rep_decode_fp32", 2, 4, 2, 1, 64 * 30, 64, F32, 2, 10, 0, seed=56),
+    # K + 1 = 71 entries: rows span two 64-entry chunks of the route-set check
+    # and some repeats sit in the second chunk, their first occurrence in the first
+    C("rep_g4_k70", 1, 8, 2, 64 * 80 + 9, 64 * 80 + 9, 128, BF, 4, 70, 0, seed=60),
 ]
+
+
+def _cross_chunk_repeats(route):
+    """Rows in which an entry at position >= 64 repeats a block first listed
+    before position 64."""
+    r = route.numpy()
+    n = 0
+    for idx in np.ndindex(r.shape[:-1]):
+        row = [int(x) for x in r[idx]]
+        first = {}
+        for pos, j in enumerate(row):
+            if j < 0:
+                continue
+            if j in first and first[j] < 64 <= pos:
+                n += 1
+                break
+            first.setdefault(j, pos)
+    return n
 
 
 def _dedup(route):
@@ -59,6 +80,8 @@ def test_repeated_route_entries(cfg):
     reps = sum(len([x for x in r[idx] if x >= 0]) > len(set(int(x) for x in r[idx] if x >= 0))
                for idx in np.ndindex(r.shape[:-1]))
     assert reps > 0, "the generator planted no repeat"
+    if cfg.top_k + 1 > 64:
+        assert _cross_chunk_repeats(route) > 0, "no repeat crosses the 64-entry chunk boundary"
     q, k, v = W.make_inputs(cfg, "cuda")
     dev = GH.run_device(cfg, q, k, v, trace=False, sel_in=route)
     dev2 = GH.run_device(cfg, q, k, v, trace=False, sel_in=_dedup(route))
@@ -76,10 +99,13 @@ def test_repeated_route_entries(cfg):
     assert e_o <= tol_o and e_l <= tol_l
 
 
-def test_backward_repeated_route_entries():
-    cfg = C("rep_bwd_g4", 1, 8, 2, 64 * 14 + 9, 64 * 14 + 9, 128, BF, 4, 7, 0, seed=57)
+@pytest.mark.parametrize("K,T", [(7, 64 * 14 + 9), (70, 64 * 76 + 9)], ids=["k7", "k70"])
+def test_backward_repeated_route_entries(K, T):
+    cfg = C(f"rep_bwd_g4_k{K}", 1, 8, 2, T, T, 128, BF, 4, K, 0, seed=57)
     GH.log(f"case {cfg.name}: backward over route rows with repeats")
     route = W.make_route(cfg, with_invalid=True, repeats=True)
+    if K + 1 > 64:
+        assert _cross_chunk_repeats(route) > 0, "no repeat crosses the 64-entry chunk boundary"
     q, k, v = W.make_inputs(cfg, "cuda")
     dout = W.make_grad_out(cfg, "cuda")
     dev = GH.run_device(cfg, q, k, v, trace=False, sel_in=route)
