@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "select+sparse-attn tokens/s at T=128K; TFLOP/s & HBM GB/s as % of peak"
 METRIC_BWD = "training pass (select+sparse-attn forward + attention backward) tokens/s"
@@ -233,7 +234,7 @@ def attn_kernel_name(cfg):
     if cfg.decode:
         return "attn_decode_mfma+combine" if cfg.dtype.itemsize == 2 else "attn_decode_split+combine"
     if cfg.dtype.itemsize != 2:
-        return "attn_prefill_valu"
+        return "attn_prefill_f32"
     return "attn_prefill_pp" if cfg.group % 4 == 0 else "attn_prefill_mfma"
 
 
@@ -418,6 +419,8 @@ def main():
     # gather bandwidth where it feeds few (one head per KV head: 59 flop/B) and
     # for decode (one query row per head)
     hbm_bound = cfg.decode or a_flops / a_bytes < 100
+    # the attention's matrix-core peak for its input type (bf16 or fp32 MFMA)
+    peak_mfma = PEAK_BF16_TFLOPS if cfg.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
     traffic = kernel_traffic(cfg.name + ("_packed" if lengths else ""))
     line = {
         "metric": METRIC,
@@ -443,9 +446,9 @@ def main():
             "kernel": attn_kernel_name(cfg),
             "bound": "mfma" if not hbm_bound else "hbm",
             "achieved": round(achieved, 2) if not hbm_bound else round(a_bytes / t_attn / 1e9, 1),
-            "peak": PEAK_BF16_TFLOPS if not hbm_bound else PEAK_HBM_GBS,
+            "peak": peak_mfma if not hbm_bound else PEAK_HBM_GBS,
             "unit": "TFLOP/s" if not hbm_bound else "GB/s",
-            "frac": round((achieved / PEAK_BF16_TFLOPS) if not hbm_bound
+            "frac": round((achieved / peak_mfma) if not hbm_bound
                           else (a_bytes / t_attn / 1e9 / PEAK_HBM_GBS), 4),
             "traffic": traffic,
             "algorithmic_flops_per_launch": a_flops,
@@ -458,7 +461,7 @@ def main():
             "select": {"ms": round(stage_ms[1], 4), "GB/s": round(s_bytes / t_sel / 1e9, 1),
                        "TFLOP/s_fp32_equiv": round(s_flops / t_sel / 1e12, 2)},
             "attn": {"ms": round(stage_ms[2], 4), "TFLOP/s": round(achieved, 2),
-                     "mfma_frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "mfma_frac": round(achieved / peak_mfma, 4),
                      "GB/s_gathered": round(a_bytes / t_attn / 1e9, 1)},
             "build_plus_select_hbm_frac": (round((b_bytes + s_bytes) / (t_build + t_sel) / 1e9 / PEAK_HBM_GBS, 4)
                                            if not cfg.decode else None),

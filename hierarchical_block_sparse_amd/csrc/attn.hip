@@ -20,8 +20,8 @@
 //    take turns: while one wave of a SIMD runs the matrix work of a block (its
 //    LDS fragment reads and MFMAs), the other runs the vector work (row max,
 //    exponentials, bf16 packing), then they swap.
-//  * attn_prefill_valu: fp32 (or any dtype) reference-precision path, one
-//    thread per query row, fp32 dot products.
+//  * attn_prefill_f32 (fp32): the layout of attn_prefill_mfma with fp32 tiles
+//    on v_mfma_f32_32x32x2_f32, fp32 products and accumulation.
 //  * attn_decode_mfma (bf16) / attn_decode_split (fp32) + attn_decode_combine:
 //    decode (one query token per sequence).  The selected blocks of a unit are
 //    split across workgroups so the HBM-bound KV stream fills the chip; partial
@@ -821,106 +821,258 @@ __global__ __launch_bounds__(512, 2) void select_attend(
 }
 
 // ---------------------------------------------------------------------------
-// fp32 (any dtype) prefill on the vector ALUs: one thread per query row.
+// fp32 prefill, MFMA (v_mfma_f32_32x32x2_f32)
+//
+// The layout of the bf16 kernels with fp32 tiles and fp32 products: S^T = K Q^T
+// with keys on the M side and the lane's query row on N, and O^T += V^T P^T.
+// One MFMA step covers two head dims (S^T) or two keys (O^T), one per lane
+// half.  Step ks of S^T takes dim 8(ks/4) + 4*half + ks%4 in lane half `half`,
+// so a lane reads the K values of four consecutive steps as one 16-byte chunk
+// and holds the matching Q values in registers.  Step ks of O^T over a 32-key
+// tile takes key 8(ks/4) + 4*half + ks%4 of the tile: exactly the key whose
+// score element ks of the lane's S^T accumulator holds, so P^T feeds the MFMA
+// as its B operand straight from registers, with no exchange between lanes.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_prefill_valu(const T* __restrict__ q,
-                                                        const T* __restrict__ k,
-                                                        const T* __restrict__ v,
-                                                        const int32_t* __restrict__ sel,
-                                                        T* __restrict__ o, float* __restrict__ lse,
-                                                        PyrGeom g) {
-  constexpr int VEC = 16 / sizeof(T);
-  __shared__ float Kt[64][D];
-  __shared__ float Vt[64][D];
+template <int D>
+struct TileGeomF32 {
+  static constexpr int CPR = D / 4;      // 16-byte chunks per row
+  static constexpr int ROW = 4 * D;      // bytes per row (a multiple of 256)
+  static constexpr int TILE = 64 * ROW;  // bytes per K or V tile
+  // K: the 16 lanes that read one chunk index from 16 consecutive rows find it
+  // at 16 different positions (mod 16) of the row, i.e. in 16 distinct 4-bank groups
+  __device__ static int swz_k(int r) { return r % 16; }
+  // V: a lane half reads 32 consecutive floats of one key row (8 chunks) and
+  // the other half those of a key 4 rows on; flipping chunk bit 3 every 4 rows
+  // puts the two halves on different banks
+  __device__ static int swz_v(int r) { return 8 * ((r / 4) % 2); }
+};
+
+// Issue the K and V tiles of block j: instruction t of a tile fills LDS chunks
+// [64t, 64t+64); chunk p holds row p / CPR, logical chunk (p % CPR) ^ swz(row).
+// Rows past the sequence end re-read its last row (the causal mask gives them
+// zero weight).
+template <int D, int NW>
+__device__ __forceinline__ void issue_tiles_f32(const float* kh, const float* vh, int64_t Tk, int j,
+                                                unsigned char* ktile, unsigned char* vtile, int w,
+                                                int l) {
+  using TG = TileGeomF32<D>;
+  const int64_t key0 = (int64_t)j * PYR_BLOCK;
+#pragma unroll
+  for (int tt = 0; tt < TG::CPR / NW; ++tt) {
+    const int t = tt * NW + w;
+    const int p = t * 64 + l, row = p / TG::CPR, sc = p % TG::CPR;
+    const int64_t kp = min<int64_t>(key0 + row, Tk - 1);
+    const float* ka = kh + kp * D + (sc ^ TG::swz_k(row)) * 4;
+    const float* va = vh + kp * D + (sc ^ TG::swz_v(row)) * 4;
+    __builtin_amdgcn_global_load_lds((const void*)ka, (lds_void*)(ktile + t * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)va, (lds_void*)(vtile + t * 1024), 16, 0, 0);
+  }
+}
+
+// Per-wave state of the fp32 kernel: 32 query rows of one head.
+template <int D>
+struct F32Wave {
+  float4 qf[D / 8];     // Q: row lr, dims 8c + 4*half .. +3
+  f32x16 oacc[D / 32];  // O^T: dim dt*32 + (e/4)*8 + half*4 + e%4, row lr
+  float m_run, l_run;   // running max (log2 domain) and the lane half's sum
+  int64_t row0;         // first query position of the wave
+  int kfrag[2];         // byte offset of the lane's K row in a tile, per 32-key tile
+  int kswz;             // its swizzle (the same for both 32-key tiles)
+  int voff[D / 32];     // byte offset of the lane's V value, key 4*half, per dim tile
+};
+
+// One selected block (key block j, tiles in rd): loads of the next selected
+// block (jn >= 0) go to wr first.  rd and wr are distinct __shared__ arrays,
+// so the compiler does not wait for those loads before reading rd.
+template <int D, int NW>
+__device__ __forceinline__ void f32_block(F32Wave<D>& s_, const unsigned char* rd, int j,
+                                          unsigned char* wr, int jn, const float* kh,
+                                          const float* vh, int64_t Tk, float sl2, int w, int l) {
+  using TG = TileGeomF32<D>;
+  const int half = l / 32, lr = l % 32;
+  if (jn >= 0) issue_tiles_f32<D, NW>(kh, vh, Tk, jn, wr, wr + TG::TILE, w, l);
+  const unsigned char* Kt = rd;
+  const unsigned char* Vt = rd + TG::TILE;
+  const int64_t key0 = (int64_t)j * PYR_BLOCK;
+  f32x16 s[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
+#pragma unroll
+    for (int c4 = 0; c4 < D / 32; ++c4) {
+      float4 a[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        a[c] = *reinterpret_cast<const float4*>(Kt + s_.kfrag[kt] +
+                                                (((2 * (4 * c4 + c) + half) ^ s_.kswz) << 4));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 qv = s_.qf[4 * c4 + c];
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[c].x, qv.x, s[kt], 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[c].y, qv.y, s[kt], 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[c].z, qv.z, s[kt], 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[c].w, qv.w, s[kt], 0, 0, 0);
+      }
+      // keep the compiler from hoisting all reads of the block (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // element e of tile kt is key kt*32 + (e/4)*8 + half*4 + e%4 of the block
+  if (key0 + PYR_BLOCK - 1 > s_.row0) {  // the diagonal block (or a later one)
+    const int rel = (int)(s_.row0 - key0) + lr;  // the lane row's position in the block
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (kt * 32 + (e / 4) * 8 + half * 4 + (e % 4) > rel) s[kt][e] = -INFINITY;
+  }
+  float mraw = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mraw = fmaxf(mraw, fmaxf(s[0][e], s[1][e]));
+  mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+  const float mx = mraw * sl2;
+  const bool need = mx > s_.m_run + kRescaleLog2;
+  if (__any(need)) {
+    const float m_new = need ? mx : s_.m_run;
+    const float alpha = m_new == s_.m_run ? 1.f : __builtin_amdgcn_exp2f(s_.m_run - m_new);
+    s_.l_run *= alpha;
+    s_.m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s_.oacc[dt][e] *= alpha;
+  }
+  // a row that has seen no visible key yet keeps m_run = -inf: all its p are 0
+  const float mneg = s_.m_run == -INFINITY ? 0.f : -s_.m_run;
+  float psum = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][e], sl2, mneg));
+      s[kt][e] = p;
+      psum += p;
+    }
+  s_.l_run += psum;
+  // O^T += V^T P^T: step ks of tile kt takes key kt*32 + 8(ks/4) + 4*half + ks%4
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      float a[4][D / 32];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          a[c][dt] = *reinterpret_cast<const float*>(Vt + (kt * 32 + 8 * k4 + c) * TG::ROW +
+                                                     s_.voff[dt]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          s_.oacc[dt] =
+              __builtin_amdgcn_mfma_f32_32x32x2f32(a[c][dt], s[kt][4 * k4 + c], s_.oacc[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_prefill_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const int32_t* __restrict__ sel, float* __restrict__ o, float* __restrict__ lse, PyrGeom g,
+    int wg_per_unit) {
+  using TG = TileGeomF32<D>;
+  constexpr int NT = NW * 64;
+  // two stages [K tile, V tile], separate arrays used in a fixed rotation
+  __shared__ __align__(16) unsigned char st0[2 * TG::TILE];
+  __shared__ __align__(16) unsigned char st1[2 * TG::TILE];
   __shared__ int s_sel[kMaxSel];
-  const int t = threadIdx.x;
-  const int hsub = (int)(blockIdx.x % g.G);
+  __shared__ int s_n;
+  // the raw route row, in the second stage (free until the second block's loads)
+  static_assert(kMaxSel * 4 <= TG::TILE, "route row fits a tile");
+  int* s_raw = reinterpret_cast<int*>(st1);
+
+  const int tid = threadIdx.x, w = tid / 64, l = tid % 64;
+  const int half = l / 32, lr = l % 32;
+  const int sub = (int)(blockIdx.x % wg_per_unit);
   int bi, hk, i;
   int64_t unit;
-  unit_of(g, blockIdx.x / g.G, bi, hk, i, unit);
+  unit_of(g, blockIdx.x / wg_per_unit, bi, hk, i, unit);
   const PyrSeq sq = pyr_seq(g, bi);
   if (i >= sq.nqb) return;  // past the end of a shorter packed sequence
-  const int h = hk * g.G + hsub;
+  const int h = hk * g.G + sub * (NW / 2) + w / 2;  // two waves of 32 rows per head
   const float sl2 = g.scale * PYR_LOG2E;
-  const int64_t rp = (int64_t)i * PYR_BLOCK + t;
-  const bool valid = rp < sq.Tq;
-  for (int jj = t; jj <= g.K; jj += 64) s_sel[jj] = sel[unit * (g.K + 1) + jj];
-  float qr[D], acc[D];
-  const T* qrow = q + (sq.q0 + h * sq.qhs + (valid ? rp : 0)) * D;
-  for (int d0 = 0; d0 < D; d0 += VEC) {
-    float x[VEC];
-    unpack16<T>(ld16(qrow + d0), x);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) qr[d0 + e] = x[e] * sl2;
+  const float* kh = k + (sq.k0 + hk * sq.khs) * D;
+  const float* vh = v + (sq.k0 + hk * sq.khs) * D;
+
+  for (int jj = tid; jj <= g.K; jj += NT) s_raw[jj] = sel[unit * (g.K + 1) + jj];
+  __syncthreads();  // s_raw visible
+  if (w == 0) {     // compact the route row: entries outside [0, nb) and repeats are skipped
+    const int n = route_compact_wave(s_raw, g.K + 1, sq.nb, s_sel, 0, [](int) { return true; });
+    if (l == 0) s_n = n;
   }
-#pragma unroll
-  for (int d = 0; d < D; ++d) acc[d] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
-  const T* kh = k + (sq.k0 + hk * sq.khs) * D;
-  const T* vh = v + (sq.k0 + hk * sq.khs) * D;
   __syncthreads();
-  for (int jj = 0; jj <= g.K; ++jj) {
-    const int j = s_sel[jj];
-    // outside [0, nb) or a repeat of an earlier entry: uniform across the workgroup
-    if (!route_entry_used(s_sel, jj, j, sq.nb)) continue;
-    const int64_t key0 = (int64_t)j * PYR_BLOCK;
-    __syncthreads();
-    for (int s = t; s < 64 * (D / VEC); s += 64) {
-      const int key = s / (D / VEC), c = (s % (D / VEC)) * VEC;
-      const int64_t kp = key0 + key;
-      float xk[VEC], xv[VEC];
-      if (kp < sq.Tk) {
-        unpack16<T>(ld16(kh + kp * D + c), xk);
-        unpack16<T>(ld16(vh + kp * D + c), xv);
-      } else {
+  const int nsel = s_n;
+  if (nsel > 0) issue_tiles_f32<D, NW>(kh, vh, sq.Tk, s_sel[0], st0, st0 + TG::TILE, w, l);
+
+  F32Wave<D> s_;
+  s_.row0 = (int64_t)i * PYR_BLOCK + (w % 2) * 32;
+  {
+    // rows past the end of a ragged last block load the last row; they are never stored
+    const float* qh = q + (sq.q0 + h * sq.qhs) * D;
+    const int64_t tok = min<int64_t>(s_.row0 + lr, sq.Tq - 1);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) xk[e] = xv[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        Kt[key][c + e] = xk[e];
-        Vt[key][c + e] = xv[e];
-      }
-    }
-    __syncthreads();
-    float mx = -INFINITY;
-    for (int key = 0; key < 64; ++key) {
-      if (key0 + key > rp) break;  // keys are ascending: the rest are in the future
-      float s = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) s = fmaf(qr[d], Kt[key][d], s);
-      mx = fmaxf(mx, s);
-    }
-    const float m_new = fmaxf(m, mx);
-    if (m_new == -INFINITY) continue;
-    const float alpha = exp2f(m - m_new);
-    lsum *= alpha;
-#pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] *= alpha;
-    for (int key = 0; key < 64; ++key) {
-      if (key0 + key > rp) break;
-      float s = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) s = fmaf(qr[d], Kt[key][d], s);
-      const float p = exp2f(s - m_new);
-      lsum += p;
-#pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vt[key][d], acc[d]);
-    }
-    m = m_new;
+    for (int c = 0; c < D / 8; ++c)
+      s_.qf[c] = *reinterpret_cast<const float4*>(qh + tok * D + 8 * c + 4 * half);
   }
-  if (!valid) return;
-  T* orow = o + (sq.q0 + h * sq.qhs + rp) * D;
-  const float inv = 1.f / lsum;
-  for (int d = 0; d < D; ++d) {
-    const float y = acc[d] * inv;
-    if constexpr (sizeof(T) == 4)
-      orow[d] = y;
-    else
-      orow[d] = (T)f32_to_bf16_bits(y);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s_.oacc[dt][e] = 0.f;
+  s_.m_run = -INFINITY;
+  s_.l_run = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) s_.kfrag[kt] = (kt * 32 + lr) * TG::ROW;
+  s_.kswz = TG::swz_k(lr);  // rows lr and 32 + lr share it
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+    s_.voff[dt] = 4 * half * TG::ROW + (((dt * 8 + lr / 4) ^ TG::swz_v(4 * half)) << 4) +
+                  (lr % 4) * 4;  // keys 8a + 4*half + c share swz_v(4*half)
+
+  // block jj's tiles are in st0 (jj even) or st1 (jj odd)
+  for (int jj = 0; jj < nsel; jj += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block jj landed
+    __syncthreads();                     // everyone's; the stage of block jj - 1 is free
+    f32_block<D, NW>(s_, st0, s_sel[jj], st1, jj + 1 < nsel ? s_sel[jj + 1] : -1, kh, vh, sq.Tk,
+                     sl2, w, l);
+    if (jj + 1 < nsel) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      f32_block<D, NW>(s_, st1, s_sel[jj + 1], st0, jj + 2 < nsel ? s_sel[jj + 2] : -1, kh, vh,
+                       sq.Tk, sl2, w, l);
+    }
   }
-  if (lse) lse[sq.q0 + h * sq.qhs + rp] = (m + log2f(lsum)) * PYR_LN2;
+
+  // finalize: the lane's row is row0 + lr; O^T element e of dim tile dt is dim
+  // dt*32 + (e/4)*8 + half*4 + e%4
+  const float lt = s_.l_run + __shfl_xor(s_.l_run, 32, 64);
+  const int64_t tok = s_.row0 + lr;
+  if (tok >= sq.Tq) return;
+  float* orow = o + (sq.q0 + h * sq.qhs + tok) * D;
+  const float inv = 1.f / lt;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      float4 y;
+      y.x = s_.oacc[dt][g4 * 4 + 0] * inv;
+      y.y = s_.oacc[dt][g4 * 4 + 1] * inv;
+      y.z = s_.oacc[dt][g4 * 4 + 2] * inv;
+      y.w = s_.oacc[dt][g4 * 4 + 3] * inv;
+      *reinterpret_cast<float4*>(orow + dt * 32 + g4 * 8 + half * 4) = y;
+    }
+  if (lse && half == 0) lse[sq.q0 + h * sq.qhs + tok] = (s_.m_run + log2f(lt)) * PYR_LN2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1343,9 +1495,23 @@ hipError_t launch_attn_d(const PyrGeom& g, int dtype, const void* q, const void*
     else
       hipLaunchKernelGGL((attn_prefill_mfma<D, 2, 1>), grid, dim3(128), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
   } else {
-    hipLaunchKernelGGL((attn_prefill_valu<float, D>), dim3((unsigned)(units * g.G)), dim3(64), 0,
-                       st, static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), sel, static_cast<float*>(o), lse, g);
+    // two waves of 32 rows per head; at d = 128 the Q values, O accumulators
+    // and scores of a wave need more than the 256 registers of two waves per
+    // SIMD, so workgroups take at most two heads (four waves, one per SIMD)
+    const int nh = D == 64 && g.G % 4 == 0 ? 4 : (g.G % 2 == 0 ? 2 : 1);
+    const int wpu = g.G / nh;
+    const dim3 grid((unsigned)(units * wpu));
+    const float* qq = static_cast<const float*>(q);
+    const float* kk = static_cast<const float*>(k);
+    const float* vv = static_cast<const float*>(v);
+    float* oo = static_cast<float*>(o);
+    if (nh == 4)
+      hipLaunchKernelGGL((attn_prefill_f32<D, D == 64 ? 8 : 4>), grid, dim3(D == 64 ? 512 : 256), 0, st,
+                         qq, kk, vv, sel, oo, lse, g, wpu);
+    else if (nh == 2)
+      hipLaunchKernelGGL((attn_prefill_f32<D, 4>), grid, dim3(256), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
+    else
+      hipLaunchKernelGGL((attn_prefill_f32<D, 2>), grid, dim3(128), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
   }
   return hipGetLastError();
 }

@@ -62,12 +62,12 @@ def run_device(cfg: W.Config, q, k, v, trace=True, sel_in=None, fused=False):
 
 
 def check_fast_selection(p, q, k, v, pyr, sel, tids, o=None, lse=None):
-    """Without a score trace the selection scores on the hi plane alone and
-    re-scores exactly only the candidates its error bound leaves undecided:
-    its route rows and trace ids must be those of the traced (every candidate
-    scored exactly) selection, bit for bit -- with the id trace and without
-    any trace.  With o and lse (a fused call) the fused launch without traces
-    must also give the same outputs."""
+    """Without a score trace (and without a fallback) the selection ranks
+    each level by counting on all its waves instead of recording scores and
+    the margin on one: its route rows and trace ids must be those of the
+    traced selection, bit for bit -- with the id trace and without any trace.
+    With o and lse (a fused call) the fused launch without traces must also
+    give the same outputs."""
     sel_f, sel_n = H.alloc_sel(p), H.alloc_sel(p)
     tids_f = torch.full_like(tids, -7)
     if o is None:
@@ -79,8 +79,8 @@ def check_fast_selection(p, q, k, v, pyr, sel, tids, o=None, lse=None):
                           H.alloc_workspace(p), tids_f, None)
         H.pyr_select_attn(p, q, k, v, pyr, sel_n, o_n, lse_n, H.alloc_workspace(p))
     torch.cuda.synchronize()
-    assert torch.equal(sel_f, sel), "route rows with the id trace only differ from the exact ones"
-    assert torch.equal(sel_n, sel), "route rows without traces differ from the exact ones"
+    assert torch.equal(sel_f, sel), "route rows with the id trace only differ from the traced ones"
+    assert torch.equal(sel_n, sel), "route rows without traces differ from the traced ones"
     assert torch.equal(tids_f, tids), "trace ids without the score trace differ"
     if o is not None:
         assert torch.equal(o_n.view(torch.int16), o.view(torch.int16))

@@ -44,6 +44,12 @@ CASES = [
     C("g3_bf16", 1, 6, 2, 64 * 33 + 5, 64 * 33 + 5, 128, torch.bfloat16, 2, 5, 3, seed=15),
     # fp32 with d=128 and G=2
     C("fp32_d128_g2", 1, 4, 2, 64 * 24, 64 * 24, 128, torch.float32, 4, 3, 0, seed=16),
+    # fp32 attention workgroup shapes: four heads of d=64 (8 waves), four heads of
+    # d=128 (two workgroups of two heads), three heads (one head per workgroup);
+    # ragged tails
+    C("fp32_d64_g4", 1, 8, 2, 64 * 21 + 9, 64 * 21 + 9, 64, torch.float32, 2, 6, 0, seed=24),
+    C("fp32_d128_g4", 1, 8, 2, 64 * 18 + 40, 64 * 18 + 40, 128, torch.float32, 4, 5, 0, seed=25),
+    C("fp32_d128_g3", 1, 6, 2, 64 * 15 + 1, 64 * 15 + 1, 128, torch.float32, 3, 4, 0, seed=26),
     # decode: 4 sequences, 1 token each at kv_len-1 (ragged last block)
     C("decode_small", 4, 8, 2, 1, 64 * 300 + 5, 128, torch.bfloat16, 4, 16, 8, seed=17),
     C("decode_fp32_g1", 3, 2, 2, 1, 64 * 70, 64, torch.float32, 2, 7, 0, seed=18),

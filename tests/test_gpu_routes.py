@@ -30,7 +30,7 @@ CASES = [
     C("rep_g2_d64", 1, 4, 2, 64 * 10, 64 * 10, 64, BF, 2, 5, 0, seed=52),
     # MHA, d = 128: attn_prefill_mfma<128, 2, 1>
     C("rep_mha_d128", 2, 2, 2, 64 * 9 + 30, 64 * 9 + 30, 128, BF, 4, 4, 0, seed=53),
-    # fp32: attn_prefill_valu
+    # fp32: attn_prefill_f32<64, 4>
     C("rep_fp32", 1, 4, 2, 64 * 8 + 3, 64 * 8 + 3, 64, F32, 2, 4, 0, seed=54),
     # decode, bf16 (attn_decode_mfma) and fp32 (attn_decode_split); K + 1 > 8
     # so a row spans several splits and a repeat can sit in a later split
