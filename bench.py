@@ -414,13 +414,14 @@ def main():
     if args.fused:   # one launch: the stage of the selection holds both
         t_sel = t_attn = stage_ms[1] / 1e3
     achieved = a_flops / t_attn / 1e12
-    # the attention's bound: MFMA where a gathered byte feeds many flops (four
-    # or more query heads per KV head: 225 flop/B at 128K, 452 at 1M), the
-    # gather bandwidth where it feeds few (one head per KV head: 59 flop/B) and
-    # for decode (one query row per head)
-    hbm_bound = cfg.decode or a_flops / a_bytes < 100
     # the attention's matrix-core peak for its input type (bf16 or fp32 MFMA)
     peak_mfma = PEAK_BF16_TFLOPS if cfg.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
+    # the attention's bound: MFMA where a gathered byte feeds many flops (bf16
+    # with four or more query heads per KV head: 225 flop/B at 128K, 452 at 1M),
+    # the gather bandwidth where it feeds few (bf16 with one head per KV head:
+    # 59 flop/B) and for decode (one query row per head); the threshold of 100
+    # flop/B for bf16 scales with the peak (6.3 flop/B for fp32)
+    hbm_bound = cfg.decode or a_flops / a_bytes < 100 * peak_mfma / PEAK_BF16_TFLOPS
     traffic = kernel_traffic(cfg.name + ("_packed" if lengths else ""))
     line = {
         "metric": METRIC,
