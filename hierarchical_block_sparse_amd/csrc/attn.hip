@@ -1381,7 +1381,13 @@ __global__ __launch_bounds__(256, 4) void attn_decode_mfma(
     if (b + 1 < nblk) step(b + 1, k1, k0, vt1, vt0);
   }
 
-  // merge the four waves' states: lane holds row lr, d = 16*dt + 4*lg + e
+  // merge the four waves' states: lane holds row lr, d = 16*dt + 4*lg + e.
+  // Row r's value of dim d sits at r*D + (d ^ dec_swz(r)): a row is a whole
+  // number of 64-bank sweeps, so without the XOR the 16 rows of a store would
+  // hit one bank; with it the 64 lanes of every store meet 64 distinct banks
+  // (bits 0-1 of the column take r % 4, bits 4-5 take r / 4), and the merge's
+  // reads of 64 consecutive dims of a row stay a permutation of 64 banks.
+  auto dec_swz = [](int r) { return (r & 3) | ((r >> 2) << 4); };
   __syncthreads();  // the V slots are free: waves 0-1 park their sums in vt0, 2-3 in vt1
   float* s_o = reinterpret_cast<float*>(w < 2 ? vt0 : vt1) + (w % 2) * 16 * D;
   if (lg == 0) {
@@ -1391,7 +1397,7 @@ __global__ __launch_bounds__(256, 4) void attn_decode_mfma(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[lr * D + 16 * dt + 4 * lg + e] = oacc[dt][e];
+    for (int e = 0; e < 4; ++e) s_o[lr * D + ((16 * dt + 4 * lg + e) ^ dec_swz(lr))] = oacc[dt][e];
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += 256) {
     const int r = idx / D, d = idx % D;
@@ -1404,7 +1410,7 @@ __global__ __launch_bounds__(256, 4) void attn_decode_mfma(
       const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[ww][r] - m);
       const float* so = reinterpret_cast<const float*>(ww < 2 ? vt0 : vt1) + (ww % 2) * 16 * D;
       lsum += a * s_l[ww][r];
-      acc += a * so[r * D + d];
+      acc += a * so[r * D + (d ^ dec_swz(r))];
     }
     float* dst = ws + (((int64_t)bhk * G + r) * nsplit + split) * (D + 2);
     if (d == 0) {
