@@ -161,7 +161,13 @@ hipError_t launch_select_d(const PyrGeom& g, int dtype, const void* q, const flo
   if (mt) {
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     switch (mt) {
-      case 1: hipLaunchKernelGGL((select_mfma<D, 1, 4>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
+      case 1:
+        if (g.decode)
+          hipLaunchKernelGGL((select_mfma<D, 1, 4, true>), grid, block, lds, st, qq, pyr, sel, tid_,
+                             tsc, g);
+        else
+          hipLaunchKernelGGL((select_mfma<D, 1, 4>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g);
+        break;
       case 2: hipLaunchKernelGGL((select_mfma<D, 2, 4>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
       case 4: hipLaunchKernelGGL((select_mfma<D, 4, 4>), grid, block, lds, st, qq, pyr, sel, tid_, tsc, g); break;
       default:  // G = 8: eight waves of four M tiles
@@ -184,7 +190,7 @@ size_t pyr_select_lds_bytes(const PyrGeom& g, int dtype) {
   const bool mfma = mfma_tiles(g, dtype) != 0;
   // dynamic layout, plus the candidate stages of the MFMA path (a static array)
   return SelLayout(g.K, g.branching, g.D, mfma, mfma_tiles(g, dtype) == 8 ? 8 : kWaves).total +
-         (mfma ? (size_t)kSelStages * kChunk * 4 * g.D : 0);
+         (mfma ? (size_t)(g.decode ? kSelStagesDecode : kSelStages) * kChunk * 4 * g.D : 0);
 }
 
 hipError_t pyr_launch_select(const PyrGeom& g, int dtype, const void* q, const float* pyr,

@@ -16,6 +16,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 32;   // candidates per LDS chunk (MFMA path): two 16-wide N tiles
 constexpr int kZbuf = 8192;  // fp32 scratch for the generic path
 constexpr int kSelStages = 2;  // candidate chunks in LDS (MFMA path): one scored while one loads
+constexpr int kSelStagesDecode = 4;  // decode: one stage per wave (score_exact_dec)
 // Slots after the ancestors in the layout's misc area (4 bytes each).
 enum SelMisc {
   kNkept = 0,    // kept count
@@ -401,6 +402,53 @@ __device__ __forceinline__ void score_exact(const unsigned char* lvl, const int*
   }
 }
 
+// Decode's exact scores: every wave holds the unit's G query rows (one
+// 16-row tile) and scores its own chunks c = w, w + NW, ... of the list from
+// a stage of its own (st + w * kChunk * 4 * D), loading a chunk and then
+// scoring it with no workgroup barrier in between.  A chunk's few real rows
+// take far less than its load's latency, so score_exact's barrier-paced
+// pipeline (every wave on every chunk) spent a load latency per chunk.  A
+// wave's (max, sum) pair of an entry is then its whole LogSumExp: it goes to
+// the wave-0 slot and the other slots get the empty pair, so merged_score
+// gives what score_exact gives.  Every thread calls it; the caller's barrier
+// makes the partials visible.
+template <int D, int NW>
+__device__ __forceinline__ void score_exact_dec(const unsigned char* lvl, const int* cand, int n,
+                                                const uint4 (&qa)[1][D / 32], uint32_t rowvalid,
+                                                float sl2, lds_f32x2* part, int cmax,
+                                                unsigned char* st, int w, int l) {
+  constexpr int CPR = D / 8;
+  unsigned char* mine = st + w * (kChunk * 4 * D);
+  const int nchunks = (n + kChunk - 1) / kChunk;
+  for (int c = w; c < nchunks; c += NW) {
+    issue_chunk<D, 64>(lvl, cand, nullptr, n, c, mine, 0, l);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of chunk c
+#pragma unroll
+    for (int nt = 0; nt < kChunk / 16; ++nt) {
+      if (c * kChunk + nt * 16 >= n) break;  // uniform
+      f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+      const int r = nt * 16 + (l % 16);
+      const unsigned char* row = mine + r * 4 * D;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const int off = ((4 * ks + l / 16) ^ (r % CPR)) << 4;
+        const bf16x8 bhv = as_bf16x8(*reinterpret_cast<const uint4*>(row + off));
+        const bf16x8 blv = as_bf16x8(*reinterpret_cast<const uint4*>(row + 2 * D + off));
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[0][ks]), bhv, acc[0], 0, 0, 0);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[0][ks]), blv, acc[0], 0, 0, 0);
+      }
+      float m, s;
+      tile_lse<1, false>(acc, rowvalid, sl2, m, s);
+      const int cn = c * kChunk + nt * 16 + l;
+      if (l < 16 && cn < n) {
+        part[cn] = f32x2{m, s};
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) part[ww * cmax + cn] = f32x2{-INFINITY, 0.f};
+      }
+    }
+  }
+}
+
 // Merged score of entry j from the waves' partials (natural log; NaN ranks
 // last as -inf).  The exact path and the re-scoring of undecided candidates
 // both use it, so a candidate gets the same bits from either.
@@ -431,6 +479,17 @@ __device__ __forceinline__ int count_above(const uint64_t* key, int n, uint64_t 
   return cnt;
 }
 
+// Number of the 16 keys at key[0..16) above kj.
+__device__ __forceinline__ int count16(const uint64_t* key, uint64_t kj) {
+  ulonglong2 a[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) a[u] = *reinterpret_cast<const ulonglong2*>(key + 2 * u);
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) cnt += (a[u].x > kj) + (a[u].y > kj);
+  return cnt;
+}
+
 // Rank key of a score at candidate position j: larger score first, then the
 // lower position (the lower node index: candidates ascend by index).
 __device__ __forceinline__ uint64_t rank_key(float sc, int j) {
@@ -439,11 +498,11 @@ __device__ __forceinline__ uint64_t rank_key(float sc, int j) {
 
 // Ranking of one scored level without a score trace or fallback, after
 // score_exact and its barrier: every candidate's merged score gets a 64-bit
-// key (score, then the lower position), each thread counts the keys above
-// its candidates' (the ranks, spread over all waves), the candidates ranked
-// below Ku are flagged, and wave 0 compacts them in index order into kept[].
+// key (score, then the lower position), the keys above each candidate's are
+// counted (its rank; the counting is spread over all threads), and wave 0
+// compacts the candidates ranked below Ku in index order into kept[].
 // The kept set is the one top_k_and_trace keeps from the same scores.
-template <int NW>
+template <int NW, bool BAL = false>
 __device__ __forceinline__ void rank_level(const PyrGeom& g, int level, int C, int Ku,
                                            const SelLayout& lay, unsigned char* smem,
                                            int32_t* tr_ids, int w, int l) {
@@ -458,8 +517,35 @@ __device__ __forceinline__ void rank_level(const PyrGeom& g, int level, int C, i
   int* misc = reinterpret_cast<int*>(smem + lay.off_misc) + PYR_MAX_LEVELS;
   const int C16 = (C + 15) & ~15;  // <= cmax, a multiple of 32
   for (int j = tid; j < C16; j += NT) key[j] = j < C ? rank_key(merged_score<NW>(part, cmax, j), j) : 0ull;
+  if (BAL && C > NT)  // the counts are accumulated below
+    for (int j = tid; j < C; j += NT) flag[j] = 0;
   lds_barrier();
-  for (int j = tid; j < C; j += NT) flag[j] = count_above(key, C16, key[j]) < Ku;
+  if (!BAL || C <= NT) {
+    // a candidate per thread: its rank (the keys above its key)
+    for (int j = tid; j < C; j += NT) flag[j] = count_above(key, C16, key[j]);
+  } else {
+    // BAL, more candidates than threads (decode: C = b*K + b - 1 just over
+    // the 256 threads): the (candidate, 16-key batch) pairs are spread
+    // evenly, each thread takes a contiguous run of them and adds its counts
+    // into the ranks, instead of a few threads counting a second candidate.
+    const int nbt = C16 / 16;
+    const int U = C * nbt;
+    const int u0 = (int)((int64_t)U * tid / NT), u1 = (int)((int64_t)U * (tid + 1) / NT);
+    if (u0 < u1) {
+      int j = u0 / nbt, b = u0 % nbt, cnt = 0;
+      uint64_t kj = key[j];
+      for (int u = u0; u < u1; ++u) {
+        cnt += count16(key + 16 * b, kj);
+        if (++b == nbt && u + 1 < u1) {
+          atomicAdd(&flag[j], cnt);
+          b = 0;
+          cnt = 0;
+          kj = key[++j];
+        }
+      }
+      atomicAdd(&flag[j], cnt);
+    }
+  }
   lds_barrier();
   if (w == 0) {
     const uint64_t lt = (1ull << l) - 1ull;
@@ -471,7 +557,7 @@ __device__ __forceinline__ void rank_level(const PyrGeom& g, int level, int C, i
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = j0 + 64 * u + l;
-        f[u] = j < C && flag[j] != 0;
+        f[u] = j < C && flag[j] < Ku;
         id[u] = j < C ? cand[j] : 0;
       }
 #pragma unroll
@@ -497,7 +583,7 @@ __device__ __forceinline__ void rank_level(const PyrGeom& g, int level, int C, i
 // row (and trace) of the unit.  Without a score trace and without a
 // fallback, scored levels are ranked by rank_level; otherwise by
 // top_k_and_trace, which also records scores and the margin.
-template <int D, int MT, int NW>
+template <int D, int MT, int NW, bool DEC = false>
 __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
                                                  const float* __restrict__ pyr,
                                                  int32_t* __restrict__ sel,
@@ -545,9 +631,11 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
   // 8 consecutive d at 32*ks + 8*(l/16).
   uint4 qa[MT][D / 32];
   uint32_t rowvalid = 0;  // bit (mt*4 + j): C-layout row 4*(l/16)+j of tile mt is a real row
+  // (DEC: every wave holds the same rows, the G real ones in its first tile)
+  const int rbase = DEC ? 0 : w * RW;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int ra = w * RW + mt * 16 + (l % 16);
+    const int ra = rbase + mt * 16 + (l % 16);
     int h;
     int64_t tok;
     if (g.decode) {
@@ -562,7 +650,7 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
     for (int ks = 0; ks < D / 32; ++ks) qa[mt][ks] = ld16(qrow + ks * 32 + 8 * (l / 16));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int rc = w * RW + mt * 16 + 4 * (l / 16) + j;
+      const int rc = rbase + mt * 16 + 4 * (l / 16) + j;
       const bool real = g.decode ? rc < g.G : (int64_t)i * PYR_BLOCK + rc % PYR_BLOCK < sq.Tq;
       if (real) rowvalid |= 1u << (mt * 4 + j);
     }
@@ -599,11 +687,14 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
       continue;
     }
     const unsigned char* lvl = split + g.loff[level] * 4 * D;
-    score_exact<D, MT, NW>(lvl, cand, nullptr, C, qa, rowvalid, full, sl2, part, lay.cmax, st0,
-                           st1, w, l);
+    if constexpr (DEC)
+      score_exact_dec<D, NW>(lvl, cand, C, qa, rowvalid, sl2, part, lay.cmax, st0, w, l);
+    else
+      score_exact<D, MT, NW>(lvl, cand, nullptr, C, qa, rowvalid, full, sl2, part, lay.cmax, st0,
+                             st1, w, l);
     lds_barrier();
     if (ranked) {
-      rank_level<NW>(g, level, C, Ku, lay, smem, tr_ids, w, l);
+      rank_level<NW, DEC>(g, level, C, Ku, lay, smem, tr_ids, w, l);
       continue;
     }
     for (int j = tid; j < C; j += NT) score[j] = merged_score<NW>(part, lay.cmax, j);
@@ -621,21 +712,22 @@ __device__ __forceinline__ void select_mfma_unit(const bf16_t* __restrict__ q,
 // NW waves of MT M tiles each, at most 128 VGPRs (four waves per SIMD):
 // four four-wave workgroups (G = 4) or two eight-wave ones (G = 8) share a
 // CU, so other units' scoring fills a unit's ranking and load latency.
-template <int D, int MT, int NW>
+template <int D, int MT, int NW, bool DEC = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void select_mfma(
     const bf16_t* __restrict__ q, const float* __restrict__ pyr, int32_t* __restrict__ sel,
     int32_t* __restrict__ trace_ids, float* __restrict__ trace_scores, PyrGeom g) {
   constexpr int STAGE = kChunk * 4 * D;  // bytes per LDS stage
   static_assert(kSelStages == 2, "two candidate stages");
+  static_assert(!DEC || (MT == 1 && NW <= kSelStagesDecode), "decode: one tile, a stage per wave");
   // The layout is the one dynamic array: with a second __shared__ variable
   // the compiler would give each its own alias scope and wait for every chunk
   // load in flight before any LDS read, undoing the prefetch.
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ __attribute__((aligned(16))) unsigned char stages[kSelStages * STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char stages[(DEC ? kSelStagesDecode : kSelStages) * STAGE];
   int64_t unit;
   if (!sel_unit(g, unit)) return;
-  select_mfma_unit<D, MT, NW>(q, pyr, sel, trace_ids, trace_scores, g, unit, smem, stages,
-                              stages + STAGE);
+  select_mfma_unit<D, MT, NW, DEC>(q, pyr, sel, trace_ids, trace_scores, g, unit, smem, stages,
+                                   stages + STAGE);
 }
 
 }  // namespace
