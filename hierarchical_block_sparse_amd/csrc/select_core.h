@@ -517,33 +517,23 @@ __device__ __forceinline__ void rank_level(const PyrGeom& g, int level, int C, i
   int* misc = reinterpret_cast<int*>(smem + lay.off_misc) + PYR_MAX_LEVELS;
   const int C16 = (C + 15) & ~15;  // <= cmax, a multiple of 32
   for (int j = tid; j < C16; j += NT) key[j] = j < C ? rank_key(merged_score<NW>(part, cmax, j), j) : 0ull;
-  if (BAL && C > NT)  // the counts are accumulated below
-    for (int j = tid; j < C; j += NT) flag[j] = 0;
+  if (BAL && C > NT)  // the counts of candidates NT .. C-1 are accumulated below
+    for (int j = NT + tid; j < C; j += NT) flag[j] = 0;
   lds_barrier();
   if (!BAL || C <= NT) {
-    // a candidate per thread: its rank (the keys above its key)
+    // a candidate per thread: its rank (the keys above its key); the lanes of
+    // a wave read the same keys (LDS broadcast)
     for (int j = tid; j < C; j += NT) flag[j] = count_above(key, C16, key[j]);
   } else {
     // BAL, more candidates than threads (decode: C = b*K + b - 1 just over
-    // the 256 threads): the (candidate, 16-key batch) pairs are spread
-    // evenly, each thread takes a contiguous run of them and adds its counts
-    // into the ranks, instead of a few threads counting a second candidate.
+    // the threads): candidate tid as above, and the 16-key batches of the
+    // candidates past NT spread one per thread and added into their ranks,
+    // instead of a few threads counting a second candidate in full
+    flag[tid] = count_above(key, C16, key[tid]);
     const int nbt = C16 / 16;
-    const int U = C * nbt;
-    const int u0 = (int)((int64_t)U * tid / NT), u1 = (int)((int64_t)U * (tid + 1) / NT);
-    if (u0 < u1) {
-      int j = u0 / nbt, b = u0 % nbt, cnt = 0;
-      uint64_t kj = key[j];
-      for (int u = u0; u < u1; ++u) {
-        cnt += count16(key + 16 * b, kj);
-        if (++b == nbt && u + 1 < u1) {
-          atomicAdd(&flag[j], cnt);
-          b = 0;
-          cnt = 0;
-          kj = key[++j];
-        }
-      }
-      atomicAdd(&flag[j], cnt);
+    for (int t = tid; t < (C - NT) * nbt; t += NT) {
+      const int j = NT + t / nbt, bt = t % nbt;
+      atomicAdd(&flag[j], count16(key + 16 * bt, key[j]));
     }
   }
   lds_barrier();
