@@ -53,6 +53,12 @@ CASES = [
     # decode: 4 sequences, 1 token each at kv_len-1 (ragged last block)
     C("decode_small", 4, 8, 2, 1, 64 * 300 + 5, 128, torch.bfloat16, 4, 16, 8, seed=17),
     C("decode_fp32_g1", 3, 2, 2, 1, 64 * 70, 64, torch.float32, 2, 7, 0, seed=18),
+    # decode selection with many more candidates than threads (b*K + b - 1 = 803
+    # against 256: the ranking's extra candidates spread by key batch), sixteen
+    # query heads per KV head (the whole 16-row tile real), d = 64
+    C("decode_g16_d64_k200", 2, 32, 2, 1, 64 * 700 + 3, 64, torch.bfloat16, 4, 200, 8, seed=27),
+    # decode, eight heads per KV head, 403 candidates per scored level
+    C("decode_g8_k100", 2, 16, 2, 1, 64 * 500 + 40, 128, torch.bfloat16, 4, 100, 8, seed=28),
     # K larger than the number of past blocks everywhere
     C("k_exceeds", 1, 4, 2, 64 * 9, 64 * 9, 128, torch.bfloat16, 2, 12, 0, seed=19),
     # one pyramid level below the root (b >= nb)
