@@ -16,18 +16,19 @@
 //   3. the K best (score desc, index asc) are kept, in ascending index order.
 // The route row is the finest kept set, the diagonal block, then -1.
 //
-// Scoring, bf16 prefill path: rows are the M side of v_mfma_f32_16x16x32_bf16
-// and candidates the N side; each wave keeps its rows of Q in VGPRs for the
-// whole unit.  Pooled keys are fp32; each is split into hi = bf16(x) and
+// Scoring, bf16 path: rows are the M side of v_mfma_f32_16x16x32_bf16 and
+// candidates the N side; each wave keeps its rows of Q in VGPRs for the whole
+// unit.  Pooled keys are fp32; each is split into hi = bf16(x) and
 // lo = bf16(x - hi) and both are contracted against the exact bf16 q, so a dot
 // product carries ~2^-17 relative error instead of bf16's 2^-9.  The build
 // stores the hi/lo rows beside the means (plane 1), and candidates go through
 // LDS in chunks of 32 with direct global-to-LDS loads, two stages deep (one
-// barrier per chunk).  Each wave reduces its
-// rows' LogSumExp per candidate in-lane and across its 4 lane groups with
-// shuffles, as (max, sum) pairs in the log2 domain; the waves' partials are
-// merged once per level.  Generic path (fp32 inputs, decode, other group
-// sizes): fp32 dot products on the vector ALUs, same selection logic.
+// barrier per chunk); in decode (a 16-row tile holding the G query rows) each
+// wave scores its own chunks instead.  Each wave reduces its rows' LogSumExp
+// per candidate in-lane and across its 4 lane groups with shuffles, as (max,
+// sum) pairs in the log2 domain; the waves' partials are merged once per
+// level.  Generic path (fp32 inputs, and bf16 group sizes the MFMA tiles do
+// not cover): fp32 dot products on the vector ALUs, same selection logic.
 #include <math.h>
 
 #include "pyr_device.h"
@@ -38,8 +39,8 @@
 namespace {
 
 // ---------------------------------------------------------------------------
-// Generic path: fp32 dot products on the vector ALUs (fp32 inputs, decode,
-// group sizes the MFMA path does not tile).
+// Generic path: fp32 dot products on the vector ALUs (fp32 inputs, prefill
+// and decode; bf16 group sizes the MFMA path does not tile).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void select_valu(const T* __restrict__ q,
