@@ -50,6 +50,9 @@ CASES = [
     C("fp32_d64_g4", 1, 8, 2, 64 * 21 + 9, 64 * 21 + 9, 64, torch.float32, 2, 6, 0, seed=24),
     C("fp32_d128_g4", 1, 8, 2, 64 * 18 + 40, 64 * 18 + 40, 128, torch.float32, 4, 5, 0, seed=25),
     C("fp32_d128_g3", 1, 6, 2, 64 * 15 + 1, 64 * 15 + 1, 128, torch.float32, 3, 4, 0, seed=26),
+    # fp32, eight heads per KV head at d = 128 (four two-head workgroups per
+    # unit), K beyond the history: route rows padded with -1
+    C("fp32_g8_k_exceeds", 1, 16, 2, 64 * 9 + 33, 64 * 9 + 33, 128, torch.float32, 2, 12, 0, seed=29),
     # decode: 4 sequences, 1 token each at kv_len-1 (ragged last block)
     C("decode_small", 4, 8, 2, 1, 64 * 300 + 5, 128, torch.bfloat16, 4, 16, 8, seed=17),
     C("decode_fp32_g1", 3, 2, 2, 1, 64 * 70, 64, torch.float32, 2, 7, 0, seed=18),
