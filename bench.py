@@ -229,13 +229,18 @@ def cpu_baseline(cfg, q, k, v, n_units, backward=False):
     }
 
 
-def attn_kernel_name(cfg):
-    """The attention kernel the library runs for this workload."""
+def attn_kernel_name(cfg, packed=False):
+    """The attention kernels the library runs for this workload, in launch
+    order (dense bfloat16 prefill with G a multiple of 4 and (K+1) * G/4 >= 64
+    first writes the block-transposed copy of v into the workspace)."""
     if cfg.decode:
         return "attn_decode_mfma+combine" if cfg.dtype.itemsize == 2 else "attn_decode_split+combine"
     if cfg.dtype.itemsize != 2:
         return "attn_prefill_f32"
-    return "attn_prefill_pp" if cfg.group % 4 == 0 else "attn_prefill_mfma"
+    if cfg.group % 4 == 0:
+        vt = not packed and (cfg.top_k + 1) * (cfg.group // 4) >= 64
+        return "attn_vt_build+attn_prefill_pp" if vt else "attn_prefill_pp"
+    return "attn_prefill_mfma"
 
 
 def planted_recall(cfg, sel):
@@ -444,7 +449,7 @@ def main():
                                          if cfg.decode else "build+select+attn"),
         },
         "roofline": {
-            "kernel": attn_kernel_name(cfg),
+            "kernel": attn_kernel_name(cfg, packed=bool(lengths)),
             "bound": "mfma" if not hbm_bound else "hbm",
             "achieved": round(achieved, 2) if not hbm_bound else round(a_bytes / t_attn / 1e9, 1),
             "peak": peak_mfma if not hbm_bound else PEAK_HBM_GBS,

@@ -73,6 +73,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kRescaleLog2 = 8.f;  // rescale O only when a row max grows by > 2^8
+constexpr int kVtRow = PYR_BLOCK * 2;  // bytes per row of a transposed V tile (attn_vt_build)
 
 template <int D>
 struct TileGeom {
@@ -338,11 +339,18 @@ struct FragOffsets {
   // (2*ks + half) ^ swz = 2*ks ^ (swz ^ half): byte offset krow + (32*ks ^ kx)
   int krow, kx;
   int v[D / 32];  // V^T fragment of dim tile dt: keys 4*half + l%16/4 (and + 8)
+  // transposed V tiles (VT, see attn_vt_build): row d = dt*32 + lr of the tile
+  // holds chunk c at c ^ vsw(d), vsw(d) = (d / 2) % 8 = (lr / 2) % 8; the lane's
+  // fragment chunk is 4*kt + 2*k2 + half, read at that ^ vsw: (4*kt + 2*k2) ^ vx
+  int vt[D / 32], vx;
   __device__ FragOffsets(int l) {
     using TG = TileGeom<D>;
     const int half = l / 32, lr = l % 32, g16 = l / 16, s16 = l % 16;
     krow = lr * TG::ROW;
     kx = (TG::swz_k(lr) ^ half) << 4;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) vt[dt] = (dt * 32 + lr) * kVtRow;
+    vx = half ^ ((lr / 2) % 8);
     const int r1 = 4 * half + s16 / 4;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
@@ -354,8 +362,10 @@ struct FragOffsets {
 
 // Tile loads of block j for the 8-wave kernel (same layout as issue_tiles):
 // the block's first row is a uniform base and each lane adds a 32-bit
-// offset, clamped to the last row of the sequence.
-template <int D>
+// offset, clamped to the last row of the sequence.  VT: vh is the (batch, KV
+// head)'s transposed V (attn_vt_build), block j's tile the 64*D elements at
+// vh + j*64*D, D rows of 128 bytes stored with chunk q of row r at q ^ ((r/2) % 8).
+template <int D, bool VT = false>
 __device__ __forceinline__ void tile_loads8(const bf16_t* kh, const bf16_t* vh, int64_t Tk, int j,
                                           int w, int l, unsigned char* ktile,
                                           unsigned char* vtile) {
@@ -371,7 +381,13 @@ __device__ __forceinline__ void tile_loads8(const bf16_t* kh, const bf16_t* vh, 
     const int p = t * 64 + l, row = p / TG::CPR, sc = p % TG::CPR;
     const int rr = row < last ? row : last;
     const bf16_t* ka = kb + rr * D + (sc ^ TG::swz_k(row)) * 8;
-    const bf16_t* va = vb + rr * D + (sc ^ TG::swz_v(row)) * 8;
+    const bf16_t* va;
+    if constexpr (VT) {
+      const int vr = p / 8, vq = p % 8;
+      va = vb + vr * PYR_BLOCK + (vq ^ ((vr / 2) % 8)) * 8;
+    } else {
+      va = vb + rr * D + (sc ^ TG::swz_v(row)) * 8;
+    }
     __builtin_amdgcn_global_load_lds((const void*)ka, (lds_void*)(ktile + t * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)va, (lds_void*)(vtile + t * 1024), 16, 0, 0);
   }
@@ -454,7 +470,7 @@ struct PpSlot {
   __device__ static constexpr int idx(int t) { return DO_S && DO_PV ? t / 2 : t; }
 };
 
-template <int D, bool DO_S, bool DO_PV>
+template <int D, bool DO_S, bool DO_PV, bool VT>
 __device__ __forceinline__ bf16x8 pp_frag(int t, const lds_u8* Kn, const lds_u8* Vx,
                                           const FragOffsets<D>& fo) {
   using TG = TileGeom<D>;
@@ -467,13 +483,18 @@ __device__ __forceinline__ bf16x8 pp_frag(int t, const lds_u8* Kn, const lds_u8*
     return __builtin_bit_cast(bf16x8, x);
   }
   const int u = SL::idx(t), kt = u / (D / 16), k2 = (u / (D / 32)) % 2, dt = u % (D / 32);
+  if constexpr (VT) {  // one 16-byte read: the tile's keys are in the fragment's order
+    const u32x4v x =
+        *reinterpret_cast<const lds_u32x4*>(Vx + fo.vt[dt] + (((kt * 4 + 2 * k2) ^ fo.vx) << 4));
+    return __builtin_bit_cast(bf16x8, x);
+  }
   const lds_u8* p = Vx + kt * HALF + fo.v[dt] + 16 * k2 * TG::ROW;
   const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
   const s16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * TG::ROW));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t1, t2, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int D, bool DO_S, bool DO_PV>
+template <int D, bool DO_S, bool DO_PV, bool VT = false>
 __device__ __forceinline__ void pp_matrix(const lds_u8* Kn, const lds_u8* Vx,
                                           const FragOffsets<D>& fo, const uint4 (&qb)[D / 16],
                                           f32x16 (&s)[2], const uint32_t (&p)[2][8],
@@ -490,10 +511,10 @@ __device__ __forceinline__ void pp_matrix(const lds_u8* Kn, const lds_u8* Vx,
   }
   bf16x8 fr[NM];
 #pragma unroll
-  for (int t = 0; t < kPpPF && t < NM; ++t) fr[t] = pp_frag<D, DO_S, DO_PV>(t, Kn, Vx, fl);
+  for (int t = 0; t < kPpPF && t < NM; ++t) fr[t] = pp_frag<D, DO_S, DO_PV, VT>(t, Kn, Vx, fl);
 #pragma unroll
   for (int t = 0; t < NM; ++t) {
-    if (t + kPpPF < NM) fr[t + kPpPF] = pp_frag<D, DO_S, DO_PV>(t + kPpPF, Kn, Vx, fl);
+    if (t + kPpPF < NM) fr[t + kPpPF] = pp_frag<D, DO_S, DO_PV, VT>(t + kPpPF, Kn, Vx, fl);
     if (SL::is_s(t)) {
       const int u = SL::idx(t), kt = u % 2, ks = u / 2;
       s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t], as_bf16x8(qb[ks]), s[kt], 0, 0, 0);
@@ -538,8 +559,8 @@ __device__ __forceinline__ void pp_vector(f32x16 (&s)[2], uint32_t (&p)[2][8],
   l_run += ps0 + ps1;
 }
 
-// Inputs of the ping-pong kernel's block loop.
-template <int D>
+// Inputs of the ping-pong kernel's block loop (VT: vh is the transposed V).
+template <int D, bool VT = false>
 struct PpRun {
   const bf16_t* kh;
   const bf16_t* vh;
@@ -591,15 +612,16 @@ __device__ __forceinline__ unsigned char* pp_v(int y) {
 }
 
 // This wave's share of the loads of block y (if it exists) into slot S.
-template <int D, int S>
-__device__ __forceinline__ void pp_issue(const PpRun<D>& r, int y) {
-  if (y < r.nsel) tile_loads8<D>(r.kh, r.vh, r.Tk, r.ord[y], r.w, r.l, pp_k<S>(y), pp_v<S>(y));
+template <int D, int S, bool VT>
+__device__ __forceinline__ void pp_issue(const PpRun<D, VT>& r, int y) {
+  if (y < r.nsel)
+    tile_loads8<D, VT>(r.kh, r.vh, r.Tk, r.ord[y], r.w, r.l, pp_k<S>(y), pp_v<S>(y));
 }
 
 // Wait for this wave's loads of block y: the loads of block y+1 (issued after
 // them) may stay in flight.
-template <int D>
-__device__ __forceinline__ void pp_wait(const PpRun<D>& r, int y) {
+template <int D, bool VT>
+__device__ __forceinline__ void pp_wait(const PpRun<D, VT>& r, int y) {
   using TG = TileGeom<D>;
   constexpr int NLOAD = 2 * (TG::CPR / 8);  // tile-load instructions per block per wave
   if (y + 1 < r.nsel)
@@ -615,8 +637,8 @@ __device__ __forceinline__ void pp_wait(const PpRun<D>& r, int y) {
 // For group 0 the vector phase is the odd global phase 2x+1, for group 1 the
 // even one 2x+2.
 // J: the slot of block x (x % 4) when known at compile time, else -1.
-template <int D, bool MASK, bool DO_S, int J>
-__device__ __forceinline__ void pp_block(const PpRun<D>& r, int x, const FragOffsets<D>& fo,
+template <int D, bool MASK, bool DO_S, int J, bool VT>
+__device__ __forceinline__ void pp_block(const PpRun<D, VT>& r, int x, const FragOffsets<D>& fo,
                                          const uint4 (&qb)[D / 16], f32x16 (&s)[2],
                                          uint32_t (&p)[2][8], f32x16 (&oacc)[D / 32],
                                          float& m_run, float& l_run) {
@@ -631,19 +653,20 @@ __device__ __forceinline__ void pp_block(const PpRun<D>& r, int x, const FragOff
   if (!r.grp) pp_wait(r, x + 1);
   lds_barrier();
   if (!r.grp) pp_issue<D, JL>(r, x + 3);
-  pp_matrix<D, DO_S, true>((lds_u8*)pp_k<JN>(x + 1), (lds_u8*)pp_v<J>(x), fo, qb, s, p, oacc);
+  pp_matrix<D, DO_S, true, VT>((lds_u8*)pp_k<JN>(x + 1), (lds_u8*)pp_v<J>(x), fo, qb, s, p, oacc);
 }
 
 // Attention of one unit's four query heads sub*4 .. sub*4+3 of KV head hk by
 // the eight waves of the workgroup.  s_sel holds the unit's route row (K+1
 // entries, visible to every thread); s_ord and s_cnt are LDS scratch.  Must be
-// called by every thread.
-template <int D>
+// called by every thread.  VT (dense batches): v is the transposed V of
+// attn_vt_build instead of V.
+template <int D, bool VT = false>
 __device__ __forceinline__ void pp_unit(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                         const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
-                                        float* __restrict__ lse, const PyrGeom& g, int hk, int i,
-                                        int sub, const PyrSeq& sq, const int* s_sel, int* s_ord,
-                                        int* s_cnt) {
+                                        float* __restrict__ lse, const PyrGeom& g, int bi, int hk,
+                                        int i, int sub, const PyrSeq& sq, const int* s_sel,
+                                        int* s_ord, int* s_cnt) {
   using TG = TileGeom<D>;
   static_assert(TG::TILE <= kPpTile, "tile slots are sized for d <= 128");
   const int tid = threadIdx.x, l = tid % 64;
@@ -684,7 +707,8 @@ __device__ __forceinline__ void pp_unit(const bf16_t* __restrict__ q, const bf16
   lds_barrier();  // the order is in LDS; the Q loads stay in flight
   const int nsel = s_cnt[0], nun = s_cnt[1];
   const bf16_t* kh = k + (sq.k0 + hk * sq.khs) * D;
-  const bf16_t* vh = v + (sq.k0 + hk * sq.khs) * D;
+  const bf16_t* vh = VT ? v + ((int64_t)bi * g.Hk + hk) * g.nb * PYR_BLOCK * D
+                        : v + (sq.k0 + hk * sq.khs) * D;
 
   const FragOffsets<D> fo(l);
   f32x16 oacc[D / 32];
@@ -697,7 +721,7 @@ __device__ __forceinline__ void pp_unit(const bf16_t* __restrict__ q, const bf16
   uint32_t p[2][8];
 
   if (nsel > 0) {
-    PpRun<D> r;
+    PpRun<D, VT> r;
     r.kh = kh;
     r.vh = vh;
     r.ord = s_ord;
@@ -716,7 +740,7 @@ __device__ __forceinline__ void pp_unit(const bf16_t* __restrict__ q, const bf16
     // global phase 0 starts: block 2 loads; group 1 sits it out
     pp_issue<D, 2>(r, 2);
     if (grp) lds_barrier();
-    pp_matrix<D, true, false>((lds_u8*)pp_k0, (lds_u8*)pp_v0, fo, qb, s, p, oacc);  // S(0)
+    pp_matrix<D, true, false, VT>((lds_u8*)pp_k0, (lds_u8*)pp_v0, fo, qb, s, p, oacc);  // S(0)
     // blocks before the last that need no mask, four at a time with every
     // slot named at compile time; then the others (masked blocks go last)
     const int last = nsel - 1;
@@ -763,7 +787,7 @@ __device__ __forceinline__ void pp_unit(const bf16_t* __restrict__ q, const bf16
     lse[sq.q0 + h * sq.qhs + tok] = lt > 0.f ? (m_run + log2f(lt)) * PYR_LN2 : -INFINITY;
 }
 
-template <int D>
+template <int D, bool VT>
 __global__ __launch_bounds__(512, 2) void attn_prefill_pp(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int32_t* __restrict__ sel, bf16_t* __restrict__ o, float* __restrict__ lse, PyrGeom g,
@@ -779,7 +803,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_pp(
   if (i >= sq.nqb) return;  // past the end of a shorter packed sequence
   for (int jj = threadIdx.x; jj <= g.K; jj += 512) s_sel[jj] = sel[unit * (g.K + 1) + jj];
   __syncthreads();
-  pp_unit<D>(q, k, v, o, lse, g, hk, i, sub, sq, s_sel, s_ord, s_cnt);
+  pp_unit<D, VT>(q, k, v, o, lse, g, bi, hk, i, sub, sq, s_sel, s_ord, s_cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -817,7 +841,7 @@ __global__ __launch_bounds__(512, 2) void select_attend(
   const int nk = reinterpret_cast<const int*>(pp_v0 + lay.off_misc)[PYR_MAX_LEVELS];
   for (int j = threadIdx.x; j <= g.K; j += 512) s_sel[j] = j < nk ? kept[j] : (j == nk ? i : -1);
   __syncthreads();
-  pp_unit<D>(q, k, v, o, lse, g, hk, i, 0, sq, s_sel, s_ord, s_cnt);
+  pp_unit<D>(q, k, v, o, lse, g, bi, hk, i, 0, sq, s_sel, s_ord, s_cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -1459,10 +1483,55 @@ __global__ __launch_bounds__(64) void attn_decode_combine(const float* __restric
   if (lse && l == 0) lse[qh] = (m + log2f(s)) * PYR_LN2;
 }
 
+// Block-transposed copy of V for attn_prefill_pp<D, true>: block j of
+// (batch, KV head) bh becomes 64*D elements at vt + (bh*nb + j)*64*D, D rows
+// of its 64 keys, so that a V^T fragment of the PV product (8 keys of one
+// dim) is one 16-byte LDS read instead of two transposed 8-byte reads.
+// Within every 16 keys the order is 0-3, 8-11, 4-7, 12-15: the order in which
+// the fragment's two lane halves take the keys of P^T from the S^T
+// accumulator.  Keys past the sequence end are zero (the causal mask gives
+// them no weight).  Dense batches; one workgroup per block, grid-strided.
+template <int D>
+__global__ __launch_bounds__(256) void attn_vt_build(const bf16_t* __restrict__ v,
+                                                bf16_t* __restrict__ vt, PyrGeom g) {
+  __shared__ __align__(16) bf16_t tile[PYR_BLOCK][D + 8];
+  const int64_t nblk = (int64_t)g.B * g.Hk * g.nb;
+  for (int64_t x = blockIdx.x; x < nblk; x += gridDim.x) {
+    const int64_t bh = x / g.nb;
+    const int j = (int)(x % g.nb);
+    const bf16_t* vb = v + (bh * g.Tks + (int64_t)j * PYR_BLOCK) * D;
+    for (int idx = threadIdx.x; idx < PYR_BLOCK * D / 8; idx += 256) {
+      const int r = idx / (D / 8), c = idx % (D / 8);
+      const uint4 val = (int64_t)j * PYR_BLOCK + r < g.Tk ? ld16(vb + r * D + c * 8)
+                                                          : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&tile[r][c * 8]) = val;
+    }
+    __syncthreads();
+    bf16_t* out = vt + x * PYR_BLOCK * D;
+    for (int idx = threadIdx.x; idx < D * 8; idx += 256) {
+      const int d = idx / 8, c8 = idx % 8;  // 16 bytes: positions 8*c8 .. +7 of row d
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t pair = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int pos = c8 * 8 + e + h, p16 = pos % 16;
+          const int key = pos - p16 + (p16 < 4 || p16 >= 12 ? p16 : (p16 < 8 ? p16 + 4 : p16 - 4));
+          pair |= (uint32_t)tile[key][d] << (16 * h);
+        }
+        w[e / 2] = pair;
+      }
+      *reinterpret_cast<uint4*>(out + d * PYR_BLOCK + c8 * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    __syncthreads();  // the tile is read before the next block overwrites it
+  }
+}
+
 template <int D>
 hipError_t launch_attn_d(const PyrGeom& g, int dtype, const void* q, const void* k,
                          const void* v, const int32_t* sel, void* o, float* lse, void* ws,
-                         hipStream_t st) {
+                         size_t ws_bytes, hipStream_t st) {
   const int64_t units = (int64_t)g.B * g.Hk * g.nqb;
   if (units == 0 || g.Tq == 0) return hipSuccess;
   if (g.decode) {
@@ -1494,8 +1563,18 @@ hipError_t launch_attn_d(const PyrGeom& g, int dtype, const void* q, const void*
     const bf16_t* kk = static_cast<const bf16_t*>(k);
     const bf16_t* vv = static_cast<const bf16_t*>(v);
     bf16_t* oo = static_cast<bf16_t*>(o);
-    if (nh == 4)
-      hipLaunchKernelGGL((attn_prefill_pp<D>), grid, dim3(512), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
+    const size_t vtb = pyr_attn_vt_bytes(g, dtype);
+    if (nh == 4 && vtb > 0 && ws && ws_bytes >= vtb) {
+      // V read through its block-transposed copy in the workspace
+      bf16_t* vt = static_cast<bf16_t*>(ws);
+      const int64_t nblk = (int64_t)g.B * g.Hk * g.nb;
+      hipLaunchKernelGGL((attn_vt_build<D>), dim3((unsigned)(nblk < (1 << 20) ? nblk : (1 << 20))),
+                         dim3(256), 0, st, vv, vt, g);
+      hipLaunchKernelGGL((attn_prefill_pp<D, true>), grid, dim3(512), 0, st, qq, kk, vt, sel, oo, lse, g,
+                         wpu);
+    } else if (nh == 4)
+      hipLaunchKernelGGL((attn_prefill_pp<D, false>), grid, dim3(512), 0, st, qq, kk, vv, sel, oo, lse, g,
+                         wpu);
     else if (nh == 2)
       hipLaunchKernelGGL((attn_prefill_mfma<D, 4, 1>), grid, dim3(256), 0, st, qq, kk, vv, sel, oo, lse, g, wpu);
     else
@@ -1532,11 +1611,11 @@ bool pyr_select_attend_fused(const PyrGeom& g, int dtype) {
 hipError_t pyr_launch_select_attend(const PyrGeom& g, int dtype, const void* q, const void* k,
                                     const void* v, const float* pyr, int32_t* sel,
                                     int32_t* trace_ids, float* trace_scores, void* o, float* lse,
-                                    void* ws, hipStream_t st) {
+                                    void* ws, size_t ws_bytes, hipStream_t st) {
   if (!pyr_select_attend_fused(g, dtype)) {
     const hipError_t e = pyr_launch_select(g, dtype, q, pyr, sel, trace_ids, trace_scores, st);
     if (e != hipSuccess) return e;
-    return pyr_launch_attn(g, dtype, q, k, v, sel, o, lse, ws, st);
+    return pyr_launch_attn(g, dtype, q, k, v, sel, o, lse, ws, ws_bytes, st);
   }
   const int64_t units = (int64_t)g.B * g.Hk * g.nqb;
   if (units == 0 || g.Tq == 0) return hipSuccess;
@@ -1553,6 +1632,20 @@ hipError_t pyr_launch_select_attend(const PyrGeom& g, int dtype, const void* q, 
   return hipGetLastError();
 }
 
+// The transposed copy costs one HBM round trip of V and saves one LDS read
+// per V^T fragment each time a workgroup attends a block: it pays when every
+// tile of V is attended by enough workgroups, (K + 1) route slots x G/4
+// workgroups per unit.  On MI355X the two break even near 33 visits (d = 128:
+// G = 4, K = 32 at 128K keys); at 130 (G = 8, K = 64 at 1M keys) the copy
+// makes the attention 4% faster.  64 leaves a margin on both sides.
+constexpr int kVtMinVisits = 64;
+
+size_t pyr_attn_vt_bytes(const PyrGeom& g, int dtype) {
+  if (dtype != 1 || g.decode || g.cu || g.G % 4 != 0) return 0;
+  if ((int64_t)(g.K + 1) * (g.G / 4) < kVtMinVisits) return 0;
+  return (size_t)g.B * g.Hk * g.nb * PYR_BLOCK * g.D * sizeof(bf16_t);
+}
+
 size_t pyr_attn_ws_bytes(const PyrGeom& g) {
   if (!g.decode) return 0;
   return (size_t)g.B * g.Hk * g.G * decode_splits(g.K) * (g.D + 2) * sizeof(float);
@@ -1560,9 +1653,9 @@ size_t pyr_attn_ws_bytes(const PyrGeom& g) {
 
 hipError_t pyr_launch_attn(const PyrGeom& g, int dtype, const void* q, const void* k,
                            const void* v, const int32_t* sel, void* o, float* lse, void* ws,
-                           hipStream_t st) {
-  return g.D == 64 ? launch_attn_d<64>(g, dtype, q, k, v, sel, o, lse, ws, st)
-                   : launch_attn_d<128>(g, dtype, q, k, v, sel, o, lse, ws, st);
+                           size_t ws_bytes, hipStream_t st) {
+  return g.D == 64 ? launch_attn_d<64>(g, dtype, q, k, v, sel, o, lse, ws, ws_bytes, st)
+                   : launch_attn_d<128>(g, dtype, q, k, v, sel, o, lse, ws, ws_bytes, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1621,5 +1714,5 @@ hipError_t pyr_launch_attn_noalloc(const PyrGeom& g, int dtype, const void* q, c
     const hipError_t e = scratch_of(st, &ws);
     if (e != hipSuccess) return e;
   }
-  return pyr_launch_attn(g, dtype, q, k, v, sel, o, lse, ws, st);
+  return pyr_launch_attn(g, dtype, q, k, v, sel, o, lse, ws, 0, st);  // (no transposed V)
 }

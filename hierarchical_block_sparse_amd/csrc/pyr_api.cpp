@@ -183,7 +183,7 @@ int64_t pyr_num_query_blocks(const pyr_problem* p) {
 
 size_t pyr_attn_workspace_bytes(const pyr_problem* p) {
   PyrGeom g;
-  return resolve(p, &g) == PYR_OK ? pyr_attn_ws_bytes(g) : 0;
+  return resolve(p, &g) == PYR_OK ? pyr_attn_ws_bytes(g) + pyr_attn_vt_bytes(g, p->dtype) : 0;
 }
 
 pyr_status pyr_build_pyramid(const pyr_problem* p, const void* k, float* pyramid,
@@ -246,10 +246,11 @@ pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void
   if (!empty && need > 0 && (!workspace || workspace_bytes < need))
     return fail(PYR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
-  if (!empty && need > 0 && !aligned16(workspace))
+  if (!empty && workspace && (need > 0 || pyr_attn_vt_bytes(g, p->dtype) > 0) && !aligned16(workspace))
     return fail(PYR_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   if (empty) return PYR_OK;
-  return hip_status(pyr_launch_attn(g, p->dtype, q, k, v, sel, o, lse, workspace, stream),
+  return hip_status(pyr_launch_attn(g, p->dtype, q, k, v, sel, o, lse, workspace,
+                                    workspace ? workspace_bytes : 0, stream),
                     "pyr_block_sparse_attn launch");
 }
 
@@ -296,14 +297,15 @@ pyr_status pyr_select_attn(const pyr_problem* p, const void* q, const void* k, c
   if (!empty && need > 0 && (!workspace || workspace_bytes < need))
     return fail(PYR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
-  if (!empty && need > 0 && !aligned16(workspace))
+  if (!empty && workspace && (need > 0 || pyr_attn_vt_bytes(g, p->dtype) > 0) && !aligned16(workspace))
     return fail(PYR_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   if (empty) return PYR_OK;
   if (!pyr_select_attend_fused(g, p->dtype) && pyr_select_lds_bytes(g, p->dtype) > 160 * 1024)
     return fail(PYR_ERR_UNSUPPORTED, "selection needs %zu bytes of LDS (> 160 KiB)",
                 pyr_select_lds_bytes(g, p->dtype));
   return hip_status(pyr_launch_select_attend(g, p->dtype, q, k, v, pyramid, sel, trace_ids,
-                                             trace_scores, o, lse, workspace, stream),
+                                             trace_scores, o, lse, workspace,
+                                             workspace ? workspace_bytes : 0, stream),
                     "pyr_select_attn launch");
 }
 

@@ -88,10 +88,17 @@ hipError_t pyr_launch_append(const PyrGeom& g, int dtype, const void* k, int64_t
 hipError_t pyr_launch_select(const PyrGeom& g, int dtype, const void* q, const float* pyr,
                              int32_t* sel, int32_t* trace_ids, float* trace_scores,
                              hipStream_t st);
+// Workspace bytes the attention needs (decode's partial states; 0 otherwise).
 size_t pyr_attn_ws_bytes(const PyrGeom& g);
+// Workspace bytes the attention can use for a block-transposed copy of V
+// (bf16 prefill of a dense batch, query heads per KV head G a multiple of 4,
+// (top_k + 1) * G/4 >= 64; 0 otherwise).  Used when the caller's workspace
+// holds that many bytes.
+size_t pyr_attn_vt_bytes(const PyrGeom& g, int dtype);
+// ws_bytes: the workspace's size (0: read V directly).
 hipError_t pyr_launch_attn(const PyrGeom& g, int dtype, const void* q, const void* k,
                            const void* v, const int32_t* sel, void* o, float* lse, void* ws,
-                           hipStream_t st);
+                           size_t ws_bytes, hipStream_t st);
 // The attention with its workspace (if any) in the library's fixed per-device
 // scratch array; the caller has checked pyr_attn_ws_bytes(g) against its size.
 hipError_t pyr_launch_attn_noalloc(const PyrGeom& g, int dtype, const void* q, const void* k,
@@ -104,7 +111,7 @@ bool pyr_select_attend_fused(const PyrGeom& g, int dtype);
 hipError_t pyr_launch_select_attend(const PyrGeom& g, int dtype, const void* q, const void* k,
                                     const void* v, const float* pyr, int32_t* sel,
                                     int32_t* trace_ids, float* trace_scores, void* o, float* lse,
-                                    void* ws, hipStream_t st);
+                                    void* ws, size_t ws_bytes, hipStream_t st);
 // Backward of the attention (bfloat16 prefill): workspace bytes and launcher.
 size_t pyr_attn_bwd_ws_bytes(const PyrGeom& g);
 // Upper bound on the work items of the key-gradient kernel (its grid size).

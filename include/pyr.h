@@ -146,11 +146,20 @@ int32_t pyr_pyramid_planes(const pyr_problem* p);
 /* Query blocks per (batch, KV head): ceil(q_len/64) in prefill, 1 in decode
  * (PISA abstract: selection runs per query block). */
 int64_t pyr_num_query_blocks(const pyr_problem* p);
-/* Bytes of device workspace pyr_block_sparse_attn needs (0 if none): decode
- * splits a unit's selected blocks over several workgroups and merges their
- * partial online-softmax states (PHBA §A.1.3 keeps those accumulators on
- * chip within one query tile; decode has one query token per unit, so its
- * blocks are split to fill the GPU). */
+/* Bytes of device workspace pyr_block_sparse_attn uses (0 if none).
+ *  - Decode splits a unit's selected blocks over several workgroups and
+ *    merges their partial online-softmax states there (PHBA §A.1.3 keeps
+ *    those accumulators on chip within one query tile; decode has one query
+ *    token per unit, so its blocks are split to fill the GPU).  Decode
+ *    requires it.
+ *  - Dense bfloat16 prefill with G = q_heads / kv_heads a multiple of 4 and
+ *    (top_k + 1) * G / 4 >= 64 (every block of v then feeds enough
+ *    workgroups for a transposed copy to pay for its HBM round trip) may
+ *    take B * kv_heads * ceil(kv_len/64) * 64 * head_dim * 2 bytes for a
+ *    block-transposed copy of v, which the attention reads in place of v.
+ *    Optional: with a NULL or smaller workspace the kernels read v directly,
+ *    and o and lse are the same bits either way.
+ * Other problems use none. */
 size_t pyr_attn_workspace_bytes(const pyr_problem* p);
 
 /* ---- the hot path ---- */
@@ -243,8 +252,14 @@ pyr_status pyr_budgets_from_entropy(const float* entropy, int32_t n_heads, int32
  *              pyr_select_topk writes them)                          (input)
  *   o          [B, Hq, q_len, d] in p->dtype                         (output)
  *   lse        NULL or [B, Hq, q_len] float32, natural log            (output)
- *   workspace  device scratch of workspace_bytes >=
- *              pyr_attn_workspace_bytes(p); may be NULL when that is 0.
+ *   workspace  device scratch, 16-byte aligned, of workspace_bytes.  Decode
+ *              requires workspace_bytes >= pyr_attn_workspace_bytes(p)
+ *              (PYR_ERR_WORKSPACE otherwise); for prefill the workspace is
+ *              optional and used only when it holds
+ *              pyr_attn_workspace_bytes(p) bytes (then the kernel reads a
+ *              transposed copy of v it writes there; results are
+ *              identical).  May be NULL when not required.  Its contents on
+ *              entry do not matter and on return are unspecified.
  * Route entries outside [0, ceil(kv_len/64)) are ignored (the host cannot read
  * device route rows without synchronising, so they are not an error). */
 pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void* k,
@@ -254,8 +269,9 @@ pyr_status pyr_block_sparse_attn(const pyr_problem* p, const void* q, const void
 /* pyr_block_sparse_attn for callers that cannot allocate device memory: code
  * under HIP graph capture, serving loops that must not call hipMalloc, and
  * harnesses that forbid allocation.  Same arguments, results and errors as
- * pyr_block_sparse_attn without the workspace: when the problem needs one
- * (decode: pyr_attn_workspace_bytes(p) > 0), its partial states go to a
+ * pyr_block_sparse_attn without the workspace (prefill reads v directly, as
+ * with a NULL workspace): when the problem needs one (decode), its partial
+ * states go to a
  * device array of PYR_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds
  * on every GPU it runs on until the process ends (64 sequences x 8 KV heads x
  * 4 query heads per KV head at top_k = 64 and head_dim = 128 take 9.6 MB).

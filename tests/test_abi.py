@@ -77,6 +77,26 @@ def test_decode_geometry():
     assert H.pyr_attn_workspace_bytes(p) > 0
 
 
+@pytest.mark.parametrize("kv_len,hq,hk,d,k", [(1048576, 8, 1, 128, 64), (4096 + 13, 16, 2, 64, 31),
+                                              (64, 8, 2, 128, 63), (8192, 128, 8, 128, 15),
+                                              (131072, 32, 8, 128, 63)])
+def test_prefill_transposed_v_workspace(kv_len, hq, hk, d, k):
+    """Dense bfloat16 prefill with G = q_heads/kv_heads a multiple of 4 and
+    (top_k + 1) * G/4 >= 64 may use a block-transposed copy of v: one
+    64 x head_dim bf16 tile per key block of every (batch, KV head).  Other
+    prefill problems use no workspace."""
+    b = 2
+    base = dict(batch=b, n_q_heads=hq, n_kv_heads=hk, head_dim=d, q_len=kv_len, kv_len=kv_len,
+                top_k=k)
+    nb = reference.num_blocks(kv_len, 64)
+    assert H.pyr_attn_workspace_bytes(_p(**base)) == b * hk * nb * 64 * d * 2
+    g = hq // hk
+    for kw in (dict(n_q_heads=2 * hk), dict(n_q_heads=3 * hk), dict(n_q_heads=hk),
+               dict(top_k=(64 * 4) // g - 2),      # just short of the threshold
+               dict(dtype=torch.float32), dict(batch=0), dict(q_len=0, kv_len=0)):
+        assert H.pyr_attn_workspace_bytes(_p(**dict(base, **kw))) == 0, kw
+
+
 def _status(fn, *args):
     lib = H.lib()
     return getattr(lib, fn)(*args), lib.pyr_last_error().decode()
@@ -279,6 +299,8 @@ def test_packed_geometry():
     assert lib.pyr_num_query_blocks(ctypes.byref(c)) == 8
     assert lib.pyr_attn_workspace_bytes(ctypes.byref(c)) == 0
     assert lib.pyr_attn_bwd_workspace_bytes(ctypes.byref(c)) == 0
+    g4 = _packed_c(n_q_heads=8)            # packed batches read v directly
+    assert lib.pyr_attn_workspace_bytes(ctypes.byref(g4)) == 0
 
 
 def test_packed_validation():

@@ -38,6 +38,10 @@ CASES = [
     C("gqa4_8k", 1, 8, 2, 8192, 8192, 128, torch.bfloat16, 4, 16, 8, seed=12),
     # GQA G=8, one KV head (the 1M workload's shape, shortened)
     C("gqa8_4k", 1, 8, 1, 4096, 4096, 128, torch.bfloat16, 4, 16, 16, seed=13),
+    # G=8 with (K+1) * G/4 = 82 workgroup visits per key block: the attention
+    # reads v through its block-transposed copy in the workspace; d = 64,
+    # two KV heads, ragged tail
+    C("gqa8_k40_vt", 1, 16, 2, 64 * 72 + 29, 64 * 72 + 29, 64, torch.bfloat16, 4, 40, 8, seed=30),
     # d=64 bf16, G=2, b=3, two batch entries
     C("d64_g2_b3", 2, 4, 2, 64 * 50, 64 * 50, 64, torch.bfloat16, 3, 6, 4, seed=14),
     # odd group size G=3 (generic selection path, one head per workgroup attention)
