@@ -29,6 +29,8 @@
 
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int kThreads = 256;
 constexpr int kChunkMax = 16;  // finest blocks per workgroup (b^s <= 16)
 constexpr int kBatch = 4;      // blocks whose loads are in flight together
@@ -303,6 +305,30 @@ __global__ __launch_bounds__(kFoldThreads) void build_fold(float* __restrict__ p
 __device__ __forceinline__ float key_f32(float x) { return x; }
 __device__ __forceinline__ float key_f32(bf16_t x) { return bf16_to_f32(x); }
 
+// Sum of column dcol over the rows t0 + rg, t0 + rg + NG, ... below t1 of one
+// block, in that order; every row's load is issued before the first add.
+template <typename T, int D, int NG>
+__device__ __forceinline__ float block_col_sum(const T* kb, int64_t t0, int64_t t1, int rg,
+                                               int dcol) {
+  constexpr int RPT = PYR_BLOCK / NG;
+  float x[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int64_t t = t0 + rg + (int64_t)r * NG;
+    x[r] = key_f32(kb[(t < t1 ? t : t1 - 1) * D + dcol]);  // rows past t1: loaded, not added
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load issued before the first add waits
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPT; ++r)
+    if (t0 + rg + (int64_t)r * NG < t1) s += x[r];
+  return s;
+}
+
+// Siblings an append to one block can need: the children before the affected
+// one, summed over the levels (b - 1 per level at most).
+constexpr int kSibMax = 32;
+
 // Decode-time maintenance: one workgroup per (batch, KV head) recomputes every
 // node over the tokens [old_len, Tk): the level-0 nodes of the affected blocks
 // as the mean of their valid key rows, then, level by level, the affected
@@ -314,17 +340,76 @@ __global__ __launch_bounds__(kThreads) void append_nodes(const T* __restrict__ k
                                                          int64_t old_len) {
   constexpr int NG = kThreads / D;  // row groups of the level-0 reduction
   __shared__ float part[NG][D];
+  __shared__ float sib[kSibMax][D];
   const int64_t bh = blockIdx.x;
   const T* kb = k + bh * g.Tks * D;
   float* slab = pyr + bh * g.planes * g.n_tot * D;
   const int tid = threadIdx.x, dcol = tid % D, rg = tid / D;
+  const int b = g.branching;
   int64_t a0 = old_len / PYR_BLOCK, a1 = (g.Tk - 1) / PYR_BLOCK;  // affected blocks
+
+  // One affected block (every decode step that stays inside a block).  It is
+  // the last block, so the affected node of each level is the last valid one:
+  // its children are the p = anc % b nodes before the affected child (older
+  // tokens only, untouched here) and that child.  Those siblings load together
+  // with the block's rows, and the thread of each column then folds the levels
+  // in registers -- the same operations in the same order as the general loop
+  // below, without a round trip through memory per level.
+  if (a0 == a1) {
+    // block ids stay below 2^30, so 32-bit arithmetic suffices here
+    const uint32_t ub = (uint32_t)b;
+    int nsib = 0;
+    for (uint32_t an = (uint32_t)a0, lvl = 1; lvl < (uint32_t)g.L; ++lvl, an /= ub) nsib += (int)(an % ub);
+    if (nsib <= kSibMax) {
+      const int64_t t0 = a0 * PYR_BLOCK;
+      const int64_t t1 = t0 + PYR_BLOCK < g.Tk ? t0 + PYR_BLOCK : g.Tk;
+      // sibling e (levels in order, children in order) goes straight to LDS
+      // row sib[e], loaded by row group e % NG; a row group is whole waves,
+      // each wave taking 64 consecutive columns
+      const int wrg = __builtin_amdgcn_readfirstlane(rg);
+      const int c0 = __builtin_amdgcn_readfirstlane(dcol - (tid % 64));
+      uint32_t an = (uint32_t)a0;
+      for (int lvl = 1, e = 0; lvl < g.L; ++lvl, an /= ub) {
+        const uint32_t p = an % ub;
+        const int64_t first = g.loff[lvl - 1] + (an - p);
+        for (uint32_t jj = 0; jj < p; ++jj, ++e)
+          if (e % NG == wrg)
+            __builtin_amdgcn_global_load_lds((const void*)(slab + (first + jj) * D + dcol),
+                                             (lds_void*)&sib[e][c0], 4, 0, 0);
+      }
+      part[rg][dcol] = block_col_sum<T, D, NG>(kb, t0, t1, rg, dcol);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's siblings are in LDS
+      __syncthreads();
+      if (rg != 0) return;
+      float tot = 0.f;
+#pragma unroll
+      for (int r = 0; r < NG; ++r) tot += part[r][dcol];
+      float v = tot / (float)(t1 - t0);
+      put_node<D>(g, slab, g.loff[0] + a0, dcol, v);
+      uint32_t m = (uint32_t)a0;  // the affected node of the level below
+      for (int lvl = 1, e = 0; lvl < g.L; ++lvl) {
+        const uint32_t p = m % ub;
+        float num = 0.f, den = 0.f;
+        for (uint32_t jj = 0; jj < p; ++jj, ++e) {
+          const float w = (float)pyr_node_tokens(g.Tk, b, lvl - 1, (int64_t)(m - p + jj));
+          num += sib[e][dcol] * w;
+          den += w;
+        }
+        const float w = (float)pyr_node_tokens(g.Tk, b, lvl - 1, (int64_t)m);
+        num += v * w;
+        den += w;
+        v = num / den;
+        m /= ub;
+        put_node<D>(g, slab, g.loff[lvl] + m, dcol, v);
+      }
+      return;
+    }
+  }
+
   for (int64_t j = a0; j <= a1; ++j) {
     const int64_t t0 = j * PYR_BLOCK;
     const int64_t t1 = t0 + PYR_BLOCK < g.Tk ? t0 + PYR_BLOCK : g.Tk;
-    float s = 0.f;
-    for (int64_t t = t0 + rg; t < t1; t += NG) s += key_f32(kb[t * D + dcol]);
-    part[rg][dcol] = s;
+    part[rg][dcol] = block_col_sum<T, D, NG>(kb, t0, t1, rg, dcol);
     __syncthreads();
     if (rg == 0) {
       float tot = 0.f;
@@ -336,7 +421,6 @@ __global__ __launch_bounds__(kThreads) void append_nodes(const T* __restrict__ k
   }
   __threadfence_block();
   __syncthreads();
-  const int b = g.branching;
   for (int lvl = 1; lvl < g.L; ++lvl) {
     a0 /= b;
     a1 /= b;
