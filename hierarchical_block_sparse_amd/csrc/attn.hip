@@ -1451,21 +1451,46 @@ __global__ __launch_bounds__(64) void attn_decode_combine(const float* __restric
                                                           float* __restrict__ lse, PyrGeom g,
                                                           int nsplit) {
   constexpr int DPL = D / 64;
+  constexpr int U = 16;  // splits whose loads are in flight together
   const int64_t row = blockIdx.x;  // (bhk * G + r)
   const int l = threadIdx.x;
-  float m = -INFINITY, s = 0.f, acc[DPL];
+  const float* src = ws + row * nsplit * (D + 2);
+  // the largest split maximum, then every split's sum and output weighted by
+  // 2^(its maximum - that); loads of U splits are issued before their use
+  // (indices past the last split are clamped to it, their values masked)
+  float m = -INFINITY;
+  for (int sp0 = 0; sp0 < nsplit; sp0 += U) {
+    float mm[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = sp0 + u < nsplit ? sp0 + u : nsplit - 1;
+      mm[u] = src[sp * (D + 2)];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = sp0 + u < nsplit ? fmaxf(m, mm[u]) : m;
+  }
+  float s = 0.f, acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float* src = ws + (row * nsplit + sp) * (D + 2);
-    const float m2 = src[0], s2 = src[1];
-    const float mx = fmaxf(m, m2);
-    if (mx == -INFINITY) continue;
-    const float a1 = exp2f(m - mx), a2 = exp2f(m2 - mx);
-    s = s * a1 + s2 * a2;
+  for (int sp0 = 0; sp0 < nsplit; sp0 += U) {
+    float mm[U], ss[U], xx[U][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = acc[e] * a1 + src[2 + l * DPL + e] * a2;
-    m = mx;
+    for (int u = 0; u < U; ++u) {
+      const int sp = sp0 + u < nsplit ? sp0 + u : nsplit - 1;
+      mm[u] = src[sp * (D + 2)];
+      ss[u] = src[sp * (D + 2) + 1];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) xx[u][e] = src[sp * (D + 2) + 2 + l * DPL + e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // an empty split (maximum -inf) adds nothing; so does every split of a
+      // row with no visible key
+      const float a = sp0 + u < nsplit && mm[u] != -INFINITY ? exp2f(mm[u] - m) : 0.f;
+      s += ss[u] * a;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] += xx[u][e] * a;
+    }
   }
   const int64_t bhk = row / g.G;
   const int r = (int)(row % g.G);
