@@ -22,6 +22,12 @@ build -> select -> attention -> pyr_block_sparse_attn_bwd for a seeded dL/do,
 `value` is tokens/s of that pass and `roofline` describes the backward call
 (its flops counted as 10 d per visible (query row, key) pair per head: the
 recomputed scores, dP, dQ, dK and dV products).
+
+With --graph one step is captured in a HIP graph after the eager, event-timed
+steps, and `value` and `ms_per_step` come from K replays of that graph (no
+launch gaps between the step's kernels); the stage times and the roofline stay
+those of the eager steps (the kernels are the same), and
+`stages.eager_ms_per_step` keeps the eager rate.
 """
 
 from __future__ import annotations
@@ -60,6 +66,9 @@ def parse():
                     help="selection and attention in one pyr_select_attn call per step")
     ap.add_argument("--backward", action="store_true",
                     help="time the training pass (forward + backward of the attention)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (stage times and "
+                         "the roofline still come from eagerly launched, event-timed steps)")
     ap.add_argument("--cold-steps", type=int, default=-1,
                     help="cold-cache steps timed after the warm ones (-1: as many as --steps; 0: none)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -386,6 +395,32 @@ def main():
     stage_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
                 for i in range(n_stage)]
     ms_per_step = elapsed * 1e3 / args.steps
+    eager_ms_per_step = None
+    if args.graph:
+        # one step captured on torch's capture stream (the library launches on
+        # the current stream and only launches kernels), then replayed
+        print(f"# capturing one step, timing {args.steps} replays", file=sys.stderr, flush=True)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            stream = torch.cuda.current_stream()
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            stream = torch.cuda.current_stream()
+            step()
+        stream = torch.cuda.current_stream()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        eager_ms_per_step = ms_per_step
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # the same steps from cold caches: 1 GiB written before each step evicts the
     # L2s and the 256 MB Infinity Cache; timed by the events only
@@ -474,6 +509,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.graph:
+        line["config"]["launch"] = "one step captured in a HIP graph, replayed"
+        line["stages"]["eager_ms_per_step"] = round(eager_ms_per_step, 4)
     if not lengths:
         line["planted_recall"] = planted_recall(cfg, sel)
     tokens_sa = tokens / ((stage_ms[1] + stage_ms[2]) / 1e3)
