@@ -124,6 +124,44 @@ def test_decode_append_steps(dtype, d, b):
         t = new
 
 
+@pytest.mark.parametrize("b,nblk", [(16, 4096), (2, 1000)], ids=["b16_45_siblings", "b2_10_levels"])
+def test_append_inside_one_block_sibling_counts(b, nblk):
+    """Appends that stay inside the last block take the on-chip fold when the
+    affected nodes' older siblings number at most 32 (summed over the levels),
+    and the level loop otherwise: with b = 16 and 4096 blocks the last block's
+    ancestors have 15 older siblings on each of three levels (45, the level
+    loop); with b = 2 and 1000 blocks they have 8 over ten levels (the fold).
+    Both must match the oracle's fresh build and keep the untouched nodes."""
+    cfg = C(f"append_b{b}", 2, 4, 2, 1, 64 * nblk, 64, torch.bfloat16, b, 8, 0, seed=55 + b)
+    cap = 64 * nblk
+    gen = torch.Generator(device="cuda").manual_seed(5500 + b)
+    kc = torch.randn((cfg.batch, cfg.n_kv_heads, cap, 64), generator=gen, device="cuda").to(cfg.dtype)
+    last = nblk - 1
+    sib = 0
+    m, lv = last, 1
+    while lv < H.pyr_num_levels(_problem(cfg, cap, cap, q_len=1)):
+        sib += m % b
+        m //= b
+        lv += 1
+    GH.log(f"case b={b}: last block {last}, {sib} older siblings over the levels")
+    assert (sib > 32) == (b == 16)
+    t = 64 * last + 5
+    p = _problem(cfg, t, cap, q_len=1)
+    pyr = torch.zeros(H.pyramid_shape(p), dtype=torch.float32, device="cuda")
+    H.pyr_build_pyramid(p, kc, pyr)
+    for new in (t + 1, t + 2, t + 40, cap):   # one token, one token, a chunk, the rest of the block
+        before = pyr.clone()
+        pn = _problem(cfg, new, cap, q_len=1)
+        H.pyr_append_pyramid(pn, kc, t, pyr)
+        torch.cuda.synchronize()
+        err, tol = _check_levels(pyr, pn, kc[:, :, :new], b)
+        GH.log(f"  append {t} -> {new}: max abs err {err:.3e} (tol {tol:.1e})")
+        assert err <= tol
+        off0 = H.pyr_level_offset(pn, 0)
+        assert torch.equal(pyr[:, :, :, off0:off0 + last], before[:, :, :, off0:off0 + last])
+        t = new
+
+
 def test_decode_path_over_a_cache():
     """The decode path on a cache with spare rows (build at kv_len - 1, append
     the last token, select, attend) gives the bits of the same path on a cache
