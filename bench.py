@@ -240,14 +240,14 @@ def cpu_baseline(cfg, q, k, v, n_units, backward=False):
 
 def attn_kernel_name(cfg, packed=False):
     """The attention kernels the library runs for this workload, in launch
-    order (dense bfloat16 prefill with G a multiple of 4 and (K+1) * G/4 >= 64
+    order (dense bfloat16 prefill with G a multiple of 4 and (K+1) * G/4 >= 16
     first writes the block-transposed copy of v into the workspace)."""
     if cfg.decode:
         return "attn_decode_mfma+combine" if cfg.dtype.itemsize == 2 else "attn_decode_split+combine"
     if cfg.dtype.itemsize != 2:
         return "attn_prefill_f32"
     if cfg.group % 4 == 0:
-        vt = not packed and (cfg.top_k + 1) * (cfg.group // 4) >= 64
+        vt = not packed and (cfg.top_k + 1) * (cfg.group // 4) >= 16
         return "attn_vt_build+attn_prefill_pp" if vt else "attn_prefill_pp"
     return "attn_prefill_mfma"
 

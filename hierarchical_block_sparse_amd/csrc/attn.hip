@@ -1660,10 +1660,10 @@ hipError_t pyr_launch_select_attend(const PyrGeom& g, int dtype, const void* q, 
 // The transposed copy costs one HBM round trip of V and saves one LDS read
 // per V^T fragment each time a workgroup attends a block: it pays when every
 // tile of V is attended by enough workgroups, (K + 1) route slots x G/4
-// workgroups per unit.  On MI355X the two break even near 33 visits (d = 128:
-// G = 4, K = 32 at 128K keys); at 130 (G = 8, K = 64 at 1M keys) the copy
-// makes the attention 4% faster.  64 leaves a margin on both sides.
-constexpr int kVtMinVisits = 64;
+// workgroups per unit.  Measured on MI355X at d = 128 and 128K keys, the copy
+// included: 9 visits (G = 4, K = 8) 1.9% slower, 17 and 18 visits 1% faster,
+// 25 and 33 visits 1.8% faster; at 130 visits (G = 8, K = 64, 1M keys) 2-4%.
+constexpr int kVtMinVisits = 16;
 
 size_t pyr_attn_vt_bytes(const PyrGeom& g, int dtype) {
   if (dtype != 1 || g.decode || g.cu || g.G % 4 != 0) return 0;

@@ -92,7 +92,7 @@ hipError_t pyr_launch_select(const PyrGeom& g, int dtype, const void* q, const f
 size_t pyr_attn_ws_bytes(const PyrGeom& g);
 // Workspace bytes the attention can use for a block-transposed copy of V
 // (bf16 prefill of a dense batch, query heads per KV head G a multiple of 4,
-// (top_k + 1) * G/4 >= 64; 0 otherwise).  Used when the caller's workspace
+// (top_k + 1) * G/4 >= 16; 0 otherwise).  Used when the caller's workspace
 // holds that many bytes.
 size_t pyr_attn_vt_bytes(const PyrGeom& g, int dtype);
 // ws_bytes: the workspace's size (0: read V directly).

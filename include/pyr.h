@@ -153,7 +153,7 @@ int64_t pyr_num_query_blocks(const pyr_problem* p);
  *    token per unit, so its blocks are split to fill the GPU).  Decode
  *    requires it.
  *  - Dense bfloat16 prefill with G = q_heads / kv_heads a multiple of 4 and
- *    (top_k + 1) * G / 4 >= 64 (every block of v then feeds enough
+ *    (top_k + 1) * G / 4 >= 16 (every block of v then feeds enough
  *    workgroups for a transposed copy to pay for its HBM round trip) may
  *    take B * kv_heads * ceil(kv_len/64) * 64 * head_dim * 2 bytes for a
  *    block-transposed copy of v, which the attention reads in place of v.

@@ -82,7 +82,7 @@ def test_decode_geometry():
                                               (131072, 32, 8, 128, 63)])
 def test_prefill_transposed_v_workspace(kv_len, hq, hk, d, k):
     """Dense bfloat16 prefill with G = q_heads/kv_heads a multiple of 4 and
-    (top_k + 1) * G/4 >= 64 may use a block-transposed copy of v: one
+    (top_k + 1) * G/4 >= 16 may use a block-transposed copy of v: one
     64 x head_dim bf16 tile per key block of every (batch, KV head).  Other
     prefill problems use no workspace."""
     b = 2
@@ -92,7 +92,7 @@ def test_prefill_transposed_v_workspace(kv_len, hq, hk, d, k):
     assert H.pyr_attn_workspace_bytes(_p(**base)) == b * hk * nb * 64 * d * 2
     g = hq // hk
     for kw in (dict(n_q_heads=2 * hk), dict(n_q_heads=3 * hk), dict(n_q_heads=hk),
-               dict(top_k=(64 * 4) // g - 2),      # just short of the threshold
+               dict(top_k=(16 * 4) // g - 2),      # just short of the threshold
                dict(dtype=torch.float32), dict(batch=0), dict(q_len=0, kv_len=0)):
         assert H.pyr_attn_workspace_bytes(_p(**dict(base, **kw))) == 0, kw
 

@@ -1,5 +1,5 @@
 """GPU checks of the attention's optional prefill workspace: dense bfloat16
-prefill with G = q_heads/kv_heads a multiple of 4 and (top_k + 1) * G/4 >= 64
+prefill with G = q_heads/kv_heads a multiple of 4 and (top_k + 1) * G/4 >= 16
 reads v through a block-transposed copy written into the workspace when the
 caller passes one of pyr_attn_workspace_bytes(p) bytes.  The copy only moves
 v's elements (keys past the sequence end become zeros, which the causal mask
