@@ -95,16 +95,20 @@ __device__ __forceinline__ void issue_tiles(const bf16_t* kh, const bf16_t* vh, 
                                             unsigned char* ktile, unsigned char* vtile, int w,
                                             int l) {
   using TG = TileGeom<D>;
-  const int64_t key0 = (int64_t)j * PYR_BLOCK;
+  const int64_t key0 = (int64_t)__builtin_amdgcn_readfirstlane(j) * PYR_BLOCK;
+  const bf16_t* kb = kh + key0 * D;
+  const bf16_t* vb = vh + key0 * D;
+  const int64_t lim = Tk - 1 - key0;
+  const int last = lim < PYR_BLOCK - 1 ? (int)lim : PYR_BLOCK - 1;
 #pragma unroll
   for (int tt = 0; tt < TG::CPR / NW; ++tt) {
     const int t = tt * NW + w;
     const int p = t * 64 + l, row = p / TG::CPR, sc = p % TG::CPR;
-    const int64_t kp = min<int64_t>(key0 + row, Tk - 1);
-    const bf16_t* ka = kh + kp * D + (sc ^ TG::swz_k(row)) * 8;
-    const bf16_t* va = vh + kp * D + (sc ^ TG::swz_v(row)) * 8;
-    __builtin_amdgcn_global_load_lds((const void*)ka, (lds_void*)(ktile + t * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)va, (lds_void*)(vtile + t * 1024), 16, 0, 0);
+    const int rr = row < last ? row : last;
+    const uint32_t ko = (uint32_t)(rr * D + (sc ^ TG::swz_k(row)) * 8) * 2;
+    const uint32_t vo = (uint32_t)(rr * D + (sc ^ TG::swz_v(row)) * 8) * 2;
+    lds_dma16(kb, TG::TILE, ko, (lds_dma_void*)(ktile + t * 1024));
+    lds_dma16(vb, TG::TILE, vo, (lds_dma_void*)(vtile + t * 1024));
   }
 }
 
@@ -370,7 +374,8 @@ __device__ __forceinline__ void tile_loads8(const bf16_t* kh, const bf16_t* vh, 
                                           int w, int l, unsigned char* ktile,
                                           unsigned char* vtile) {
   using TG = TileGeom<D>;
-  const int64_t key0 = (int64_t)j * PYR_BLOCK;
+  // j is uniform; taking it from lane 0 keeps the tile bases in scalar registers
+  const int64_t key0 = (int64_t)__builtin_amdgcn_readfirstlane(j) * PYR_BLOCK;
   const bf16_t* kb = kh + key0 * D;
   const bf16_t* vb = vh + key0 * D;
   const int64_t lim = Tk - 1 - key0;
@@ -380,16 +385,18 @@ __device__ __forceinline__ void tile_loads8(const bf16_t* kh, const bf16_t* vh, 
     const int t = tt * 8 + w;
     const int p = t * 64 + l, row = p / TG::CPR, sc = p % TG::CPR;
     const int rr = row < last ? row : last;
-    const bf16_t* ka = kb + rr * D + (sc ^ TG::swz_k(row)) * 8;
-    const bf16_t* va;
+    const uint32_t ko = (uint32_t)(rr * D + (sc ^ TG::swz_k(row)) * 8) * 2;
+    uint32_t vo;
     if constexpr (VT) {
       const int vr = p / 8, vq = p % 8;
-      va = vb + vr * PYR_BLOCK + (vq ^ ((vr / 2) % 8)) * 8;
+      vo = (uint32_t)(vr * PYR_BLOCK + (vq ^ ((vr / 2) % 8)) * 8) * 2;
     } else {
-      va = vb + rr * D + (sc ^ TG::swz_v(row)) * 8;
+      vo = (uint32_t)(rr * D + (sc ^ TG::swz_v(row)) * 8) * 2;
     }
-    __builtin_amdgcn_global_load_lds((const void*)ka, (lds_void*)(ktile + t * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)va, (lds_void*)(vtile + t * 1024), 16, 0, 0);
+    // buffer form of the LDS DMA: LDS reads of the other slots keep
+    // per-read waits while these loads are in flight
+    lds_dma16(kb, TG::TILE, ko, (lds_dma_void*)(ktile + t * 1024));
+    lds_dma16(vb, TG::TILE, vo, (lds_dma_void*)(vtile + t * 1024));
   }
 }
 
@@ -459,7 +466,10 @@ __device__ __forceinline__ float half_rowmax(f32x16& s, int kt, int half, int re
 // Matrix phase: S^T of a whole block (two 32-key M tiles, DO_S) from Kn and
 // O^T += V^T P^T of a whole block (DO_PV) from Vx and p.  The MFMAs alternate
 // between the two products and their LDS fragments are read kPpPF ahead.
-constexpr int kPpPF = 6;
+#ifndef PYR_PP_PF
+#define PYR_PP_PF 6
+#endif
+constexpr int kPpPF = PYR_PP_PF;
 
 template <int D, bool DO_S, bool DO_PV>
 struct PpSlot {
@@ -527,6 +537,7 @@ __device__ __forceinline__ void pp_matrix(const lds_u8* Kn, const lds_u8* Vx,
     __builtin_amdgcn_sched_barrier(0);
   }
 }
+
 
 // Vector phase: the block's scores in s -> P^T in p (packed bf16 pairs), with
 // the running max, the rescale of O and l, and the row sum.
@@ -880,16 +891,20 @@ __device__ __forceinline__ void issue_tiles_f32(const float* kh, const float* vh
                                                 unsigned char* ktile, unsigned char* vtile, int w,
                                                 int l) {
   using TG = TileGeomF32<D>;
-  const int64_t key0 = (int64_t)j * PYR_BLOCK;
+  const int64_t key0 = (int64_t)__builtin_amdgcn_readfirstlane(j) * PYR_BLOCK;
+  const float* kb = kh + key0 * D;
+  const float* vb = vh + key0 * D;
+  const int64_t lim = Tk - 1 - key0;
+  const int last = lim < PYR_BLOCK - 1 ? (int)lim : PYR_BLOCK - 1;
 #pragma unroll
   for (int tt = 0; tt < TG::CPR / NW; ++tt) {
     const int t = tt * NW + w;
     const int p = t * 64 + l, row = p / TG::CPR, sc = p % TG::CPR;
-    const int64_t kp = min<int64_t>(key0 + row, Tk - 1);
-    const float* ka = kh + kp * D + (sc ^ TG::swz_k(row)) * 4;
-    const float* va = vh + kp * D + (sc ^ TG::swz_v(row)) * 4;
-    __builtin_amdgcn_global_load_lds((const void*)ka, (lds_void*)(ktile + t * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)va, (lds_void*)(vtile + t * 1024), 16, 0, 0);
+    const int rr = row < last ? row : last;
+    const uint32_t ko = (uint32_t)(rr * D + (sc ^ TG::swz_k(row)) * 4) * 4;
+    const uint32_t vo = (uint32_t)(rr * D + (sc ^ TG::swz_v(row)) * 4) * 4;
+    lds_dma16(kb, TG::TILE, ko, (lds_dma_void*)(ktile + t * 1024));
+    lds_dma16(vb, TG::TILE, vo, (lds_dma_void*)(vtile + t * 1024));
   }
 }
 
@@ -1316,20 +1331,21 @@ __global__ __launch_bounds__(256, 4) void attn_decode_mfma(
   // d = 32*ks + 8*lg), and a quarter of the V tile into vt (rows past the
   // sequence repeat its last row; the mask gives them no weight)
   auto load = [&](int b, uint4 (&kr)[KS], unsigned char* vt) {
-    const int64_t key0 = (int64_t)s_blk[b] * PYR_BLOCK;
+    const int64_t key0 = (int64_t)__builtin_amdgcn_readfirstlane(s_blk[b]) * PYR_BLOCK;
     const int64_t lim = g.Tk - 1 - key0;
     const int last = lim < PYR_BLOCK - 1 ? (int)lim : PYR_BLOCK - 1;
     const int kk = 16 * w + lr;
     const bf16_t* krow = kh + (key0 + (kk < last ? kk : last)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kr[ks] = ld16_nt(krow + ks * 32 + 8 * lg);
+    const bf16_t* vb = vh + key0 * D;
 #pragma unroll
     for (int tt = 0; tt < TL; ++tt) {
       const int t = tt * 4 + w;
       const int p = t * 64 + l, row = p / TG::CPR, sc = p % TG::CPR;
       const int rr = row < last ? row : last;
-      const bf16_t* va = vh + (key0 + rr) * D + (sc ^ TG::swz_v(row)) * 8;
-      __builtin_amdgcn_global_load_lds((const void*)va, (lds_void*)(vt + t * 1024), 16, 0, 0);
+      const uint32_t vo = (uint32_t)(rr * D + (sc ^ TG::swz_v(row)) * 8) * 2;
+      lds_dma16(vb, TG::TILE, vo, (lds_dma_void*)(vt + t * 1024));
     }
   };
   // per-lane byte offset of the V^T fragment of d tile dt: row 16w + 4*lg +

@@ -204,3 +204,22 @@ __device__ __forceinline__ int route_compact_wave(const int* raw, int cnt, int n
                                                   int n0, Keep keep) {
   return route_compact_used(raw, cnt, route_used_mask(raw, cnt, nb), out, n0, keep);
 }
+
+// Direct 16-byte global -> LDS load through a buffer resource (the MUBUF form
+// of the LDS DMA).  Lane i's 16 bytes at base + voffset land at
+// lds + 16 * i; base and lds must be wave-uniform, and byte offsets at or past
+// `bytes` read as zero instead of touching memory.  Like the global form, it
+// is counted by the vector-memory counter only.  It replaces
+// __builtin_amdgcn_global_load_lds where a kernel reads LDS while such loads
+// are in flight: the compiler treats the global form as a flat access that may
+// also be counted by the LDS counter, and then every wait for an LDS read
+// becomes a wait for all of them; with the buffer form it keeps counting the
+// reads one by one.
+typedef __attribute__((address_space(3))) void lds_dma_void;
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t bytes, uint32_t voffset,
+                                          lds_dma_void* lds) {
+  // word 3 of a raw gfx9 buffer resource: 32-bit data format, no stride, no swizzle
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voffset, 0, 0, 0);
+}
