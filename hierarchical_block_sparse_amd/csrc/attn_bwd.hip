@@ -82,14 +82,21 @@ __device__ __forceinline__ void load_tile(const bf16_t* base, int64_t row0, int6
                                           unsigned char* tile, int w, int l) {
   using TG = BTile<D>;
   static_assert(64 * TG::CPR % NT == 0, "tile must split evenly");
+  // row0 is uniform: from lane 0, so the tile base stays in scalar registers
+  const int64_t r0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(row0 >> 32)) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((int)row0));
+  const int64_t rb = r0 < last ? r0 : last;
+  const int lim = (int)min<int64_t>(last - rb, 63);
+  const bf16_t* tb = base + rb * D;
 #pragma unroll
   for (int t = 0; t < 64 * TG::CPR / NT; ++t) {
     const int p = t * NT + w * 64 + l;
     const int row = p / TG::CPR, sc = p % TG::CPR;
-    const int64_t r = min<int64_t>(row0 + row, last);
-    const bf16_t* src = base + r * D + (sc ^ TG::swz(row)) * 8;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(tile + (t * NT + w * 64) * 16),
-                                     16, 0, 0);
+    const int rr = row < lim ? row : lim;
+    // buffer form of the LDS DMA: the tile reads of other stages keep
+    // per-read waits while these loads are in flight
+    lds_dma16(tb, TG::TILE, (uint32_t)(rr * D + (sc ^ TG::swz(row)) * 8) * 2,
+              (lds_dma_void*)(tile + (t * NT + w * 64) * 16));
   }
 }
 
@@ -590,11 +597,9 @@ __device__ __forceinline__ void load_visitor(const bf16_t* q, const bf16_t* dout
   const int64_t r0 = (int64_t)i * PYR_BLOCK;
   load_tile<D, 256>(q + bh * g.Tq * D, r0, g.Tq - 1, st, w, l);
   load_tile<D, 256>(dout + bh * g.Tq * D, r0, g.Tq - 1, st + TG::TILE, w, l);
-  if (l < 8) {
-    const float* src = rec + (bh * g.nqb + i) * kRec + (w * 8 + l) * 4;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(st + 2 * TG::TILE + w * 128), 16,
-                                     0, 0);
-  }
+  if (l < 8)
+    lds_dma16(rec + (bh * g.nqb + i) * kRec, kRec * 4, (uint32_t)(w * 8 + l) * 16,
+              (lds_dma_void*)(st + 2 * TG::TILE + w * 128));
 }
 
 // Work-list metadata of the key-gradient kernel.
