@@ -520,7 +520,21 @@ __device__ __forceinline__ void rank_level(const PyrGeom& g, int level, int C, i
   if (BAL && C > NT)  // the counts of candidates NT .. C-1 are accumulated below
     for (int j = NT + tid; j < C; j += NT) flag[j] = 0;
   lds_barrier();
-  if (!BAL || C <= NT) {
+  if (NW == 4 && !BAL && 2 * C16 <= NT) {
+    // at most half a candidate per thread (four waves; with eight the
+    // kernel's extra registers for this path cost more than it saves): the
+    // first half of the threads
+    // counts the keys above each candidate's in the first half of the list,
+    // the second half in the rest (the lanes of a wave read the same keys:
+    // LDS broadcast), and the two counts meet in LDS
+    const int hh = 2 * tid >= NT, j = tid - hh * (NT / 2);
+    const int nh = ((C16 / 2) + 15) & ~15;  // keys of the first half, a multiple of 16
+    int cnt = 0;
+    if (j < C) cnt = count_above(key + hh * nh, hh ? C16 - nh : nh, key[j]);
+    if (hh && j < C) flag[j] = cnt;
+    lds_barrier();
+    if (!hh && j < C) flag[j] += cnt;
+  } else if (!BAL || C <= NT) {
     // a candidate per thread: its rank (the keys above its key); the lanes of
     // a wave read the same keys (LDS broadcast)
     for (int j = tid; j < C; j += NT) flag[j] = count_above(key, C16, key[j]);
